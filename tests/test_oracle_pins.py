@@ -1,0 +1,444 @@
+"""Pins for the CPU oracle: checks against closed forms, brute force, special
+cases and library routines -- never against the oracle's own formulas.
+
+Citations refer to the page "Opportunistic Expert Activation (OEA) - L2"
+(sections 2, 3, 4) and the page "DynaExq" (sections 2.2, 2.5, 3.2).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit, softmax
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+def _ulp_f32(v: np.ndarray) -> np.ndarray:
+    v = np.abs(v.astype(np.float32))
+    return np.spacing(v).astype(np.float64)
+
+
+def test_cexpf_within_two_ulp_of_libm():
+    # Cody-Waite exp vs exp() in double rounded to fp32, over [-80, 0].
+    xs = np.concatenate([
+        np.linspace(-80.0, 0.0, 20001, dtype=np.float32),
+        synth.rng(11).uniform(-80.0, 0.0, 20000).astype(np.float32),
+        -np.float32(2.0) ** -np.arange(1, 40, dtype=np.float32),
+        np.array([0.0, -0.0, -1e-30, -80.0], np.float32),
+    ])
+    got = np.array([oracle.cexpf(float(x)) for x in xs], np.float32)
+    ref = np.exp(xs.astype(np.float64)).astype(np.float32)
+    err_ulp = np.abs(got.astype(np.float64) - ref.astype(np.float64)) / _ulp_f32(ref)
+    assert err_ulp.max() <= 2.0, (err_ulp.max(), xs[err_ulp.argmax()])
+    assert oracle.cexpf(0.0) == 1.0
+    assert oracle.cexpf(-80.5) == 0.0 and oracle.cexpf(-1e4) == 0.0
+
+
+def test_f16_conversions_match_numpy():
+    # numpy's float16 cast is round-to-nearest-even (a library routine).
+    r = synth.rng(12)
+    vals = np.concatenate([
+        r.standard_normal(20000).astype(np.float32) * np.float32(0.01),
+        r.standard_normal(20000).astype(np.float32) * np.float32(1000.0),
+        (r.standard_normal(5000) * 1e-6).astype(np.float32),          # subnormal range
+        np.array([65504.0, 65519.99, 65520.0, 70000.0, 6.0e-8, 2.9802322e-08,
+                  2.9802326e-08, 0.0, -0.0], np.float32),
+    ])
+    # exact midpoints between neighbouring fp16 values: ties to even
+    h = np.arange(0x0400, 0x7bff, 97, dtype=np.uint16).view(np.float16).astype(np.float32)
+        # consecutive values
+    h2 = (np.arange(0x0400, 0x7bff, 97, dtype=np.uint16) + 1).view(np.float16).astype(np.float32)
+    mids = ((h.astype(np.float64) + h2.astype(np.float64)) / 2).astype(np.float32)
+    vals = np.concatenate([vals, mids, -mids])
+    got = np.array([oracle.f32_to_f16(float(v)) for v in vals], np.uint16)
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+    # fp16 -> fp32 for every finite pattern
+    pats = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    f = pats.view(np.float16)
+    fin = np.isfinite(f)
+    got2 = np.array([oracle.f16_to_f32(int(p)) for p in pats[fin][::7]], np.float32)
+    assert np.array_equal(got2, f[fin][::7].astype(np.float32))
+
+
+def test_bf16_widening_is_the_top_half():
+    bits = np.arange(0, 0x10000, 251, dtype=np.uint32).astype(np.uint16)
+    for b in bits:
+        v = np.array([int(b) << 16], np.uint32).view(np.float32)[0]
+        got = oracle.bf16_to_f32(int(b))
+        assert (math.isnan(v) and math.isnan(got)) or got == v
+
+
+# ---------------------------------------------------------------------------
+# ranking and top-k (OEA page, section 2 Q1)
+# ---------------------------------------------------------------------------
+def test_rank_matches_python_sort_with_ties():
+    for seed in range(20):
+        l = synth.tied_logits(seed, 1, 40, levels=5)[0] if seed % 2 else synth.logits(seed, 1, 128)[0]
+        order = oracle.rank(l)
+        ref = sorted(range(l.shape[0]), key=lambda j: (-float(l[j]), j))
+        assert list(order) == ref
+
+
+@pytest.mark.parametrize("N,k", [(6, 2), (8, 3), (10, 4), (9, 1)])
+def test_vanilla_topk_is_max_sum_subset(N, k):
+    # brute force over all k-subsets: the kept set maximises the exact sum of
+    # logits; among equal sums the lexicographically smallest index tuple wins.
+    for seed in range(30):
+        l = synth.tied_logits(seed, 1, N, levels=3)[0] if seed % 3 == 0 else synth.logits(seed, 1, N)[0]
+        best = max(itertools.combinations(range(N), k),
+                   key=lambda c: (math.fsum(float(l[j]) for j in c), [-j for j in c]))
+        r = oracle.route(l[None, :], k, oea=False)
+        assert sorted(r["idx"][0].tolist()) == list(best)
+
+
+def _closed_form_T(N, k, B):
+    return N * (1.0 - (1.0 - k / N) ** B)
+
+
+def test_golden_expected_union_from_page():
+    g = json.load(open(os.path.join(GOLDEN, "expected_union.json")))
+    v = _closed_form_T(g["N"], g["k"], g["B"])
+    assert round(v) == g["printed_E_T"]
+    assert round(v / _closed_form_T(g["N"], g["k"], 1)) == g["printed_ratio_vs_B1"]
+
+
+def _mc_T(B, N, k, trials, *, oea=False, k0=0, seed=0):
+    Ts = np.empty(trials)
+    cnt_sum = np.zeros(N)
+    chunk = 1000
+    done = 0
+    while done < trials:
+        n = min(chunk, trials - done)
+        L = synth.normal((seed, done), (n, B, N))
+        for t in range(n):
+            r = oracle.route(L[t], k, oea=oea, k0=k0, p=1.0)
+            d = oracle.dispatch(r["idx"], N)
+            Ts[done + t] = d["T"]
+            cnt_sum += d["cnt"]
+            assert d["cnt"].max() <= B                       # cnt_i <= B
+            assert d["T"] <= N
+            if not oea:
+                assert d["cnt"].sum() == B * k               # sum cnt = Bk for vanilla
+        done += n
+    return Ts, cnt_sum / trials
+
+
+@pytest.mark.parametrize("oea,kk", [(False, 8), (True, 3), (True, 5)])
+def test_monte_carlo_expected_union(oea, kk):
+    # iid N(0,1) logits make each token's top-kk a uniform kk-subset, so
+    # E[T] = N(1 - (1 - kk/N)^B) (OEA page, section 4).  For simplified OEA
+    # the union is over the top-k0 baselines, the same formula with k0.
+    B, N, k = 16, 128, 8
+    trials = 12000
+    Ts, mean_cnt = _mc_T(B, N, k, trials, oea=oea, k0=kk, seed=100 + kk)
+    expect = _closed_form_T(N, kk, B)
+    se = Ts.std(ddof=1) / math.sqrt(trials)
+    assert abs(Ts.mean() - expect) <= 4 * se, (Ts.mean(), expect, se)
+    if not oea:
+        # E[cnt_i] = Bk/N (OEA page, section 4, check 5)
+        assert abs(mean_cnt.mean() - B * k / N) < 1e-9
+        assert np.all(np.abs(mean_cnt - B * k / N) < 0.05)
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 32, 128])
+def test_monte_carlo_union_other_batch_sizes(B):
+    N, k = 128, 8
+    trials = 1500
+    Ts, _ = _mc_T(B, N, k, trials, seed=200 + B)
+    expect = _closed_form_T(N, k, B)
+    se = max(Ts.std(ddof=1), 1e-3) / math.sqrt(trials)
+    assert abs(Ts.mean() - expect) <= 4 * se + 1e-9, (Ts.mean(), expect)
+
+
+# ---------------------------------------------------------------------------
+# OEA (section 2 Q2, section 3, section 5 Figure 3)
+# ---------------------------------------------------------------------------
+def _exact_topp_count(l, p):
+    """t from the exact definition in double; also the distance to the boundary."""
+    order = sorted(range(len(l)), key=lambda j: (-float(l[j]), j))
+    prob = softmax(np.asarray(l, np.float64))
+    cum = np.cumsum(prob[order])
+    t = int(np.argmax(cum >= p)) + 1 if (cum >= p).any() else len(l)
+    margin = np.min(np.abs(cum - p))
+    return t, margin
+
+
+def _oea_by_definition(l, k, k0, p):
+    """Union of baselines, then each token's top-min(k,T) restricted to S_base
+    (masked top-k form, independent of the oracle's literal scan)."""
+    B, N = l.shape
+    tops = []
+    for i in range(B):
+        t, _ = _exact_topp_count(l[i], p) if p < 1 else (N, 1.0)
+        n = min(k0, t)
+        order = sorted(range(N), key=lambda j: (-float(l[i, j]), j))
+        tops.append(order[:n])
+    sbase = set().union(*map(set, tops))
+    out = []
+    for i in range(B):
+        order = sorted(sbase, key=lambda j: (-float(l[i, j]), j))
+        out.append(order[:min(k, len(sbase))])
+    return out, sbase, [len(t) for t in tops]
+
+
+@pytest.mark.parametrize("B,N,k,k0,p,scale", [
+    (4, 16, 4, 2, 0.7, 1.0), (4, 16, 4, 2, 0.7, 8.0), (16, 128, 8, 3, 1.0, 1.0),
+    (16, 128, 8, 5, 0.5, 4.0), (32, 128, 8, 3, 0.9, 8.0), (7, 12, 5, 2, 0.6, 3.0),
+    (128, 128, 8, 5, 0.7, 4.0), (3, 40, 16, 7, 0.8, 6.0),
+])
+def test_oea_matches_definition(B, N, k, k0, p, scale):
+    for seed in range(6):
+        l = synth.logits(seed, B, N, scale)
+        r = oracle.route(l, k, oea=True, k0=k0, p=p)
+        # skip tokens whose top-p crossing sits within 1e-5 of p (fp32 decides there)
+        if p < 1 and min(_exact_topp_count(l[i], p)[1] for i in range(B)) < 1e-5:
+            continue
+        ref, sbase, nb = _oea_by_definition(l, k, k0, p)
+        assert r["T"] == len(sbase)                                # T = |S_base|
+        assert list(r["n_base"]) == nb
+        mask_set = {j for j in range(N) if (r["mask"][j // 32] >> (j % 32)) & 1}
+        assert mask_set == sbase
+        for i in range(B):
+            kept = [int(e) for e in r["idx"][i] if e >= 0]
+            assert kept == ref[i]                                   # slots in rank order
+            assert set(kept[:nb[i]]) <= set(kept)                   # baseline kept
+            assert set(kept) <= sbase                               # piggyback within S_base
+            assert len(kept) == min(k, len(sbase))
+            assert abs(r["w"][i].sum() - 1.0) < 1e-12              # renormalised
+            ww = r["w"][i][:len(kept)]
+            for a in range(len(kept)):                              # w ratio = exp(l diff)
+                assert math.isclose(ww[a] / ww[0], math.exp(float(l[i, kept[a]]) - float(l[i, kept[0]])),
+                                    rel_tol=1e-12)
+
+
+def test_oea_with_k0_equal_k_is_vanilla_bit_for_bit():
+    for seed in range(10):
+        l = synth.logits(seed, 16, 128, 2.0)
+        a = oracle.route(l, 8, oea=True, k0=8, p=1.0)
+        b = oracle.route(l, 8, oea=False, renorm=True)
+        assert np.array_equal(a["idx"], b["idx"])
+        assert np.array_equal(a["w"], b["w"])
+        assert a["T"] == b["T"]
+
+
+def test_oea_batch_of_one_has_no_piggyback():
+    # OEA page, section 7 detail 2: piggybacking is redundant at B = 1.
+    for seed in range(20):
+        l = synth.logits(seed, 1, 128, 3.0)
+        r = oracle.route(l, 8, oea=True, k0=3, p=0.6)
+        kept = [e for e in r["idx"][0] if e >= 0]
+        assert len(kept) == r["n_base"][0] == r["T"]
+
+
+def test_topp_count_properties():
+    # monotone in p, t = 1 for tiny p, matches the exact definition away from the boundary
+    agree = 0
+    for seed in range(40):
+        l = synth.logits(seed, 1, 128, 4.0)[0]
+        ts = [oracle.topp_count(l, p) for p in (1e-6, 0.2, 0.4, 0.6, 0.8, 0.95, 0.999)]
+        assert ts[0] == 1
+        assert all(a <= b for a, b in zip(ts, ts[1:]))
+        assert oracle.topp_count(l, 1.0) == 128
+        for p in (0.3, 0.5, 0.7, 0.9):
+            t_ref, margin = _exact_topp_count(l, p)
+            if margin > 1e-5:
+                assert oracle.topp_count(l, p) == t_ref
+                agree += 1
+    assert agree > 100
+
+
+def test_softmax_terms_normaliser():
+    # Z is the fp32 tree sum; it must be within n*eps of the exact double sum
+    for seed in range(20):
+        l = synth.logits(seed, 1, 128, 3.0)[0]
+        e, Z = oracle.softmax_terms(l)
+        exact = math.fsum(float(v) for v in e)
+        assert abs(Z - exact) <= 128 * 2 ** -24 * exact
+        assert e.max() == 1.0
+
+
+def test_vanilla_raw_softmax_weights():
+    l = synth.logits(3, 8, 128, 2.0)
+    r = oracle.route(l, 8, oea=False, renorm=False)
+    prob = softmax(l.astype(np.float64), axis=1)
+    for i in range(8):
+        np.testing.assert_allclose(r["w"][i], prob[i, r["idx"][i]], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# dispatch (Eq. 2's cnt_i and T)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("oea", [False, True])
+def test_dispatch_properties(oea):
+    for seed in range(10):
+        B, N, k = 24, 128, 8
+        l = synth.logits(seed, B, N, 4.0)
+        r = oracle.route(l, k, oea=oea, k0=3, p=0.6)
+        d = oracle.dispatch(r["idx"], N)
+        idx = r["idx"]
+        pairs = [(int(idx[i, s]), i, i * k + s) for i in range(B) for s in range(k) if idx[i, s] >= 0]
+        ref_perm = [q for _, _, q in sorted(pairs)]                # (expert, token) order
+        total = len(pairs)
+        assert d["offsets"][N] == total == d["cnt"].sum()
+        assert list(d["perm"][:total]) == ref_perm
+        assert np.all(d["perm"][total:] == -1)
+        assert np.array_equal(np.diff(d["offsets"]), d["cnt"])
+        act = [e for e in range(N) if d["cnt"][e] > 0]
+        assert list(d["active"][:d["T"]]) == act and np.all(d["active"][d["T"]:] == -1)
+        assert d["T"] == r["T"] if oea else True                   # T_disp = |S_base|
+        assert d["cnt"].max() <= B
+
+
+def test_dispatch_empty_rows():
+    idx = -np.ones((3, 4), np.int32)
+    d = oracle.dispatch(idx, 16)
+    assert d["T"] == 0 and d["offsets"][-1] == 0 and np.all(d["perm"] == -1)
+
+
+# ---------------------------------------------------------------------------
+# router logits and expert FFN
+# ---------------------------------------------------------------------------
+def test_router_logits_match_numpy():
+    x = synth.activations(1, 5, 64).astype(np.float64)
+    wr = synth.router_weight(1, 16, 64).astype(np.float64)
+    np.testing.assert_allclose(oracle.router_logits(x, wr), x @ wr.T, rtol=1e-13, atol=1e-15)
+
+
+def _dense_swiglu(x, g, u, d):
+    a = (x @ g.T)
+    return (a * expit(a) * (x @ u.T)) @ d.T
+
+
+def _f32_experts(N, H, I, seed, same=False):
+    ex = []
+    for e in range(N):
+        g, u, d = synth.expert_weights_f32(seed, 0 if same else e, H, I)
+        ex.append(dict(fmt=oracle.FMT_F32, gate=g, up=u, down=d))
+    return ex
+
+
+@pytest.mark.parametrize("oea", [False, True])
+def test_ffn_identical_experts_reduce_to_dense_mlp(oea):
+    # With identical experts and weights summing to 1, every routing gives the
+    # dense SwiGLU MLP (numpy matmuls).
+    N, H, I, B, k = 8, 64, 32, 5, 3
+    ex = _f32_experts(N, H, I, 5, same=True)
+    x = synth.activations(2, B, H).astype(np.float64)
+    r = oracle.route(synth.logits(2, B, N, 3.0), k, oea=oea, k0=1, p=0.7)
+    y = oracle.expert_ffn(ex, H, I, x, r["idx"], r["w"])
+    g, u, d = [m.astype(np.float64) for m in (ex[0]["gate"], ex[0]["up"], ex[0]["down"])]
+    np.testing.assert_allclose(y, _dense_swiglu(x, g, u, d), rtol=1e-10, atol=1e-13)
+
+
+def test_ffn_weights_and_indices_through_scaled_down_projections():
+    # Expert e = expert 0 with W_down scaled by c_e: y_i = (sum_s w_is c_{e_is}) MLP(x_i).
+    N, H, I, B, k = 6, 32, 48, 7, 3
+    g, u, d = synth.expert_weights_f32(9, 0, H, I)
+    c = 2.0 ** np.arange(-2, N - 2, dtype=np.float64)     # powers of two: exact scaling
+    ex = [dict(fmt=oracle.FMT_F32, gate=g, up=u, down=(d * np.float32(c[e])).astype(np.float32))
+          for e in range(N)]
+    x = synth.activations(3, B, H).astype(np.float64)
+    r = oracle.route(synth.logits(3, B, N, 2.0), k, oea=False)
+    y = oracle.expert_ffn(ex, H, I, x, r["idx"], r["w"])
+    base = _dense_swiglu(x, g.astype(np.float64), u.astype(np.float64), d.astype(np.float64))
+    scale = (r["w"] * c[r["idx"]]).sum(1)
+    np.testing.assert_allclose(y, scale[:, None] * base, rtol=1e-9, atol=1e-14)
+
+
+def test_ffn_zero_up_gives_zero_and_empty_slots_ignored():
+    N, H, I, B, k = 4, 16, 8, 3, 2
+    ex = _f32_experts(N, H, I, 4)
+    for e in ex:
+        e["up"] = np.zeros_like(e["up"])
+    x = synth.activations(4, B, H)
+    r = oracle.route(synth.logits(4, B, N), k, oea=False)
+    assert np.all(oracle.expert_ffn(ex, H, I, x, r["idx"], r["w"]) == 0.0)
+    ex = _f32_experts(N, H, I, 4)
+    empty = -np.ones((B, k), np.int32)
+    assert np.all(oracle.expert_ffn(ex, H, I, x, empty, np.zeros((B, k))) == 0.0)
+
+
+def test_ffn_bf16_storage_equals_f32_storage_of_same_values():
+    N, H, I, B, k = 4, 32, 16, 3, 2
+    exb, exf = [], []
+    for e in range(N):
+        g, u, d = synth.expert_weights_bf16(6, e, H, I)
+        exb.append(dict(fmt=oracle.FMT_BF16, gate=g, up=u, down=d))
+        exf.append(dict(fmt=oracle.FMT_F32, gate=synth.bf16_bits_to_f32(g), up=synth.bf16_bits_to_f32(u),
+                        down=synth.bf16_bits_to_f32(d)))
+    x = synth.activations(6, B, H)
+    r = oracle.route(synth.logits(6, B, N), k, oea=False)
+    assert np.array_equal(oracle.expert_ffn(exb, H, I, x, r["idx"], r["w"]),
+                          oracle.expert_ffn(exf, H, I, x, r["idx"], r["w"]))
+
+
+# ---------------------------------------------------------------------------
+# INT4 groupwise quantiser (DynaExq low-precision versions)
+# ---------------------------------------------------------------------------
+def _unpack(q, rows, cols):
+    lo = (q & 0x0F).astype(np.int32) - 8            # even columns, low nibble
+    hi = (q >> 4).astype(np.int32) - 8
+    out = np.empty((rows, cols), np.int32)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def test_int4_quantiser_bounds_and_round_trip():
+    rows, cols = 9, 384
+    w = synth.to_bf16_bits(synth.normal(21, (rows, cols), 0.02))
+    w[3, 128:256] = 0                                  # an all-zero group
+    q, s = oracle.quantize_int4(w)
+    qi = _unpack(q, rows, cols)
+    wf = synth.bf16_bits_to_f32(w).astype(np.float64)
+    sf = s.view(np.float16).astype(np.float64)
+    sfull = np.repeat(sf, 128, axis=1)
+    assert np.abs(qi).max() <= 7
+    assert np.all(np.abs(wf - qi * sfull) <= sfull / 2 + 1e-30)       # |w - q s| <= s/2
+    amax = np.abs(wf).reshape(rows, cols // 128, 128).max(-1)
+    ref_s = (amax.astype(np.float32) / np.float32(7.0)).astype(np.float16)
+    assert np.array_equal(s.view(np.float16), ref_s)
+    assert s[3, 1] == 0 and np.all(qi[3, 128:256] == 0)
+    # pack -> unpack is exact
+    repacked = ((qi[:, 0::2] + 8) | ((qi[:, 1::2] + 8) << 4)).astype(np.uint8)
+    assert np.array_equal(repacked, q)
+
+
+def test_int4_ffn_equals_f32_ffn_of_dequantised_weights():
+    N, H, I, B, k = 3, 128, 128, 4, 2
+    exq, exf = [], []
+    for e in range(N):
+        mats = synth.expert_weights_bf16(8, e, H, I)
+        qe, fe = dict(fmt=oracle.FMT_INT4), dict(fmt=oracle.FMT_F32)
+        for name, m in zip(("gate", "up", "down"), mats):
+            q, s = oracle.quantize_int4(m)
+            qe[name], qe["s_" + name] = q, s
+            deq = _unpack(q, *m.shape) * np.repeat(s.view(np.float16).astype(np.float32), 128, axis=1)
+            fe[name] = deq.astype(np.float32)
+        exq.append(qe)
+        exf.append(fe)
+    x = synth.activations(8, B, H)
+    r = oracle.route(synth.logits(8, B, N), k, oea=False)
+    np.testing.assert_array_equal(oracle.expert_ffn(exq, H, I, x, r["idx"], r["w"]),
+                                  oracle.expert_ffn(exf, H, I, x, r["idx"], r["w"]))
+
+
+def test_hotness_ema_closed_form():
+    # DynaExq section 2.5: S <- a S + (1 - a) c; from S=0 with constant c,
+    # after n updates S = c (1 - a^n).
+    S = np.zeros(5)
+    c = np.array([0, 1, 2, 5, 9], np.int32)
+    for _ in range(12):
+        S = oracle.hotness_ema(S, c, 0.9)
+    np.testing.assert_allclose(S, c * (1 - 0.9 ** 12), rtol=1e-14)
