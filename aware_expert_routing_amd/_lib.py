@@ -1,0 +1,200 @@
+"""ctypes binding of libmoe (the C ABI declared in include/moe.h).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream straight to the library and raises on a non-zero
+status.  Nothing here computes any part of the layer; if the built library
+is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
+MOE_DT_F32, MOE_DT_BF16 = 0, 1
+MOE_W_F32, MOE_W_BF16, MOE_W_INT4_G128 = 0, 1, 2
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class ExpertHandle(ctypes.Structure):
+    """Mirror of moe_expert_handle (64 bytes)."""
+    _fields_ = [("fmt", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("reserved", ctypes.c_int64)]
+
+
+HANDLE_BYTES = ctypes.sizeof(ExpertHandle)
+assert HANDLE_BYTES == 64
+
+_lib = None
+
+# (name, argtypes, restype)
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGNATURES = [
+    ("moe_router_logits", [_P, _I, _P, _I, _I, _I, _P, _P], _I),
+    ("moe_route_topk", [_P, _I, _I, _I, _I, _P, _P, _P], _I),
+    ("moe_route_oea", [_P, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P], _I),
+    ("moe_dispatch", [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
+    ("moe_ffn_workspace_bytes", [_I, _I, _I, _I], _S),
+    ("moe_expert_ffn", [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _S, _P], _I),
+    ("moe_handle_publish", [_P, _I, ctypes.POINTER(ExpertHandle), _P], _I),
+    ("moe_quantize_int4_g128", [_P, _I, _I, _P, _P, _P], _I),
+    ("moe_hotness_ema", [_P, _P, _I, _F, _P], _I),
+    ("moe_status_str", [_I], ctypes.c_char_p),
+    ("moe_last_error", [], ctypes.c_char_p),
+]
+EXPORTED = [name for name, _, _ in _SIGNATURES]
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmoe.so not found at {LIB_PATH}; build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    l = ctypes.CDLL(LIB_PATH)
+    for name, args, res in _SIGNATURES:
+        f = getattr(l, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = l
+    return l
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status, lib().moe_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _x_dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return MOE_DT_BF16
+    if x.dtype == torch.float32:
+        return MOE_DT_F32
+    raise TypeError(f"activations must be float32 or bfloat16, got {x.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI, minus the moe_ prefix)
+# ---------------------------------------------------------------------------
+def router_logits(x, w_r, logits=None, stream=None):
+    B, H = x.shape
+    N = w_r.shape[0]
+    if logits is None:
+        logits = torch.empty(B, N, device=x.device, dtype=torch.float32)
+    _check("moe_router_logits", lib().moe_router_logits(_ptr(x), _x_dtype(x), _ptr(w_r), B, H, N,
+                                                        _ptr(logits), _stream(stream)))
+    return logits
+
+
+def route_topk(logits, k: int, renorm: bool = True, idx=None, w=None, stream=None):
+    B, N = logits.shape
+    dev = logits.device
+    idx = torch.empty(B, k, device=dev, dtype=torch.int32) if idx is None else idx
+    w = torch.empty(B, k, device=dev, dtype=torch.float32) if w is None else w
+    _check("moe_route_topk", lib().moe_route_topk(_ptr(logits), B, N, k, int(bool(renorm)), _ptr(idx),
+                                                  _ptr(w), _stream(stream)))
+    return idx, w
+
+
+def route_oea(logits, k0: int, p: float, k: int, out=None, stream=None):
+    """Returns dict idx, w, n_base, mask, T (device tensors)."""
+    B, N = logits.shape
+    dev = logits.device
+    if out is None:
+        out = dict(idx=torch.empty(B, k, device=dev, dtype=torch.int32),
+                   w=torch.empty(B, k, device=dev, dtype=torch.float32),
+                   n_base=torch.empty(B, device=dev, dtype=torch.int32),
+                   mask=torch.empty((N + 31) // 32, device=dev, dtype=torch.int32),
+                   T=torch.empty(1, device=dev, dtype=torch.int32))
+    _check("moe_route_oea", lib().moe_route_oea(_ptr(logits), B, N, k0, float(p), k, _ptr(out["idx"]),
+                                                _ptr(out["w"]), _ptr(out.get("n_base")),
+                                                _ptr(out.get("mask")), _ptr(out.get("T")),
+                                                _stream(stream)))
+    return out
+
+
+def dispatch(idx, N: int, out=None, stream=None):
+    """Returns dict cnt, offsets, perm, active, T (device tensors)."""
+    B, k = idx.shape
+    dev = idx.device
+    if out is None:
+        out = dict(cnt=torch.empty(N, device=dev, dtype=torch.int32),
+                   offsets=torch.empty(N + 1, device=dev, dtype=torch.int32),
+                   perm=torch.empty(B * k, device=dev, dtype=torch.int32),
+                   active=torch.empty(N, device=dev, dtype=torch.int32),
+                   T=torch.empty(1, device=dev, dtype=torch.int32))
+    _check("moe_dispatch", lib().moe_dispatch(_ptr(idx), B, N, k, _ptr(out["cnt"]), _ptr(out["offsets"]),
+                                              _ptr(out["perm"]), _ptr(out["active"]), _ptr(out["T"]),
+                                              _stream(stream)))
+    return out
+
+
+def ffn_workspace_bytes(B: int, k: int, H: int, I: int) -> int:
+    return int(lib().moe_ffn_workspace_bytes(B, k, H, I))
+
+
+def expert_ffn(table, N: int, H: int, I: int, x, idx, w, disp, y=None, ws=None, stream=None):
+    B, k = idx.shape
+    dev = x.device
+    if y is None:
+        y = torch.empty(B, H, device=dev, dtype=torch.float32)
+    nbytes = ffn_workspace_bytes(B, k, H, I)
+    if ws is None:
+        ws = torch.empty(nbytes, device=dev, dtype=torch.uint8)
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        _ptr(table), N, H, I, _ptr(x), _x_dtype(x), _ptr(idx), _ptr(w), _ptr(disp["offsets"]),
+        _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]), B, k, _ptr(y), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+    return y
+
+
+def handle_publish(table, e: int, h: ExpertHandle, stream=None):
+    _check("moe_handle_publish", lib().moe_handle_publish(_ptr(table), e, ctypes.byref(h), _stream(stream)))
+
+
+def quantize_int4_g128(w_bf16, q=None, scales=None, stream=None):
+    rows, cols = w_bf16.shape
+    dev = w_bf16.device
+    q = torch.empty(rows, cols // 2, device=dev, dtype=torch.uint8) if q is None else q
+    scales = torch.empty(rows, cols // 128, device=dev, dtype=torch.int16) if scales is None else scales
+    _check("moe_quantize_int4_g128", lib().moe_quantize_int4_g128(_ptr(w_bf16), rows, cols, _ptr(q),
+                                                                  _ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def hotness_ema(S, cnt, alpha: float, stream=None):
+    _check("moe_hotness_ema", lib().moe_hotness_ema(_ptr(S), _ptr(cnt), S.shape[0], float(alpha),
+                                                    _stream(stream)))
+    return S
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()

@@ -1,0 +1,146 @@
+// libmoe C ABI: host-side argument checks, then kernel launches on the
+// caller's stream.  No call allocates memory or synchronises; invalid
+// arguments return a negative status before anything is enqueued.
+#include <stdio.h>
+#include <string.h>
+
+#include "internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* msg) {
+    snprintf(g_last_error, sizeof g_last_error, "%s", msg);
+    return status;
+}
+
+int hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return MOE_OK;
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(e));
+    return MOE_EHIP;
+}
+
+int check_sizes(int B, int N, int k) {
+    if (N < 1 || N > moe::kMaxExperts) return fail(MOE_EINVAL, "N must be in [1, 128]");
+    if (k < 1 || k > N || k > moe::kMaxTopK) return fail(MOE_EINVAL, "k must be in [1, min(N, 16)]");
+    if (B < 1) return fail(MOE_EINVAL, "B must be >= 1");
+    if (B > moe::kMaxBatch) return fail(MOE_EUNSUPPORTED, "B > 128 is not supported");
+    return MOE_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+MOE_API const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_EUNSUPPORTED: return "unsupported size";
+        case MOE_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+MOE_API const char* moe_last_error(void) { return g_last_error; }
+
+MOE_API int moe_router_logits(const void* x, int x_dtype, const float* w_r, int B, int H, int N,
+                              float* logits, void* stream) {
+    if (!x || !w_r || !logits) return fail(MOE_EINVAL, "null pointer");
+    if (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16) return fail(MOE_EINVAL, "bad x_dtype");
+    if (N < 1 || N > moe::kMaxExperts) return fail(MOE_EINVAL, "N must be in [1, 128]");
+    if (B < 1) return fail(MOE_EINVAL, "B must be >= 1");
+    if (B > moe::kMaxBatch) return fail(MOE_EUNSUPPORTED, "B > 128 is not supported");
+    if (H < 8 || H % 8) return fail(MOE_EINVAL, "H must be a positive multiple of 8");
+    return hip_status(moe::launch_router_logits(x, x_dtype, w_r, B, H, N, logits, as_stream(stream)),
+                      "moe_router_logits");
+}
+
+MOE_API int moe_route_topk(const float* logits, int B, int N, int k, int renorm, int32_t* idx,
+                           float* w, void* stream) {
+    if (!logits || !idx || !w) return fail(MOE_EINVAL, "null pointer");
+    int st = check_sizes(B, N, k);
+    if (st) return st;
+    return hip_status(moe::launch_route(logits, B, N, k, k, 1.0f, 0, renorm ? 1 : 0, idx, w,
+                                        nullptr, nullptr, nullptr, as_stream(stream)),
+                      "moe_route_topk");
+}
+
+MOE_API int moe_route_oea(const float* logits, int B, int N, int k0, float p, int k, int32_t* idx,
+                          float* w, int32_t* n_base, uint32_t* sbase_mask, int32_t* T,
+                          void* stream) {
+    if (!logits || !idx || !w) return fail(MOE_EINVAL, "null pointer");
+    int st = check_sizes(B, N, k);
+    if (st) return st;
+    if (k0 < 1 || k0 > k) return fail(MOE_EINVAL, "k0 must be in [1, k]");
+    if (!(p > 0.0f)) return fail(MOE_EINVAL, "p must be > 0 (p >= 1 disables top-p)");
+    return hip_status(moe::launch_route(logits, B, N, k, k0, p, 1, 1, idx, w, n_base, sbase_mask, T,
+                                        as_stream(stream)),
+                      "moe_route_oea");
+}
+
+MOE_API int moe_dispatch(const int32_t* idx, int B, int N, int k, int32_t* cnt, int32_t* offsets,
+                         int32_t* perm, int32_t* active, int32_t* T, void* stream) {
+    if (!idx || !cnt || !offsets || !perm || !active || !T) return fail(MOE_EINVAL, "null pointer");
+    int st = check_sizes(B, N, k);
+    if (st) return st;
+    return hip_status(moe::launch_dispatch(idx, B, N, k, cnt, offsets, perm, active, T,
+                                           as_stream(stream)),
+                      "moe_dispatch");
+}
+
+MOE_API size_t moe_ffn_workspace_bytes(int B, int k, int H, int I) {
+    if (B < 1 || k < 1 || H < 1 || I < 1) return 0;
+    return moe::ffn_workspace_bytes(B, k, H, I);
+}
+
+MOE_API int moe_expert_ffn(const moe_expert_handle* table, int N, int H, int I, const void* x,
+                           int x_dtype, const int32_t* idx, const float* w, const int32_t* offsets,
+                           const int32_t* perm, const int32_t* active, const int32_t* T, int B,
+                           int k, float* y, void* ws, size_t ws_bytes, void* stream) {
+    if (!table || !x || !idx || !w || !offsets || !perm || !active || !T || !y || !ws)
+        return fail(MOE_EINVAL, "null pointer");
+    int st = check_sizes(B, N, k);
+    if (st) return st;
+    if (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16) return fail(MOE_EINVAL, "bad x_dtype");
+    if (H < 8 || H % 8 || I < 8 || I % 8) return fail(MOE_EINVAL, "H and I must be positive multiples of 8");
+    if (H > 16384 || I > 16384) return fail(MOE_EUNSUPPORTED, "H and I above 16384 are not supported");
+    if (ws_bytes < moe::ffn_workspace_bytes(B, k, H, I)) return fail(MOE_EINVAL, "workspace too small");
+    moe::FfnArgs a{};
+    a.table = table;
+    a.N = N; a.H = H; a.I = I; a.B = B; a.k = k;
+    a.x = x; a.x_dtype = x_dtype;
+    a.idx = idx; a.w = w; a.offsets = offsets; a.perm = perm; a.active = active; a.T = T;
+    a.y = y;
+    return hip_status(moe::launch_expert_ffn(a, ws, as_stream(stream)), "moe_expert_ffn");
+}
+
+MOE_API int moe_handle_publish(moe_expert_handle* table, int e, const moe_expert_handle* h,
+                               void* stream) {
+    if (!table || !h) return fail(MOE_EINVAL, "null pointer");
+    if (e < 0 || e >= moe::kMaxExperts) return fail(MOE_EINVAL, "expert index out of range");
+    if (h->fmt != MOE_W_F32 && h->fmt != MOE_W_BF16 && h->fmt != MOE_W_INT4_G128)
+        return fail(MOE_EINVAL, "bad weight format");
+    if (!h->w_gate || !h->w_up || !h->w_down) return fail(MOE_EINVAL, "null weight pointer");
+    if (h->fmt == MOE_W_INT4_G128 && (h->group != 128 || !h->s_gate || !h->s_up || !h->s_down))
+        return fail(MOE_EINVAL, "INT4 handle needs group 128 and scale pointers");
+    return hip_status(moe::launch_handle_publish(table, e, *h, as_stream(stream)), "moe_handle_publish");
+}
+
+MOE_API int moe_quantize_int4_g128(const uint16_t* w, int rows, int cols, uint8_t* q,
+                                   uint16_t* scales, void* stream) {
+    if (!w || !q || !scales) return fail(MOE_EINVAL, "null pointer");
+    if (rows < 1 || cols < 128 || cols % 128) return fail(MOE_EINVAL, "cols must be a positive multiple of 128");
+    return hip_status(moe::launch_quantize_int4(w, rows, cols, q, scales, as_stream(stream)),
+                      "moe_quantize_int4_g128");
+}
+
+MOE_API int moe_hotness_ema(float* S, const int32_t* cnt, int N, float alpha, void* stream) {
+    if (!S || !cnt) return fail(MOE_EINVAL, "null pointer");
+    if (N < 1 || N > moe::kMaxExperts) return fail(MOE_EINVAL, "N must be in [1, 128]");
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(MOE_EINVAL, "alpha must be in [0, 1]");
+    return hip_status(moe::launch_hotness_ema(S, cnt, N, alpha, as_stream(stream)), "moe_hotness_ema");
+}

@@ -1,0 +1,49 @@
+// Internal declarations shared by the libmoe translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 128;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxBatch = 128;
+
+// Launchers: called after argument validation; return the launch status.
+hipError_t launch_router_logits(const void* x, int x_dtype, const float* w_r, int B, int H, int N,
+                                float* logits, hipStream_t s);
+hipError_t launch_route(const float* logits, int B, int N, int k, int k0, float p, int oea,
+                        int renorm, int32_t* idx, float* w, int32_t* n_base, uint32_t* mask,
+                        int32_t* T, hipStream_t s);
+hipError_t launch_dispatch(const int32_t* idx, int B, int N, int k, int32_t* cnt,
+                           int32_t* offsets, int32_t* perm, int32_t* active, int32_t* T,
+                           hipStream_t s);
+hipError_t launch_hotness_ema(float* S, const int32_t* cnt, int N, float alpha, hipStream_t s);
+hipError_t launch_handle_publish(moe_expert_handle* table, int e, moe_expert_handle h,
+                                 hipStream_t s);
+hipError_t launch_quantize_int4(const uint16_t* w, int rows, int cols, uint8_t* q,
+                                uint16_t* scales, hipStream_t s);
+
+struct FfnArgs {
+    const moe_expert_handle* table;
+    int N, H, I, B, k;
+    const void* x;
+    int x_dtype;
+    const int32_t* idx;
+    const float* w;
+    const int32_t* offsets;
+    const int32_t* perm;
+    const int32_t* active;
+    const int32_t* T;
+    float* y;
+    float* hbuf;   // [B*k, I] fp32: SwiGLU activations per routed pair
+    float* dbuf;   // [B*k, H] fp32: weighted down-projection per routed pair
+};
+
+size_t ffn_workspace_bytes(int B, int k, int H, int I);
+hipError_t launch_expert_ffn(const FfnArgs& a, void* ws, hipStream_t s);
+
+}  // namespace moe

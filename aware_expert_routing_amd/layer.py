@@ -1,0 +1,111 @@
+"""A decode MoE layer assembled from the libmoe entry points.
+
+The layer owns device weights, the per-expert handle table (page "DynaExq",
+section 2.2: stable handles resolved at run time) and preallocated buffers,
+so a forward call enqueues kernels only: router logits -> vanilla top-k or
+OEA routing (page "Opportunistic Expert Activation (OEA) - L2", section 2 Q2)
+-> dispatch -> expert FFN with weighted combine.  T and every size that
+depends on the routing stay on the device.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class ExpertTensors:
+    fmt: int
+    gate: torch.Tensor
+    up: torch.Tensor
+    down: torch.Tensor
+    s_gate: torch.Tensor | None = None
+    s_up: torch.Tensor | None = None
+    s_down: torch.Tensor | None = None
+
+    def handle(self) -> L.ExpertHandle:
+        h = L.ExpertHandle()
+        h.fmt = self.fmt
+        h.group = 128 if self.fmt == L.MOE_W_INT4_G128 else 0
+        h.w_gate, h.w_up, h.w_down = self.gate.data_ptr(), self.up.data_ptr(), self.down.data_ptr()
+        if self.fmt == L.MOE_W_INT4_G128:
+            h.s_gate, h.s_up, h.s_down = self.s_gate.data_ptr(), self.s_up.data_ptr(), self.s_down.data_ptr()
+        h.reserved = 0
+        return h
+
+
+@dataclass
+class Buffers:
+    """Per-batch-size device buffers for one forward call."""
+    B: int
+    logits: torch.Tensor
+    route: dict
+    disp: dict
+    y: torch.Tensor
+    ws: torch.Tensor
+    extra: dict = field(default_factory=dict)
+
+
+class MoELayer:
+    def __init__(self, H: int, I: int, N: int, k: int, w_r: torch.Tensor | None,
+                 experts: list[ExpertTensors], device="cuda"):
+        self.H, self.I, self.N, self.k = H, I, N, k
+        self.w_r = w_r
+        self.experts = list(experts)
+        self.device = torch.device(device)
+        self.table = torch.zeros(N * L.HANDLE_BYTES, dtype=torch.uint8, device=self.device)
+        for e, ex in enumerate(self.experts):
+            L.handle_publish(self.table, e, ex.handle())
+        self._bufs: dict[int, Buffers] = {}
+
+    def publish(self, e: int, ex: ExpertTensors, stream=None):
+        """Point expert e at a new weight version (ordered on the stream)."""
+        self.experts[e] = ex
+        L.handle_publish(self.table, e, ex.handle(), stream)
+
+    def buffers(self, B: int) -> Buffers:
+        b = self._bufs.get(B)
+        if b is None:
+            dev, N, k = self.device, self.N, self.k
+            i32 = dict(device=dev, dtype=torch.int32)
+            route = dict(idx=torch.empty(B, k, **i32), w=torch.empty(B, k, device=dev, dtype=torch.float32),
+                         n_base=torch.empty(B, **i32), mask=torch.empty((N + 31) // 32, **i32),
+                         T=torch.empty(1, **i32))
+            disp = dict(cnt=torch.empty(N, **i32), offsets=torch.empty(N + 1, **i32),
+                        perm=torch.empty(B * k, **i32), active=torch.empty(N, **i32), T=torch.empty(1, **i32))
+            ws = torch.empty(L.ffn_workspace_bytes(B, k, self.H, self.I), device=dev, dtype=torch.uint8)
+            b = Buffers(B, torch.empty(B, N, device=dev, dtype=torch.float32), route, disp,
+                        torch.empty(B, self.H, device=dev, dtype=torch.float32), ws)
+            self._bufs[B] = b
+        return b
+
+    def route(self, logits: torch.Tensor, mode: str, k0: int = 0, p: float = 1.0,
+              buf: Buffers | None = None, stream=None) -> Buffers:
+        B = logits.shape[0]
+        buf = buf or self.buffers(B)
+        if mode == "topk":
+            L.route_topk(logits, self.k, True, buf.route["idx"], buf.route["w"], stream)
+        elif mode == "oea":
+            L.route_oea(logits, k0, p, self.k, buf.route, stream)
+        else:
+            raise ValueError(mode)
+        L.dispatch(buf.route["idx"], self.N, buf.disp, stream)
+        return buf
+
+    def ffn(self, x: torch.Tensor, buf: Buffers, stream=None) -> torch.Tensor:
+        return L.expert_ffn(self.table, self.N, self.H, self.I, x, buf.route["idx"], buf.route["w"],
+                            buf.disp, buf.y, buf.ws, stream)
+
+    def forward(self, x: torch.Tensor, mode: str = "oea", k0: int = 3, p: float = 1.0,
+                logits: torch.Tensor | None = None, stream=None) -> Buffers:
+        """Whole layer.  If `logits` is given the router GEMV is skipped."""
+        B = x.shape[0]
+        buf = self.buffers(B)
+        if logits is None:
+            logits = L.router_logits(x, self.w_r, buf.logits, stream)
+        self.route(logits, mode, k0, p, buf, stream)
+        self.ffn(x, buf, stream)
+        return buf

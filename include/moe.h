@@ -1,0 +1,208 @@
+/*
+ * moe.h -- C ABI of libmoe, a decode-time Mixture-of-Experts layer for
+ * AMD Instinct MI355X (gfx950) with Opportunistic Expert Activation routing.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless the comment says (host).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it; the call returns without synchronising and
+ *     never allocates device or host memory.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns a negative status and enqueues nothing.
+ *   - Results that size later work (T, counts, offsets) stay in device memory;
+ *     no call reads them back to the host.
+ *   - The caller owns every buffer.  Buffers must not overlap unless stated.
+ *   - Limits: 1 <= N <= 128 experts, 1 <= k <= min(N, 16), 1 <= B <= 128.
+ *   - Non-finite logits, and idx entries outside [-1, N) or repeated within a
+ *     token's row, are undefined behaviour (not checked on the device).
+ *
+ * Page citations
+ *   [OEA]  "Opportunistic Expert Activation (OEA) - L2" (zhaifeiyue.github.io)
+ *   [DYN]  "Dynamic Expert Quantization for Scalable MoE Inference" notes
+ *          (hotelren.com), sections 2.1-2.5 / 3.1-3.5.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,         /* argument out of range or null pointer           */
+    MOE_EUNSUPPORTED = -2,   /* valid but beyond this build's limits (B > 128)  */
+    MOE_EHIP = -3            /* a HIP runtime call or kernel launch failed      */
+};
+
+/* activation element type */
+enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
+
+/* expert weight formats */
+enum {
+    MOE_W_F32 = 0,           /* fp32                                            */
+    MOE_W_BF16 = 1,          /* bf16                                            */
+    MOE_W_INT4_G128 = 2      /* symmetric INT4, groups of 128 input columns,    */
+                             /* fp16 scales (see moe_quantize_int4_g128)        */
+};
+
+/*
+ * Per-expert stable handle [DYN section 2.2 "versioned expert residency" /
+ * 3.2: a handle's identity never changes; it resolves at run time to the
+ * active version's pointer and quantisation parameters, so a version change
+ * rewrites the handle and never the kernel arguments].
+ *
+ * Layouts (row-major, [out, in]):
+ *   w_gate, w_up : [I, H]     w_down : [H, I]
+ *   MOE_W_F32/BF16: one element per weight.
+ *   MOE_W_INT4_G128: bytes [rows, cols/2]; each byte holds two weights, the
+ *     even column in the low nibble, as the unsigned nibble q + 8 with
+ *     q in [-8, 7]; weight = q * s where s (fp16 bits) is scales[row, col/128].
+ *     s_gate, s_up : [I, H/128]   s_down : [H, I/128]; NULL for other formats.
+ * The table is an array of N handles in device memory.  64 bytes each.
+ */
+typedef struct moe_expert_handle {
+    int32_t fmt;             /* MOE_W_*                                         */
+    int32_t group;           /* 128 for MOE_W_INT4_G128, else 0                 */
+    const void *w_gate;
+    const void *w_up;
+    const void *w_down;
+    const uint16_t *s_gate;
+    const uint16_t *s_up;
+    const uint16_t *s_down;
+    int64_t reserved;        /* keeps the record at 64 bytes; set to 0          */
+} moe_expert_handle;
+
+/*
+ * Router logits [OEA section 2 Q1: each token's router scores over N experts].
+ *   logits[b, e] = sum_h x[b, h] * w_r[e, h], accumulated in fp32.
+ *   x      : [B, H], element type x_dtype (MOE_DT_F32 or MOE_DT_BF16)
+ *   w_r    : [N, H] fp32
+ *   logits : [B, N] fp32 (written)
+ * H must be a multiple of 8.
+ */
+int moe_router_logits(const void *x, int x_dtype, const float *w_r, int B, int H, int N,
+                      float *logits, void *stream);
+
+/*
+ * Vanilla top-k routing [OEA section 2 Q1: each token routes to k of N
+ * experts by router score].
+ *   Ranking is (logit descending, expert index ascending).
+ *   idx : [B, k] int32, the k best experts of each token in rank order.
+ *   w   : [B, k] fp32.  renorm != 0: softmax restricted to the kept experts
+ *         (sums to 1); renorm == 0: the full softmax probability.
+ */
+int moe_route_topk(const float *logits, int B, int N, int k, int renorm, int32_t *idx,
+                   float *w, void *stream);
+
+/*
+ * OEA routing [OEA section 2 Q2 and section 3 (Algorithm 1 flow); section 5
+ * Figure 3 for the simplified form].
+ *   Phase 1: t_i = length of the shortest rank prefix whose softmax mass
+ *     reaches p (the crossing expert included; p >= 1 turns top-p off, so
+ *     t_i = N); n_i = min(k0, t_i); token i's baseline is its top n_i experts.
+ *     S_base = union of the baselines, T = |S_base|.
+ *   Phase 2: token i keeps the first min(k, T) members of S_base in its own
+ *     rank order (its baseline first, then lower-ranked experts already in
+ *     S_base); the kept softmax scores are renormalised to sum to 1.
+ *   The top-p decision uses a fixed fp32 arithmetic so it is reproducible:
+ *     m = top logit, e_j = exp(l_j - m) by Cody-Waite reduction and a
+ *     degree-7 Taylor polynomial (0 below -80), Z = pairwise tree sum over
+ *     128 slots in expert order, prefix sums in rank order, test c >= p * Z.
+ *   idx        : [B, k] int32 in rank order, -1 in unused slots
+ *   w          : [B, k] fp32, 0 in unused slots
+ *   n_base     : [B] int32, n_i (may be NULL)
+ *   sbase_mask : [ceil(N/32)] uint32, bit e%32 of word e/32 set iff e in S_base
+ *                (may be NULL)
+ *   T          : [1] int32, |S_base| (may be NULL)
+ * Requires 1 <= k0 <= k and p > 0.
+ */
+int moe_route_oea(const float *logits, int B, int N, int k0, float p, int k, int32_t *idx,
+                  float *w, int32_t *n_base, uint32_t *sbase_mask, int32_t *T, void *stream);
+
+/*
+ * Dispatch [OEA section 4, Eq. 2: cnt_i tokens per expert, T = number of
+ * experts with cnt_i > 0; section 7: inserted before the expert dispatch].
+ *   cnt     : [N]   tokens routed to each expert
+ *   offsets : [N+1] exclusive prefix sum of cnt (offsets[N] = routed pairs)
+ *   perm    : [B*k] pair ids token*k + slot sorted by (expert, token);
+ *             entries past offsets[N] are -1
+ *   active  : [N]   experts with cnt > 0 in ascending order, then -1
+ *   T       : [1]   number of active experts
+ * idx entries outside [0, N) (e.g. -1) are skipped.
+ */
+int moe_dispatch(const int32_t *idx, int B, int N, int k, int32_t *cnt, int32_t *offsets,
+                 int32_t *perm, int32_t *active, int32_t *T, void *stream);
+
+/* Workspace bytes moe_expert_ffn needs for these sizes (host call). */
+size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
+
+/*
+ * Expert FFN and weighted combine [OEA section 4, Eq. 2 and check 4: every
+ * activated expert's weights are fetched once; the cost is b*T + a*sum(cnt)].
+ *   For every active expert e and each routed pair (token i, slot s):
+ *     g = W_gate,e x_i, u = W_up,e x_i, a = silu(g) * u, d = W_down,e a,
+ *     y_i = sum over token i's filled slots of w[i, s] * d.
+ *   table  : [N] moe_expert_handle (device); each expert's format may differ
+ *   x      : [B, H] (x_dtype); with bf16/INT4 experts activations are used in
+ *            bf16 (fp32 inputs are rounded to nearest even)
+ *   idx, w : routing output [B, k]; offsets, perm, active, T: dispatch output
+ *   y      : [B, H] fp32, overwritten
+ *   ws     : workspace of at least moe_ffn_workspace_bytes(B, k, H, I) bytes
+ * Accumulation is fp32.  H and I must be multiples of 8 (of 128 when any
+ * expert is INT4).  Each active expert's weights are streamed from HBM once
+ * per call (tokens are processed in groups of up to 16 per pass).
+ */
+int moe_expert_ffn(const moe_expert_handle *table, int N, int H, int I, const void *x,
+                   int x_dtype, const int32_t *idx, const float *w, const int32_t *offsets,
+                   const int32_t *perm, const int32_t *active, const int32_t *T, int B, int k,
+                   float *y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Publish a new version of expert e's handle [DYN section 2.2 / 3.2
+ * "publish-then-switch": a version becomes visible only after its data is
+ * complete; the forward path keeps using the previous version until then].
+ *   h (host) is copied by value into the launch, so it may be freed on return.
+ *   The write is ordered on `stream`: work enqueued on the stream before the
+ *   call sees the old handle, work after it sees the new one.  A version
+ *   copied on another stream must be made visible to `stream` (an event wait)
+ *   before publishing.  The old weights may be freed only after work that can
+ *   read them has completed.
+ */
+int moe_handle_publish(moe_expert_handle *table, int e, const moe_expert_handle *h, void *stream);
+
+/*
+ * Build the INT4 low-precision version of a bf16 matrix [DYN section 3.2:
+ * each expert keeps a high- and a low-precision version; section 3.4:
+ * versions are prepacked in kernel-ready form].
+ *   w      : [rows, cols] bf16 bits, cols a multiple of 128
+ *   q      : [rows, cols/2] packed nibbles (layout as in moe_expert_handle)
+ *   scales : [rows, cols/128] fp16 bits
+ *   Per row and group of 128 columns: s = fp16(absmax / 7) (fp32 quotient,
+ *   rounded to nearest even), q = clamp(rint(w / s), -8, 7) with the fp32
+ *   quotient (q = 0 when s = 0).
+ */
+int moe_quantize_int4_g128(const uint16_t *w, int rows, int cols, uint8_t *q, uint16_t *scales,
+                           void *stream);
+
+/*
+ * Hotness estimate [DYN section 2.5: per-expert counters c folded into a
+ * smoothed score S <- alpha * S + (1 - alpha) * c].
+ *   S : [N] fp32, updated in place;  cnt : [N] int32 (e.g. dispatch's cnt).
+ */
+int moe_hotness_ema(float *S, const int32_t *cnt, int N, float alpha, void *stream);
+
+/* Static description of a status code (host). */
+const char *moe_status_str(int status);
+
+/* Message of the last failure on the calling thread ("" if none) (host). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,195 @@
+"""GPU parity of the expert FFN (SwiGLU + weighted combine) and of the whole
+decode layer against the CPU oracle.
+
+Bar: max|y - y_ref| <= 1e-2 * rms(y_ref) for bf16 experts (fp32 accumulate),
+<= 2e-2 * rms(y_ref) for INT4 group-128 experts, and a tighter 1e-4 for fp32
+experts (fp32 products and sums over at most a few thousand terms).
+Page "Opportunistic Expert Activation (OEA) - L2", section 4 (Eq. 2, check 4);
+page "DynaExq", section 2.2 / 3.2 (handles, INT4 low-precision versions).
+"""
+import numpy as np
+import pytest
+import torch
+
+import aware_expert_routing_amd as moe
+import oracle
+import synth
+from gpu_util import DEV, bf16_dev, build_layer, max_err_over_rms
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2, "int4": 2e-2}
+
+
+def _run_and_check(layer, host, x_np, x_dev, logits, mode, k0, p, tol, tokens=None):
+    buf = layer.forward(x_dev, mode, k0, p, logits=torch.from_numpy(logits).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.route(logits, layer.k, oea=(mode == "oea"), k0=k0, p=p)
+    assert np.array_equal(buf.route["idx"].cpu().numpy(), ref["idx"])
+    rows = np.arange(x_np.shape[0]) if tokens is None else np.asarray(tokens)
+    yref = oracle.expert_ffn(host, layer.H, layer.I, x_np[rows], ref["idx"][rows], ref["w"][rows])
+    err, rms = max_err_over_rms(buf.y[torch.from_numpy(rows).to(DEV)], yref)
+    assert err <= tol * rms, (err, rms, err / rms)
+    return buf, err / rms
+
+
+def _x(seed, B, H, dtype):
+    x = synth.activations(seed, B, H)
+    if dtype == "bf16":
+        xb = synth.to_bf16_bits(x)
+        return synth.bf16_bits_to_f32(xb), bf16_dev(xb)
+    return x, torch.from_numpy(x).to(DEV)
+
+
+def test_tiny_fp32_layer_vanilla_and_oea():
+    N, k, H, I, B = 16, 4, 256, 128, 4
+    layer, host = build_layer(N, k, H, I, 1, fmt="f32", with_router=False)
+    x, xd = _x(1, B, H, "f32")
+    for scale in (1.0, 8.0):
+        logits = synth.logits(1, B, N, scale)
+        _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL["f32"])
+        _run_and_check(layer, host, x, xd, logits, "oea", 2, 0.7, TOL["f32"])
+
+
+@pytest.mark.parametrize("N,k,H,I,B,mode,k0,p", [
+    (16, 4, 520, 136, 24, "topk", 0, 1.0),    # ragged chunks and ragged row tiles
+    (16, 4, 520, 136, 24, "oea", 2, 0.7),
+    (8, 4, 256, 128, 64, "topk", 0, 1.0),     # > 16 tokens per expert: several passes
+    (32, 16, 384, 264, 9, "topk", 0, 1.0),    # k = 16
+    (128, 8, 256, 128, 128, "oea", 3, 1.0),   # B = 128
+    (128, 8, 256, 128, 1, "oea", 3, 1.0),     # B = 1
+    (12, 3, 1024, 640, 5, "oea", 1, 0.9),
+])
+def test_bf16_ffn_shapes(N, k, H, I, B, mode, k0, p):
+    layer, host = build_layer(N, k, H, I, 2, fmt="bf16", with_router=False)
+    x, xd = _x(2, B, H, "bf16")
+    logits = synth.logits(2, B, N, 4.0)
+    _run_and_check(layer, host, x, xd, logits, mode, k0, p, TOL["bf16"])
+
+
+def test_fp32_activations_with_bf16_experts():
+    N, k, H, I, B = 16, 4, 256, 128, 8
+    layer, host = build_layer(N, k, H, I, 3, fmt="bf16", with_router=False)
+    x = synth.activations(3, B, H)
+    # the library rounds fp32 activations to bf16 for bf16 experts; the oracle sees exact x
+    logits = synth.logits(3, B, N)
+    _run_and_check(layer, host, x, torch.from_numpy(x).to(DEV), logits, "topk", 0, 1.0, TOL["bf16"])
+
+
+@pytest.mark.parametrize("int4", ["all", "mixed"])
+def test_int4_and_mixed_experts(int4):
+    N, k, H, I, B = 16, 4, 512, 256, 32
+    which = range(N) if int4 == "all" else range(4, N)       # 4 hot bf16, 12 cold INT4
+    layer, host = build_layer(N, k, H, I, 4, fmt="bf16", int4_experts=which, with_router=False)
+    # the GPU's INT4 bytes equal the oracle's, bit for bit
+    for e in which:
+        for name in ("gate", "up", "down"):
+            assert np.array_equal(getattr(layer.experts[e], name).cpu().numpy(), host[e][name])
+            assert np.array_equal(getattr(layer.experts[e], "s_" + name).cpu().numpy().view(np.uint16),
+                                  host[e]["s_" + name])
+    x, xd = _x(4, B, H, "bf16")
+    logits = (synth.logits(4, B, N, 1.0) + synth.zipf_bias(N, 1.1)[None, :]).astype(np.float32)
+    _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL["int4"])
+    _run_and_check(layer, host, x, xd, logits, "oea", 2, 1.0, TOL["int4"])
+
+
+def test_publish_switches_version():
+    # page "DynaExq" section 2.2: switching a handle changes the version the next call reads
+    N, k, H, I, B = 8, 2, 256, 128, 6
+    layer, host = build_layer(N, k, H, I, 5, fmt="bf16", with_router=False)
+    x, xd = _x(5, B, H, "bf16")
+    logits = synth.logits(5, B, N, 2.0)
+    _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL["bf16"])
+    e = 3
+    mats = synth.expert_weights_bf16(5, e, H, I)
+    qd, he = {}, dict(fmt=oracle.FMT_INT4)
+    for name, m in zip(("gate", "up", "down"), mats):
+        qd[name], qd["s_" + name] = moe.quantize_int4_g128(bf16_dev(m))
+        he[name], he["s_" + name] = oracle.quantize_int4(m)
+    layer.publish(e, moe.ExpertTensors(moe.MOE_W_INT4_G128, qd["gate"], qd["up"], qd["down"],
+                                       qd["s_gate"], qd["s_up"], qd["s_down"]))
+    host = list(host)
+    host[e] = he
+    _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL["int4"])
+
+
+def test_empty_routing_gives_zero_output():
+    N, k, H, I, B = 8, 2, 256, 128, 3
+    layer, _ = build_layer(N, k, H, I, 6, fmt="bf16", with_router=False)
+    x, xd = _x(6, B, H, "bf16")
+    buf = layer.buffers(B)
+    buf.route["idx"].fill_(-1)
+    buf.route["w"].zero_()
+    moe.dispatch(buf.route["idx"], N, buf.disp)
+    buf.y.fill_(7.0)
+    layer.ffn(xd, buf)
+    torch.cuda.synchronize()
+    assert int(buf.disp["T"].item()) == 0
+    assert torch.count_nonzero(buf.y).item() == 0
+
+
+def test_ffn_repeat_runs_are_bit_identical():
+    N, k, H, I, B = 32, 8, 512, 256, 16
+    layer, _ = build_layer(N, k, H, I, 7, fmt="bf16", with_router=False)
+    _, xd = _x(7, B, H, "bf16")
+    logits = torch.from_numpy(synth.logits(7, B, N, 2.0)).to(DEV)
+    y1 = layer.forward(xd, "topk", logits=logits).y.clone()
+    y2 = layer.forward(xd, "topk", logits=logits).y.clone()
+    assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------------------
+# Full-size layers, whole path from x (router GEMV on the GPU), in the launch
+# configuration the benchmark times.
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def qwen30b():
+    s = synth.SHAPES["qwen30b"]
+    layer, host = build_layer(s["N"], s["k"], s["H"], s["I"], 30, fmt="bf16")
+    return layer, host
+
+
+def _routing_margin_ok(logits64, k):
+    """Smallest gap between consecutive ranked logits near the cut; the GPU's
+    fp32 logits must not be able to swap two experts there."""
+    srt = -np.sort(-logits64, axis=1)
+    return float(np.min(srt[:, :k + 1][:, :-1] - srt[:, 1:k + 1]))
+
+
+@pytest.mark.parametrize("mode,k0", [("topk", 0), ("oea", 3), ("oea", 5)])
+def test_qwen30b_layer_b16_full_path(qwen30b, mode, k0):
+    layer, host = qwen30b
+    B = 16
+    x, xd = _x(31, B, layer.H, "bf16")
+    buf = layer.forward(xd, mode, k0, 1.0)
+    torch.cuda.synchronize()
+    glog = buf.logits.cpu().numpy()
+    ref_logits = oracle.router_logits(x.astype(np.float64), layer.w_r.cpu().numpy().astype(np.float64))
+    assert np.abs(glog - ref_logits).max() < 1e-4
+    assert _routing_margin_ok(ref_logits, layer.k) > 1e-4        # no near-tie the fp32 GEMV could flip
+    ref = oracle.route(ref_logits.astype(np.float32), layer.k, oea=(mode == "oea"), k0=k0, p=1.0)
+    assert np.array_equal(buf.route["idx"].cpu().numpy(), ref["idx"])
+    assert int(buf.disp["T"].item()) == oracle.dispatch(ref["idx"], layer.N)["T"]
+    yref = oracle.expert_ffn(host, layer.H, layer.I, x, ref["idx"], ref["w"])
+    err, rms = max_err_over_rms(buf.y, yref)
+    assert err <= TOL["bf16"] * rms, (err, rms)
+
+
+def test_qwen30b_layer_b128_zipf_sampled(qwen30b):
+    # many tokens per hot expert (several passes); oracle on sampled tokens
+    layer, host = qwen30b
+    B = 128
+    x, xd = _x(32, B, layer.H, "bf16")
+    logits = (synth.logits(32, B, layer.N, 0.9) + synth.zipf_bias(layer.N, 1.1)[None, :]).astype(np.float32)
+    _run_and_check(layer, host, x, xd, logits, "oea", 5, 0.7, TOL["bf16"], tokens=[0, 17, 64, 127])
+
+
+def test_qwen235b_layer_sampled():
+    s = synth.SHAPES["qwen235b"]
+    layer, host = build_layer(s["N"], s["k"], s["H"], s["I"], 235, fmt="bf16", with_router=False)
+    B = 32
+    x, xd = _x(33, B, layer.H, "bf16")
+    logits = synth.logits(33, B, layer.N, 0.9)
+    _run_and_check(layer, host, x, xd, logits, "oea", 5, 1.0, TOL["bf16"], tokens=[0, 31])
+    del layer
+    torch.cuda.empty_cache()

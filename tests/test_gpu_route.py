@@ -1,0 +1,180 @@
+"""GPU parity of router logits, vanilla top-k, OEA routing, dispatch, the INT4
+quantiser, the hotness score and handle publishing against the CPU oracle.
+
+Routing decisions (expert sets, slot order, n_i, S_base, T, counts, offsets,
+permutation, active list) must be bit-exact given identical fp32 logits; the
+renormalised gate weights must be within 1e-6.  Page "Opportunistic Expert
+Activation (OEA) - L2", sections 2 Q1/Q2, 3 and 4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import aware_expert_routing_amd as moe
+import oracle
+import synth
+from gpu_util import DEV, bf16_dev, gamma
+
+pytestmark = pytest.mark.gpu
+
+
+def _logits(kind, seed, B, N, scale=1.0, zipf=0.0):
+    if kind == "tied":
+        return synth.tied_logits(seed, B, N, levels=4)
+    l = synth.logits(seed, B, N, scale)
+    if zipf:
+        l = (l + synth.zipf_bias(N, zipf)[None, :]).astype(np.float32)
+    return l
+
+
+TOPK_CASES = [
+    # B, N, k, kind, scale, renorm
+    (4, 16, 4, "normal", 1.0, True), (4, 16, 4, "normal", 8.0, False), (16, 128, 8, "normal", 0.9, True),
+    (16, 128, 8, "tied", 1.0, True), (1, 128, 8, "normal", 1.0, True), (128, 128, 8, "normal", 1.0, True),
+    (128, 128, 16, "normal", 4.0, False), (37, 100, 7, "normal", 2.0, True), (5, 1, 1, "normal", 1.0, True),
+    (9, 33, 16, "tied", 1.0, False), (64, 128, 1, "normal", 1.0, True),
+]
+
+
+@pytest.mark.parametrize("B,N,k,kind,scale,renorm", TOPK_CASES)
+def test_route_topk_parity(B, N, k, kind, scale, renorm):
+    for seed in range(3):
+        l = _logits(kind, seed, B, N, scale)
+        idx, w = moe.route_topk(torch.from_numpy(l).to(DEV), k, renorm)
+        ref = oracle.route(l, k, oea=False, renorm=renorm)
+        assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+        assert np.abs(w.cpu().numpy().astype(np.float64) - ref["w"]).max() <= 1e-6
+
+
+OEA_CASES = [
+    # B, N, k, k0, p, kind, scale, zipf
+    (4, 16, 4, 2, 0.7, "normal", 1.0, 0.0),          # tiny layer
+    (4, 16, 4, 2, 0.7, "normal", 8.0, 0.0),          # sharpened: top-p binds
+    (16, 128, 8, 3, 1.0, "normal", 0.9, 0.0),        # simplified OEA k0=3
+    (16, 128, 8, 5, 1.0, "normal", 0.9, 0.0),
+    (16, 128, 8, 3, 0.5, "normal", 0.9, 1.1),        # Zipf bias, top-p
+    (32, 128, 8, 5, 0.7, "normal", 0.9, 1.1),
+    (64, 128, 8, 3, 0.9, "normal", 4.0, 1.1),
+    (128, 128, 8, 5, 0.5, "normal", 8.0, 0.0),
+    (1, 128, 8, 3, 0.7, "normal", 4.0, 0.0),         # B=1: no piggyback
+    (2, 128, 8, 5, 0.9, "normal", 4.0, 0.0),
+    (16, 128, 8, 3, 1.0, "tied", 1.0, 0.0),          # exact ties
+    (16, 128, 8, 4, 0.6, "tied", 1.0, 0.0),
+    (8, 128, 8, 8, 1.0, "normal", 1.0, 0.0),         # k0 = k: vanilla
+    (128, 128, 16, 7, 0.8, "normal", 6.0, 1.1),      # maximum sizes
+    (11, 40, 12, 2, 0.3, "normal", 3.0, 0.0),
+    (3, 5, 5, 1, 0.9, "normal", 1.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("B,N,k,k0,p,kind,scale,zipf", OEA_CASES)
+def test_route_oea_parity(B, N, k, k0, p, kind, scale, zipf):
+    for seed in range(3):
+        l = _logits(kind, seed, B, N, scale, zipf)
+        out = moe.route_oea(torch.from_numpy(l).to(DEV), k0, p, k)
+        ref = oracle.route(l, k, oea=True, k0=k0, p=p)
+        assert np.array_equal(out["idx"].cpu().numpy(), ref["idx"])
+        assert np.array_equal(out["n_base"].cpu().numpy(), ref["n_base"])
+        assert np.array_equal(out["mask"].cpu().numpy().view(np.uint32), ref["mask"])
+        assert int(out["T"].item()) == ref["T"]
+        assert np.abs(out["w"].cpu().numpy().astype(np.float64) - ref["w"]).max() <= 1e-6
+
+
+def test_topp_branch_is_exercised():
+    # the sharpened / Zipf cases above must actually cut some tokens below k0
+    cut = 0
+    for seed in range(3):
+        l = _logits("normal", seed, 128, 128, 8.0)
+        out = moe.route_oea(torch.from_numpy(l).to(DEV), 5, 0.5, 8)
+        cut += int((out["n_base"].cpu().numpy() < 5).sum())
+    assert cut > 50
+
+
+def test_oea_repeat_runs_are_identical():
+    l = torch.from_numpy(_logits("normal", 4, 128, 128, 4.0, 1.1)).to(DEV)
+    a = moe.route_oea(l, 3, 0.7, 8)
+    b = moe.route_oea(l, 3, 0.7, 8)
+    for key in a:
+        assert torch.equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("B,N,k,mode", [(4, 16, 4, "oea"), (16, 128, 8, "topk"), (16, 128, 8, "oea"),
+                                         (128, 128, 16, "oea"), (128, 128, 8, "topk"), (1, 8, 2, "oea")])
+def test_dispatch_parity(B, N, k, mode):
+    for seed in range(3):
+        l = _logits("normal", seed, B, N, 4.0, 1.1)
+        lt = torch.from_numpy(l).to(DEV)
+        if mode == "oea":
+            idx = moe.route_oea(lt, max(1, k // 3), 0.7, k)["idx"]
+        else:
+            idx = moe.route_topk(lt, k)[0]
+        d = moe.dispatch(idx, N)
+        ref = oracle.dispatch(idx.cpu().numpy(), N)
+        for key in ("cnt", "offsets", "perm", "active"):
+            assert np.array_equal(d[key].cpu().numpy(), ref[key]), key
+        assert int(d["T"].item()) == ref["T"]
+
+
+def test_dispatch_with_empty_slots_and_rows():
+    B, N, k = 6, 16, 4
+    idx = np.array([[3, 5, -1, -1], [-1, -1, -1, -1], [15, 0, 3, -1], [7, -1, -1, -1],
+                    [0, 1, 2, 3], [-1, -1, -1, -1]], np.int32)
+    d = moe.dispatch(torch.from_numpy(idx).to(DEV), N)
+    ref = oracle.dispatch(idx, N)
+    for key in ("cnt", "offsets", "perm", "active"):
+        assert np.array_equal(d[key].cpu().numpy(), ref[key]), key
+    empty = moe.dispatch(torch.full((3, 2), -1, dtype=torch.int32, device=DEV), N)
+    assert int(empty["T"].item()) == 0 and int(empty["offsets"][-1].item()) == 0
+
+
+@pytest.mark.parametrize("B,H,N,dtype", [(4, 256, 16, "f32"), (16, 2048, 128, "bf16"), (128, 2048, 128, "bf16"),
+                                          (33, 4096, 128, "bf16"), (5, 520, 24, "f32")])
+def test_router_logits_within_fp32_bound(B, H, N, dtype):
+    x = synth.activations(5, B, H)
+    wr = synth.router_weight(5, N, H)
+    if dtype == "bf16":
+        xb = synth.to_bf16_bits(x)
+        xd = bf16_dev(xb)
+        xv = synth.bf16_bits_to_f32(xb)
+    else:
+        xd = torch.from_numpy(x).to(DEV)
+        xv = x
+    got = moe.router_logits(xd, torch.from_numpy(wr).to(DEV)).cpu().numpy().astype(np.float64)
+    ref = oracle.router_logits(xv.astype(np.float64), wr.astype(np.float64))
+    bound = gamma(H) * (np.abs(xv.astype(np.float64)) @ np.abs(wr.astype(np.float64)).T)
+    assert np.all(np.abs(got - ref) <= bound + 1e-30)
+
+
+def test_quantizer_bit_exact():
+    rows, cols = 96, 1024
+    w = synth.to_bf16_bits(synth.normal(31, (rows, cols), 0.02))
+    w[0, :128] = 0                                            # all-zero group
+    w[1, :128] = synth.to_bf16_bits(np.full(128, -0.5, np.float32))   # constant negative group
+    w[2, 128:256] = synth.to_bf16_bits(synth.normal(32, 128, 30.0))   # large values
+    q, s = moe.quantize_int4_g128(bf16_dev(w))
+    qr, sr = oracle.quantize_int4(w)
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), sr)
+
+
+def test_hotness_ema_matches_oracle():
+    N = 128
+    S = torch.zeros(N, device=DEV)
+    Sref = np.zeros(N)
+    for step in range(20):
+        c = synth.rng(40, step).integers(0, 17, N).astype(np.int32)
+        moe.hotness_ema(S, torch.from_numpy(c).to(DEV), 0.9)
+        Sref = oracle.hotness_ema(Sref, c, 0.9)
+    assert np.allclose(S.cpu().numpy(), Sref, rtol=1e-5, atol=1e-5)
+
+
+def test_handle_publish_writes_the_record():
+    table = torch.zeros(4 * moe.HANDLE_BYTES, dtype=torch.uint8, device=DEV)
+    h = moe.ExpertHandle()
+    h.fmt, h.group = moe.MOE_W_INT4_G128, 128
+    h.w_gate, h.w_up, h.w_down = 0x1000, 0x2000, 0x3000
+    h.s_gate, h.s_up, h.s_down = 0x4000, 0x5000, 0x6000
+    moe.handle_publish(table, 2, h)
+    rec = table.cpu().numpy()[2 * 64:3 * 64].tobytes()
+    assert rec == bytes(h)
+    assert np.all(table.cpu().numpy()[:128] == 0)
