@@ -3,28 +3,32 @@
 // Page "Opportunistic Expert Activation (OEA) - L2", section 4 (Eq. 2 and
 // check 4): in decode each activated expert costs a fixed weight fetch b
 // plus a small per-token term a, and batched kernels must still load every
-// activated expert's weights.  This file therefore streams each active
-// expert's gate/up/down weights from HBM once per call, with all of the
-// expert's tokens (up to 16 per pass) applied to every weight that is loaded.
+// activated expert's weights.  This file streams each active expert's
+// gate/up/down weights from HBM once per call (per pass of up to 8 of the
+// expert's tokens) and applies every token of the pass to each loaded weight.
 // Page "DynaExq", section 2.2 / 3.2: each expert is reached through a handle
 // giving the active version's pointers and quantisation parameters, resolved
-// here per work item, so experts of one layer may be bf16, fp32 or INT4.
+// per work item, so one layer may mix bf16, fp32 and INT4 experts.
 //
-// Work decomposition (memory-bound GEMV, not a GEMM):
-//   * phase A (gate/up + SwiGLU): items are (active expert, 16 rows of I);
-//     a 256-thread workgroup takes a contiguous range of items; each wave
-//     owns 4 rows, 16 lanes per row, and every lane reads 16 contiguous bytes
-//     per chunk of 256 row bytes, so one wave instruction reads four 256-byte
-//     row segments.  A lane handles the gate row and the up row of the same
-//     index, so the SwiGLU product needs no exchange.
+// Work decomposition (a memory-bound GEMV, not a GEMM):
+//   * phase A (gate/up + SwiGLU): work items are (active expert, 16 rows of
+//     I); a lane owns the gate row and the up row of the same index, so the
+//     SwiGLU product needs no exchange.  16 lanes share a row: lane g reads
+//     bytes [256c + 16g, 256c + 16g + 16) of the row for chunks c, so one
+//     wave instruction reads four 256-byte row segments.
 //   * phase B (down + routing weight): items are (active expert, 32 rows of
-//     H); each lane handles two rows.
+//     H); a lane owns two rows.
 //   * combine: y[i] = sum over token i's filled slots, in slot order.
-// Activations of the expert's tokens are staged once per item range in LDS
-// in the weight format's layout (fp32 activations as bf16 hi/lo pairs); partial dot products are reduced across the
-// 16 lanes of a row with DPP moves.  Arithmetic is fp32: bf16 pairs use
-// v_dot2_f32_bf16, INT4 nibbles become bf16 (128 + nibble) pairs by bit
-// operations and the offset is removed with a per-block activation sum.
+// Each 256-thread workgroup takes a contiguous range of items.  A wave keeps
+// the weight loads of its next block of chunks in flight while it computes
+// the current block, and at the end of an item it has already issued the
+// loads of the next item's first block, so the weight stream does not stop
+// at item boundaries.  Activations of the pass's tokens are staged in LDS in
+// the weight format's layout (fp32 activations as bf16 hi/lo pairs for
+// bf16/INT4 weights); partial sums are reduced across the 16 lanes of a row
+// with DPP moves.  bf16 products use v_dot2_f32_bf16; INT4 nibbles become the
+// bf16 pair (128 + u, 128 + u') by bit operations, and the offset is removed
+// with the staged sum of the activations of each 32-column block.
 #include "internal.h"
 
 namespace moe {
@@ -36,23 +40,34 @@ constexpr int kRowsPerInstr = kWave / kLanesPerRow;   // 4
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;               // 4
 constexpr int kChunkBytes = kLanesPerRow * 16;          // 256 row bytes per chunk
-constexpr int kMaxTok = 16;                             // tokens per pass
-constexpr int kMaxTokInt4 = 4;                          // INT4: fewer live registers
-constexpr int kRowsA = kWaves * kRowsPerInstr;          // 16 rows of I per item
-constexpr int kRowsPerLaneB = 2;
-constexpr int kRowsB = kWaves * kRowsPerInstr * kRowsPerLaneB;   // 32 rows of H per item
-constexpr int kLdsBytes = 64 * 1024;
-constexpr int kChunkBlock = 4;                          // chunks in flight per row
+constexpr int kMaxTok = 8;                              // tokens per pass
+constexpr int kMaxTokInt4 = 2;                          // INT4: fewer live registers
+constexpr int kLdsBytes = 64 * 1024 - 256;              // staged activations (dynamic LDS)
+
+// phase A: 2 rows per lane (gate, up), 16 rows per item, 4 chunks per block
+constexpr int kNrA = 2, kRowsA = kWaves * kRowsPerInstr, kCbA = 4;
+// phase B: 2 rows per lane, 32 rows per item, 3 chunks per block
+constexpr int kNrB = 2, kRowsB = kWaves * kRowsPerInstr * kNrB, kCbB = 3;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4* gptr_u32x4;
+
+// 16-byte streaming load through the global (not flat) address space.
+__device__ __forceinline__ u32x4 load_nt16(const char* p) {
+    return __builtin_nontemporal_load((gptr_u32x4)(p));
+}
+
+// Values that are equal across the wavefront, moved to scalar registers so
+// tests on them become scalar branches.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                            __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// Sum over the 16 lanes of a row group (DPP within a row of 16 lanes).
+// Sum over the 16 lanes of a row group (DPP within each row of 16 lanes).
 __device__ __forceinline__ float row16_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
@@ -74,8 +89,8 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
 
 // Bytes of one staged activation row and of one weight row, per format.
 // With `split`, an fp32 activation a is staged for bf16/INT4 weights as the
-// pair hi = bf16(a), lo = bf16(a - hi) (two bf16 rows), so that products with
-// bf16 weights keep about 16 significant bits of a; without it a is rounded to
+// pair hi = bf16(a), lo = bf16(a - hi) (two bf16 rows), so products with bf16
+// weights keep about 16 significant bits of a; without it a is rounded to
 // bf16 once (exact for bf16 inputs).
 __host__ __device__ __forceinline__ int act_row_bytes(int fmt, int cols, bool split) {
     return fmt == MOE_W_F32 ? cols * 4 : cols * 2 * (split ? 2 : 1);
@@ -87,31 +102,24 @@ __host__ __device__ __forceinline__ int weight_row_bytes(int fmt, int cols) {
     return fmt == MOE_W_F32 ? cols * 4 : (fmt == MOE_W_BF16 ? cols * 2 : cols / 2);
 }
 __host__ __device__ __forceinline__ int tokens_per_pass(int fmt, int cols, bool split) {
-    int per = act_row_bytes(fmt, cols, split) + act_sum_bytes(fmt, cols);
-    int t = (kLdsBytes - 256) / per;
+    const int per = act_row_bytes(fmt, cols, split) + act_sum_bytes(fmt, cols);
+    const int t = kLdsBytes / per;
     const int cap = fmt == MOE_W_INT4_G128 ? kMaxTokInt4 : kMaxTok;
     return t < cap ? t : cap;
 }
 
 // ---------------------------------------------------------------------------
-// Staging: activations of `ct` pairs into LDS in the layout of format FMT.
-//   F32 : fp32 row;  BF16 : bf16 row (RNE from fp32 sources);
+// Staging of one pass's activations into LDS.
+//   F32 : fp32 row;  BF16 : bf16 row (pairs (c, c+1));
 //   INT4: bf16 row with each 8-column block stored as pairs (c, c+4), plus
-//         the fp32 sum of every 32-column block.
-// src_kind 0: x rows (x_dtype) indexed by token = pair / k; 1: fp32 hbuf rows
-// indexed by pair.
+//         the fp32 sum of every 32-column block (after the rows).
+// Phase A reads x rows (x_dtype) of token pair / k; phase B reads fp32 rows
+// of the SwiGLU buffer indexed by pair.
 // ---------------------------------------------------------------------------
-struct StageSrc {
-    const void* base;
-    int dtype;      // MOE_DT_F32 or MOE_DT_BF16
-    int by_token;   // 1: row = pair / k, 0: row = pair
-    int k;
-};
-
-__device__ __forceinline__ void load8_as_f32(const StageSrc& src, int row, int cols, int c,
+__device__ __forceinline__ void load8_as_f32(const void* base, int dtype, int row, int cols, int c,
                                              float (&v)[8]) {
-    if (src.dtype == MOE_DT_BF16) {
-        const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src.base) +
+    if (dtype == MOE_DT_BF16) {
+        const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) +
                                                         static_cast<size_t>(row) * cols + c);
         const uint32_t u[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
@@ -120,7 +128,7 @@ __device__ __forceinline__ void load8_as_f32(const StageSrc& src, int row, int c
             v[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
         }
     } else {
-        const float* p = static_cast<const float*>(src.base) + static_cast<size_t>(row) * cols + c;
+        const float* p = static_cast<const float*>(base) + static_cast<size_t>(row) * cols + c;
         const float4 a = *reinterpret_cast<const float4*>(p);
         const float4 b = *reinterpret_cast<const float4*>(p + 4);
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
@@ -128,10 +136,15 @@ __device__ __forceinline__ void load8_as_f32(const StageSrc& src, int row, int c
     }
 }
 
-__device__ void stage_rows(int fmt, bool split, const StageSrc& src, const int32_t* pairs_g, int ct,
-                           int cols, char* lds, int* lds_pairs) {
+__device__ void stage_rows(int fmt, bool split, const void* base, int dtype, int by_token_k,
+                           const int32_t* pairs_g, int ct, int cols, char* lds, const float* wts_g,
+                           int* lds_pair, float* lds_wt) {
     const int tid = threadIdx.x;
-    if (tid < ct) lds_pairs[tid] = pairs_g[tid];
+    if (tid < ct) {
+        const int pr = pairs_g[tid];
+        lds_pair[tid] = pr;
+        lds_wt[tid] = wts_g[pr];
+    }
     const int arow = act_row_bytes(fmt, cols, split);
     const int half = cols * 2;   // byte offset of the lo row when split
     const int blocks = cols / 8;
@@ -139,9 +152,9 @@ __device__ void stage_rows(int fmt, bool split, const StageSrc& src, const int32
     for (int j = tid; j < ct * blocks; j += kThreads) {
         const int t = j / blocks, b = j - t * blocks;
         const int pair = pairs_g[t];
-        const int row = src.by_token ? pair / src.k : pair;
+        const int row = by_token_k > 0 ? pair / by_token_k : pair;
         float v[8];
-        load8_as_f32(src, row, cols, 8 * b, v);
+        load8_as_f32(base, dtype, row, cols, 8 * b, v);
         char* dst = lds + t * arow;
         if (fmt == MOE_W_F32) {
             float4* d = reinterpret_cast<float4*>(dst + b * 32);
@@ -158,7 +171,6 @@ __device__ void stage_rows(int fmt, bool split, const StageSrc& src, const int32
             l[q] = split ? f32_to_bf16_rne(v[q] - hv) : 0u;
             s += split ? hv + __uint_as_float(l[q] << 16) : hv;
         }
-        // BF16 weights pair columns (c, c+1); INT4 weights pair (c, c+4).
         const bool by4 = fmt == MOE_W_INT4_G128;
         const uint4 oh = by4 ? make_uint4(h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16),
                                           h[3] | (h[7] << 16))
@@ -173,7 +185,7 @@ __device__ void stage_rows(int fmt, bool split, const StageSrc& src, const int32
             *reinterpret_cast<uint4*>(dst + half + b * 16) = ol;
         }
         if (by4) {
-            // sum over a 32-column block: lanes j..j+3 hold its four 8-column blocks
+            // a 32-column block is held by lanes j..j+3 (cols % 128 == 0)
             s += __shfl_xor(s, 1, kWave);
             s += __shfl_xor(s, 2, kWave);
             if ((b & 3) == 0) sums[t * (cols / 32) + b / 4] = s;
@@ -182,15 +194,116 @@ __device__ void stage_rows(int fmt, bool split, const StageSrc& src, const int32
 }
 
 // ---------------------------------------------------------------------------
-// Core: NR weight rows per lane against MT staged activation rows.
-// Lane `g` (0..15 within its row group) reads 16 bytes at byte offset
-// 256*c + 16*g of every row, for chunks c = 0 .. nchunks-1.
+// One unit of work of a workgroup: an item (active expert, row tile) and one
+// pass of that expert's tokens.  All fields are wave-uniform.
 // ---------------------------------------------------------------------------
+struct Unit {
+    int slot, tile, t0, ct;   // active slot, row tile, first token of the pass, tokens in it
+    int fmt;
+    bool split;
+    int first;                // first routed pair of the expert in perm
+    const char* m0;           // phase A: gate, phase B: down
+    const char* m1;           // phase A: up
+    const uint16_t* s0;
+    const uint16_t* s1;
+};
+
+template <int PHASE>
+__device__ __forceinline__ Unit make_unit(const FfnArgs& a, long item, int t0, int tiles, int cols) {
+    Unit u;
+    u.slot = uni(static_cast<int>(item / tiles));
+    u.tile = uni(static_cast<int>(item - static_cast<long>(u.slot) * tiles));
+    const int e = uni(a.active[u.slot]);
+    const moe_expert_handle& h = a.table[e];
+    u.fmt = uni(h.fmt);
+    u.split = u.fmt != MOE_W_F32 && (PHASE == 1 || a.x_dtype == MOE_DT_F32);
+    u.first = uni(a.offsets[e]);
+    const int cnt = uni(a.offsets[e + 1]) - u.first;
+    const int per_pass = tokens_per_pass(u.fmt, cols, u.split);
+    u.t0 = uni(t0);
+    u.ct = uni(min(per_pass, cnt - t0));
+    if (PHASE == 0) {
+        u.m0 = static_cast<const char*>(h.w_gate);
+        u.m1 = static_cast<const char*>(h.w_up);
+        u.s0 = h.s_gate;
+        u.s1 = h.s_up;
+    } else {
+        u.m0 = static_cast<const char*>(h.w_down);
+        u.m1 = nullptr;
+        u.s0 = h.s_down;
+        u.s1 = nullptr;
+    }
+    return u;
+}
+
+// Per-lane row addresses of a unit: phase A -> (gate r, up r); phase B ->
+// rows base + 4j of the down matrix.  Rows at or beyond `rows` are clamped to
+// row 0 so every load stays inside the matrix; their results are not stored.
+template <int NR>
+struct Rows {
+    const char* p[NR];
+    const uint16_t* s[NR];
+    int id[NR];
+    int rbytes;     // bytes per weight row
+    int nchunks;    // 256-byte chunks per row (the last may be partial)
+};
+
+template <int PHASE, int NR>
+__device__ __forceinline__ Rows<NR> unit_rows(const Unit& u, int rows, int cols) {
+    Rows<NR> R;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    R.rbytes = uni(weight_row_bytes(u.fmt, cols));
+    R.nchunks = uni((R.rbytes + kChunkBytes - 1) / kChunkBytes);
+    const int sgroups = cols / 128;
+    if constexpr (PHASE == 0) {
+        const int row = u.tile * kRowsA + wave * kRowsPerInstr + lane / kLanesPerRow;
+        const int rr = row < rows ? row : 0;
+        R.p[0] = u.m0 + static_cast<size_t>(rr) * R.rbytes;
+        R.p[1] = u.m1 + static_cast<size_t>(rr) * R.rbytes;
+        R.s[0] = u.s0 + static_cast<size_t>(rr) * sgroups;
+        R.s[1] = u.s1 + static_cast<size_t>(rr) * sgroups;
+        R.id[0] = R.id[1] = row;
+    } else {
+        const int base = u.tile * kRowsB + wave * (kRowsPerInstr * NR) + lane / kLanesPerRow;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int row = base + r * kRowsPerInstr;
+            const int rr = row < rows ? row : 0;
+            R.p[r] = u.m0 + static_cast<size_t>(rr) * R.rbytes;
+            R.s[r] = u.s0 + static_cast<size_t>(rr) * sgroups;
+            R.id[r] = row;
+        }
+    }
+    return R;
+}
+
+// Weight block: CB chunks of NR rows, raw 16-byte loads.
+template <int NR, int CB>
+struct Block {
+    u32x4 w[CB][NR];
+};
+
+// Issue the loads of block `blk`, unconditionally: offsets are clamped to the
+// row's last 16 bytes, so chunks past the row (skipped when computing) and the
+// lanes past the end of a partial chunk (masked when computing) re-read bytes
+// of the same row instead of branching around the load.
+template <int NR, int CB>
+__device__ __forceinline__ void load_block(const Rows<NR>& R, int blk, Block<NR, CB>& b) {
+    const int g = threadIdx.x & (kLanesPerRow - 1);
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+        const int off = min((blk * CB + c) * kChunkBytes + g * 16, R.rbytes - 16);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) b.w[c][r] = load_nt16(R.p[r] + off);
+    }
+}
+
+// Multiply-accumulate one chunk of NR rows against the pass's MT tokens.
 template <int FMT, bool SPLIT, int NR, int MT>
-__device__ __forceinline__ void chunk_fma(const u32x4 (&wv)[NR], int c, int g, int ct,
-                                          const char* lds, int arow, int half, const float* sums,
-                                          int cols, const float (&scale)[NR], float (&acc)[NR][MT]) {
-    const int off = c * kChunkBytes + g * 16;   // weight byte offset in the row
+__device__ __forceinline__ void chunk_fma(const u32x4 (&wv)[NR], const float (&scale)[NR], int off,
+                                          int ct, const char* lds, int arow, int half,
+                                          const float* sums, int cols, float (&acc)[NR][MT]) {
     if constexpr (FMT == MOE_W_F32) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
@@ -232,10 +345,9 @@ __device__ __forceinline__ void chunk_fma(const u32x4 (&wv)[NR], int c, int g, i
             }
         }
     } else {
-        // INT4: 32 weights (columns col0 .. col0+31, one 128-group) per lane.
-        // Each 32-bit word holds 8 nibbles; (w >> 4s) & 0x000f000f | 0x43004300
-        // is the bf16 pair (128 + u_s, 128 + u_{s+4}), matching the staged
-        // activation pairs (c, c+4).
+        // INT4: 32 weights (columns col0 .. col0+31 of one 128-group) per lane.
+        // (w >> 4s) & 0x000f000f | 0x43004300 is the bf16 pair (128 + u_s,
+        // 128 + u_{s+4}) of the word's nibbles, matching the staged pairs (c, c+4).
         const int col0 = off * 2;
         uint32_t pk[NR][16];
 #pragma unroll
@@ -277,147 +389,119 @@ __device__ __forceinline__ void chunk_fma(const u32x4 (&wv)[NR], int c, int g, i
 #pragma unroll
                 for (int r = 0; r < NR; ++r)   // sum (128 + u) x - 136 sum x = sum (u - 8) x
                     acc[r][t] = __builtin_fmaf(scale[r], __builtin_fmaf(-136.0f, xs, d[r]), acc[r][t]);
-                // keep the scheduler from hoisting every token's LDS reads at once
-                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);   // one token's LDS reads at a time
             }
         }
     }
 }
 
-template <int FMT, bool SPLIT, int NR, int MT>
-__device__ __forceinline__ void rows_dot(const char* const (&rowp)[NR], const uint16_t* const (&srow)[NR],
-                                         bool row_ok, int rbytes, int cols, int g, int ct,
-                                         const char* lds, float (&acc)[NR][MT]) {
+// Run one unit: blocks 0..nblk-1 with the next block's loads in flight while
+// the current one is computed; the last block issues the loads of the next
+// unit's first block into `pre`.  Then reduce across the 16 lanes of each row
+// and write the results.
+template <int PHASE, int FMT, bool SPLIT, int NR, int CB, int MT>
+__device__ __forceinline__ void run_unit(const FfnArgs& a, const Unit& u, const Rows<NR>& R,
+                                         const Rows<NR>& NRws, bool has_next, int rows, int cols,
+                                         const char* lds, const int* lds_pair, const float* lds_wt,
+                                         Block<NR, CB>& pre) {
+    const int g = threadIdx.x & (kLanesPerRow - 1);
+    const int nblk = (R.nchunks + CB - 1) / CB;
+    const int arow = act_row_bytes(FMT, cols, SPLIT);
+    const int half = cols * 2;
+    const float* sums = reinterpret_cast<const float*>(lds + u.ct * arow);
+    const bool partial = (R.rbytes % kChunkBytes) != 0;
+    float acc[NR][MT];
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[r][t] = 0.0f;
-    if (!row_ok) return;
-    const int arow = act_row_bytes(FMT, cols, SPLIT);
-    const int half = cols * 2;
-    const float* sums = reinterpret_cast<const float*>(lds + ct * arow);
-    const int nchunks = (rbytes + kChunkBytes - 1) / kChunkBytes;
-    // an INT4 chunk carries 32 weights per lane (a bf16 chunk 8): fewer per block
-    constexpr int CB = FMT == MOE_W_INT4_G128 ? 1 : kChunkBlock;
-    for (int c0 = 0; c0 < nchunks; c0 += CB) {
-        u32x4 wv[CB][NR];
-        float sc[CB][NR];
+    // the block after the unit's last one: the next unit's first, or (at the
+    // end of the range) a harmless re-read of this unit's first block
+    const Rows<NR>& after = has_next ? NRws : R;
+    for (int blk = 0; blk < nblk; ++blk) {
+        Block<NR, CB> cur = pre;
+        if (blk + 1 < nblk) load_block<NR, CB>(R, blk + 1, pre);
+        else load_block<NR, CB>(after, 0, pre);
 #pragma unroll
-        for (int b = 0; b < CB; ++b) {
-            const int off = (c0 + b) * kChunkBytes + g * 16;
-            const bool ok = (c0 + b) < nchunks && off < rbytes;
+        for (int c = 0; c < CB; ++c) {
+            const int chunk = blk * CB + c;
+            if (chunk >= R.nchunks) break;
+            const int off_raw = chunk * kChunkBytes + g * 16;
+            const bool lane_ok = off_raw < R.rbytes;
+            const int off = min(off_raw, R.rbytes - 16);
+            float sc[NR];
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                wv[b][r] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp[r] + off))
-                              : u32x4{0u, 0u, 0u, 0u};
-                if constexpr (FMT == MOE_W_INT4_G128)
-                    sc[b][r] = ok ? f16_bits_to_f32(srow[r][(off * 2) / 128]) : 0.0f;
-                else
-                    sc[b][r] = 1.0f;
+                sc[r] = 1.0f;
+                if constexpr (FMT == MOE_W_INT4_G128) sc[r] = f16_bits_to_f32(R.s[r][(off * 2) / 128]);
             }
+            u32x4 w[NR];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) w[r] = cur.w[c][r];
+            if (partial && chunk == R.nchunks - 1) {   // wave-uniform test
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    if constexpr (FMT == MOE_W_INT4_G128) sc[r] = lane_ok ? sc[r] : 0.0f;
+                    else w[r] = lane_ok ? w[r] : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            chunk_fma<FMT, SPLIT, NR, MT>(w, sc, off, u.ct, lds, arow, half, sums, cols, acc);
         }
-#pragma unroll
-        for (int b = 0; b < CB; ++b) {
-            const int off = (c0 + b) * kChunkBytes + g * 16;
-            if ((c0 + b) < nchunks && off < rbytes)
-                chunk_fma<FMT, SPLIT, NR, MT>(wv[b], c0 + b, g, ct, lds, arow, half, sums, cols, sc[b], acc);
-        }
     }
-}
-
-// ---------------------------------------------------------------------------
-// Phase A: gate/up rows and SwiGLU.
-// ---------------------------------------------------------------------------
-template <int FMT, bool SPLIT, int MT>
-__device__ void gateup_item(const FfnArgs& a, const moe_expert_handle& h, int row0, int ct,
-                            const char* lds, const int* lds_pairs) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int g = lane & (kLanesPerRow - 1);
-    const int row = row0 + wave * kRowsPerInstr + lane / kLanesPerRow;
-    const bool row_ok = row < a.I;
-    const int rbytes = weight_row_bytes(FMT, a.H);
-    const int rr = row_ok ? row : 0;
-    const char* rowp[2] = {static_cast<const char*>(h.w_gate) + static_cast<size_t>(rr) * rbytes,
-                           static_cast<const char*>(h.w_up) + static_cast<size_t>(rr) * rbytes};
-    const uint16_t* srow[2] = {nullptr, nullptr};
-    if constexpr (FMT == MOE_W_INT4_G128) {
-        srow[0] = h.s_gate + static_cast<size_t>(rr) * (a.H / 128);
-        srow[1] = h.s_up + static_cast<size_t>(rr) * (a.H / 128);
-    }
-    float acc[2][MT];
-    rows_dot<FMT, SPLIT, 2, MT>(rowp, srow, row_ok, rbytes, a.H, g, ct, lds, acc);
-    float mine_g = 0.0f, mine_u = 0.0f;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        const float sg = row16_sum(acc[0][t]);
-        const float su = row16_sum(acc[1][t]);
-        if (g == t) { mine_g = sg; mine_u = su; }
-    }
-    if (row_ok && g < ct) a.hbuf[static_cast<size_t>(lds_pairs[g]) * a.I + row] = silu(mine_g) * mine_u;
-}
-
-// ---------------------------------------------------------------------------
-// Phase B: down rows, scaled by the pair's routing weight.
-// ---------------------------------------------------------------------------
-template <int FMT, bool SPLIT, int MT>
-__device__ void down_item(const FfnArgs& a, const moe_expert_handle& h, int row0, int ct,
-                          const char* lds, const int* lds_pairs) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int g = lane & (kLanesPerRow - 1);
-    const int rbytes = weight_row_bytes(FMT, a.I);
-    const int base = row0 + wave * (kRowsPerInstr * kRowsPerLaneB) + lane / kLanesPerRow;
-    const bool row_ok = base < a.H;   // rows base, base+4 share validity when H % 8 == 0
-    const char* rowp[kRowsPerLaneB];
-    const uint16_t* srow[kRowsPerLaneB];
-#pragma unroll
-    for (int r = 0; r < kRowsPerLaneB; ++r) {
-        const int row = row_ok ? base + r * kRowsPerInstr : 0;
-        rowp[r] = static_cast<const char*>(h.w_down) + static_cast<size_t>(row) * rbytes;
-        srow[r] = (FMT == MOE_W_INT4_G128) ? h.s_down + static_cast<size_t>(row) * (a.I / 128) : nullptr;
-    }
-    float acc[kRowsPerLaneB][MT];
-    rows_dot<FMT, SPLIT, kRowsPerLaneB, MT>(rowp, srow, row_ok, rbytes, a.I, g, ct, lds, acc);
-#pragma unroll
-    for (int r = 0; r < kRowsPerLaneB; ++r) {
-        float mine = 0.0f;
+    const bool writer = g < u.ct;
+    const int pair = writer ? lds_pair[g] : 0;
+    if constexpr (PHASE == 0) {
+        float mg = 0.0f, mu = 0.0f;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            const float s = row16_sum(acc[r][t]);
-            if (g == t) mine = s;
+            const float sg = row16_sum(acc[0][t]);
+            const float su = row16_sum(acc[1][t]);
+            if (g == t) { mg = sg; mu = su; }
         }
-        if (row_ok && g < ct) {
-            const int pair = lds_pairs[g];
-            a.dbuf[static_cast<size_t>(pair) * a.H + base + r * kRowsPerInstr] = a.w[pair] * mine;
+        if (writer && R.id[0] < rows) a.hbuf[static_cast<size_t>(pair) * a.I + R.id[0]] = silu(mg) * mu;
+    } else {
+        const float wgt = writer ? lds_wt[g] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            float mine = 0.0f;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const float s = row16_sum(acc[r][t]);
+                if (g == t) mine = s;
+            }
+            if (writer && R.id[r] < rows)
+                a.dbuf[static_cast<size_t>(pair) * a.H + R.id[r]] = wgt * mine;
         }
     }
 }
 
-template <int FMT, bool SPLIT, int PHASE>
-__device__ __forceinline__ void run_item(const FfnArgs& a, const moe_expert_handle& h, int row0,
-                                         int ct, const char* lds, const int* lds_pairs) {
-#define MOE_ITEM_CASE(MTV)                                                              \
-    if (ct <= MTV) {                                                                    \
-        if constexpr (PHASE == 0) gateup_item<FMT, SPLIT, MTV>(a, h, row0, ct, lds, lds_pairs); \
-        else down_item<FMT, SPLIT, MTV>(a, h, row0, ct, lds, lds_pairs);                \
-        return;                                                                         \
+template <int PHASE, int FMT, bool SPLIT, int NR, int CB>
+__device__ __forceinline__ void run_unit_mt(const FfnArgs& a, const Unit& u, const Rows<NR>& R,
+                                            const Rows<NR>& NRws, bool has_next, int rows, int cols,
+                                            const char* lds, const int* lds_pair, const float* lds_wt,
+                                            Block<NR, CB>& pre) {
+#define MOE_RUN(MTV) \
+    run_unit<PHASE, FMT, SPLIT, NR, CB, MTV>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre)
+    if (u.ct <= 1) {
+        MOE_RUN(1);
+    } else if (u.ct <= 2) {
+        MOE_RUN(2);
+    } else if constexpr (FMT != MOE_W_INT4_G128) {   // INT4 passes hold at most 2 tokens
+        if (u.ct <= 4) MOE_RUN(4);
+        else MOE_RUN(8);
     }
-    MOE_ITEM_CASE(1)
-    MOE_ITEM_CASE(2)
-    MOE_ITEM_CASE(4)
-    if constexpr (FMT != MOE_W_INT4_G128) {
-        MOE_ITEM_CASE(8)
-        MOE_ITEM_CASE(16)
-    }
-#undef MOE_ITEM_CASE
+#undef MOE_RUN
 }
 
-// Persistent workgroups; workgroup b takes items [b*total/G, (b+1)*total/G).
+// Persistent workgroups; workgroup b takes items [b*total/G, (b+1)*total/G)
+// and, within each item, the passes of up to 8 tokens of its expert.
 template <int PHASE>
 __global__ __launch_bounds__(kThreads, 2) void ffn_kernel(FfnArgs a) {
-    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-    int* lds_pairs = reinterpret_cast<int*>(lds_raw + kLdsBytes - 64);
+    constexpr int NR = PHASE == 0 ? kNrA : kNrB;
+    constexpr int CB = PHASE == 0 ? kCbA : kCbB;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ int lds_pair[kMaxTok];
+    __shared__ float lds_wt[kMaxTok];
     const int T = *a.T;
     const int rows = PHASE == 0 ? a.I : a.H;
     const int cols = PHASE == 0 ? a.H : a.I;
@@ -426,40 +510,47 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_kernel(FfnArgs a) {
     const long total = static_cast<long>(T) * tiles;
     const long begin = total * blockIdx.x / gridDim.x;
     const long end = total * (blockIdx.x + 1) / gridDim.x;
-    int staged_slot = -1, staged_t0 = -1;
-    for (long it = begin; it < end; ++it) {
-        const int slot = static_cast<int>(it / tiles);
-        const int tile = static_cast<int>(it - static_cast<long>(slot) * tiles);
-        const int e = a.active[slot];
-        const moe_expert_handle h = a.table[e];
-        const int first = a.offsets[e];
-        const int cnt = a.offsets[e + 1] - first;
-        // fp32 activations meet bf16/INT4 weights as hi/lo bf16 pairs
-        const bool split = h.fmt != MOE_W_F32 && (PHASE == 1 || a.x_dtype == MOE_DT_F32);
-        const int per_pass = tokens_per_pass(h.fmt, cols, split);
-        for (int t0 = 0; t0 < cnt; t0 += per_pass) {
-            const int ct = min(per_pass, cnt - t0);
-            if (slot != staged_slot || t0 != staged_t0) {
-                __syncthreads();
-                StageSrc src;
-                if (PHASE == 0) src = StageSrc{a.x, a.x_dtype, 1, a.k};
-                else src = StageSrc{a.hbuf, MOE_DT_F32, 0, a.k};
-                stage_rows(h.fmt, split, src, a.perm + first + t0, ct, cols, lds_raw, lds_pairs);
-                __syncthreads();
-                staged_slot = slot;
-                staged_t0 = t0;
-            }
-            const int row0 = tile * rows_per_item;
-            if (h.fmt == MOE_W_BF16) {
-                if (split) run_item<MOE_W_BF16, true, PHASE>(a, h, row0, ct, lds_raw, lds_pairs);
-                else run_item<MOE_W_BF16, false, PHASE>(a, h, row0, ct, lds_raw, lds_pairs);
-            } else if (h.fmt == MOE_W_INT4_G128) {
-                if (split) run_item<MOE_W_INT4_G128, true, PHASE>(a, h, row0, ct, lds_raw, lds_pairs);
-                else run_item<MOE_W_INT4_G128, false, PHASE>(a, h, row0, ct, lds_raw, lds_pairs);
-            } else {
-                run_item<MOE_W_F32, false, PHASE>(a, h, row0, ct, lds_raw, lds_pairs);
-            }
+    if (begin >= end) return;
+    const void* src = PHASE == 0 ? a.x : static_cast<const void*>(a.hbuf);
+    const int src_dtype = PHASE == 0 ? a.x_dtype : MOE_DT_F32;
+    const int by_token = PHASE == 0 ? a.k : 0;
+
+    long item = begin;
+    Unit u = make_unit<PHASE>(a, item, 0, tiles, cols);
+    Rows<NR> R = unit_rows<PHASE, NR>(u, rows, cols);
+    Block<NR, CB> pre;
+    load_block<NR, CB>(R, 0, pre);
+    stage_rows(u.fmt, u.split, src, src_dtype, by_token, a.perm + u.first + u.t0, u.ct, cols, lds, a.w,
+               lds_pair, lds_wt);
+    __syncthreads();
+    while (true) {
+        // the unit after u: the next pass of this item, else the next item
+        long nitem = item;
+        int nt0 = u.t0 + u.ct;
+        const int cnt = a.offsets[a.active[u.slot] + 1] - u.first;
+        if (nt0 >= cnt) { nitem = item + 1; nt0 = 0; }
+        const bool has_next = nitem < end;
+        const Unit nu = has_next ? make_unit<PHASE>(a, nitem, nt0, tiles, cols) : u;
+        const Rows<NR> NRws = unit_rows<PHASE, NR>(nu, rows, cols);
+        if (u.fmt == MOE_W_BF16) {
+            if (u.split) run_unit_mt<PHASE, MOE_W_BF16, true, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
+            else run_unit_mt<PHASE, MOE_W_BF16, false, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
+        } else if (u.fmt == MOE_W_INT4_G128) {
+            if (u.split) run_unit_mt<PHASE, MOE_W_INT4_G128, true, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
+            else run_unit_mt<PHASE, MOE_W_INT4_G128, false, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
+        } else {
+            run_unit_mt<PHASE, MOE_W_F32, false, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
         }
+        if (!has_next) break;
+        if (nu.slot != u.slot || nu.t0 != u.t0) {
+            __syncthreads();
+            stage_rows(nu.fmt, nu.split, src, src_dtype, by_token, a.perm + nu.first + nu.t0, nu.ct, cols, lds,
+                       a.w, lds_pair, lds_wt);
+            __syncthreads();
+        }
+        u = nu;
+        R = NRws;
+        item = nitem;
     }
 }
 
@@ -491,13 +582,15 @@ int device_cus() {
     return g_num_cus[dev];
 }
 
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
 }  // namespace
 
+// Workspace: SwiGLU activations [B*k, I] fp32, then weighted down
+// projections [B*k, H] fp32.
 size_t ffn_workspace_bytes(int B, int k, int H, int I) {
     const size_t pairs = static_cast<size_t>(B) * k;
-    size_t hb = (pairs * I * sizeof(float) + 255) & ~size_t(255);
-    size_t db = (pairs * H * sizeof(float) + 255) & ~size_t(255);
-    return hb + db;
+    return align256(pairs * I * sizeof(float)) + align256(pairs * H * sizeof(float));
 }
 
 hipError_t launch_expert_ffn(const FfnArgs& in, void* ws, hipStream_t s) {
@@ -505,7 +598,7 @@ hipError_t launch_expert_ffn(const FfnArgs& in, void* ws, hipStream_t s) {
     const size_t pairs = static_cast<size_t>(a.B) * a.k;
     char* p = static_cast<char*>(ws);
     a.hbuf = reinterpret_cast<float*>(p);
-    a.dbuf = reinterpret_cast<float*>(p + ((pairs * a.I * sizeof(float) + 255) & ~size_t(255)));
+    a.dbuf = reinterpret_cast<float*>(p + align256(pairs * a.I * sizeof(float)));
     const int G = 2 * device_cus();
     ffn_kernel<0><<<G, kThreads, kLdsBytes, s>>>(a);
     hipError_t e = hipGetLastError();

@@ -52,95 +52,121 @@ __device__ __forceinline__ float route_exp(float x) {
     return q * __int_as_float((ni + 127) << 23);
 }
 
-// (v, j) precedes (ov, oj) in rank order: larger logit, then smaller index.
-__device__ __forceinline__ bool precedes(float v, int j, float ov, int oj) {
-    return v > ov || (v == ov && j < oj);
+// Rank order is (logit descending, expert index ascending).  A candidate is
+// encoded as a 64-bit key whose unsigned order is that rank order: the high
+// word maps the logit's bits to an order-preserving unsigned value (-0 is
+// folded to +0 first, so equal logits compare equal as floats do), the low
+// word is ~index.  Key 0 means "no candidate".
+__device__ __forceinline__ uint64_t rank_key(float l, int j) {
+    const uint32_t b = __float_as_uint(l == 0.0f ? 0.0f : l);
+    const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(j));
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+    const uint32_t o = static_cast<uint32_t>(key >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_index(uint64_t key) {
+    return static_cast<int>(~static_cast<uint32_t>(key));
 }
 
-// Wavefront argmax in rank order; every lane ends with the same winner.
-__device__ __forceinline__ void wave_best(float& v, int& j) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        float ov = __shfl_xor(v, off, kWave);
-        int oj = __shfl_xor(j, off, kWave);
-        if (precedes(ov, oj, v, j)) { v = ov; j = oj; }
-    }
+// DPP cross-lane moves (all 64 lanes active).  Row masks select which rows of
+// 16 lanes receive the moved value; the others keep `old`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp32(uint32_t old, uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp64(uint64_t old, uint64_t v) {
+    const uint32_t lo = dpp32<CTRL, ROWS>(static_cast<uint32_t>(old), static_cast<uint32_t>(v));
+    const uint32_t hi = dpp32<CTRL, ROWS>(static_cast<uint32_t>(old >> 32), static_cast<uint32_t>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Wavefront maximum of a key; returned uniform (read from lane 63).
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+    v = umax64(v, dpp64<kQuadXor1, 0xF>(v, v));
+    v = umax64(v, dpp64<kQuadXor2, 0xF>(v, v));
+    v = umax64(v, dpp64<kHalfMirror, 0xF>(v, v));
+    v = umax64(v, dpp64<kMirror, 0xF>(v, v));
+    v = umax64(v, dpp64<kRowBcast15, 0xA>(v, v));   // rows 1, 3 take rows 0, 2
+    v = umax64(v, dpp64<kRowBcast31, 0xC>(v, v));   // rows 2, 3 take row 1
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
+// Normaliser Z from the lane sums of experts (2l, 2l+1).  The DPP steps pair
+// lanes (l, l^1), then quads, then 8-lane and 16-lane halves, then rows 0+1
+// and 2+3, then the two halves of the wave: exactly the balanced pairwise
+// tree over 128 slots in expert order (fp32 addition is commutative).
+__device__ __forceinline__ float wave_tree_sum(float x) {
+    uint32_t s = __float_as_uint(x);
+    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kQuadXor1, 0xF>(s, s)));
+    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kQuadXor2, 0xF>(s, s)));
+    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kHalfMirror, 0xF>(s, s)));
+    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kMirror, 0xF>(s, s)));
+    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kRowBcast15, 0xA>(s, s)));  // rows 1, 3
+    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kRowBcast31, 0xC>(s, s)));  // row 3
+    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(s), 63)));
 }
 
-// Normaliser Z: lane sum of experts (2l, 2l+1), then the xor butterfly,
-// which is exactly the balanced pairwise tree over 128 slots in expert order.
-__device__ __forceinline__ float wave_tree_sum(float s) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) s = s + __shfl_xor(s, off, kWave);
-    return s;
-}
-
-constexpr int kNoExpert = 0x7fffffff;
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// Select up to `count` experts of the calling token in rank order among the
-// lane's two candidates that are still available.  Results are uniform
-// across the wavefront.  Stops early when nothing is left.
-__device__ __forceinline__ int select_ranked(float l0, float l1, bool avail0, bool avail1,
-                                             int e0, int e1, int count, float (&selv)[kMaxTopK],
-                                             int (&selj)[kMaxTopK]) {
+// Select up to `count` of the token's experts in rank order from the lane's
+// two candidate keys (0 = unavailable); a selected key is cleared by its
+// owner.  Results are uniform.  Stops early when nothing is left.
+__device__ __forceinline__ int select_ranked(uint64_t& key0, uint64_t& key1, int count,
+                                             float (&selv)[kMaxTopK], int (&selj)[kMaxTopK]) {
     int got = 0;
 #pragma unroll
     for (int r = 0; r < kMaxTopK; ++r) {
-        if (r >= count) break;
-        float v0 = avail0 ? l0 : kNegInf;
-        int j0 = avail0 ? e0 : kNoExpert;
-        float v1 = avail1 ? l1 : kNegInf;
-        int j1 = avail1 ? e1 : kNoExpert;
-        float v = v0;
-        int j = j0;
-        if (precedes(v1, j1, v, j)) { v = v1; j = j1; }
-        wave_best(v, j);
-        if (j == kNoExpert) break;
-        selv[r] = v;
-        selj[r] = j;
-        if (j == e0) avail0 = false;
-        if (j == e1) avail1 = false;
-        got = r + 1;
+        selv[r] = 0.0f;
+        selj[r] = -1;
+        if (r < count && got == r) {   // wave-uniform
+            const uint64_t best = wave_max_key(umax64(key0, key1));
+            if (best != 0) {
+                selv[r] = key_logit(best);
+                selj[r] = key_index(best);
+                if (key0 == best) key0 = 0;
+                if (key1 == best) key1 = 0;
+                got = r + 1;
+            }
+        }
     }
     return got;
 }
 
-// Write the kept experts of one token: lane r < k writes slot r.
-// Weights: e_r / sum_{kept} e (renorm) or e_r / Z (raw softmax), with the
-// quotient taken in double and rounded once to fp32.
+// Wavefront sum of doubles (any fixed order; used for weight denominators).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Write the kept experts of one token: lane r < kept owns slot r, computes
+// e_r = exp(l_r - m) and w_r = e_r / sum_kept e (renorm) or e_r / Z (raw
+// softmax), the quotient in double rounded once to fp32; slots >= kept get
+// expert -1 and weight 0.
 __device__ __forceinline__ void write_token(int lane, int i, int k, int kept, float m, bool renorm,
                                             float Z, const float (&selv)[kMaxTopK],
                                             const int (&selj)[kMaxTopK], int32_t* idx, float* w) {
-    float ev[kMaxTopK];
-    double denom = 0.0;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-        ev[r] = 0.0f;
-        if (r < kept) {
-            ev[r] = route_exp(selv[r] - m);
-            denom += static_cast<double>(ev[r]);
-        }
-    }
-    if (!renorm) denom = static_cast<double>(Z);
+    float my_l = 0.0f;
     int my_j = -1;
-    float my_w = 0.0f;
 #pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-        if (lane == r && r < kept) {
-            my_j = selj[r];
-            my_w = static_cast<float>(static_cast<double>(ev[r]) / denom);
-        }
-    }
+    for (int r = 0; r < kMaxTopK; ++r)
+        if (lane == r) { my_l = selv[r]; my_j = selj[r]; }
+    const bool mine = lane < kept;
+    const double ev = mine ? static_cast<double>(route_exp(my_l - m)) : 0.0;
+    const double denom = renorm ? wave_sum_f64(ev) : static_cast<double>(Z);
     if (lane < k) {
-        idx[i * k + lane] = my_j;
-        w[i * k + lane] = my_w;
+        idx[i * k + lane] = mine ? my_j : -1;
+        w[i * k + lane] = mine ? static_cast<float>(ev / denom) : 0.0f;
     }
 }
 
@@ -166,32 +192,35 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
 
     // Vanilla top-k, or OEA Phase 1.
     for (int i = wave; i < B; i += nwaves) {
-        const float l0 = e0 < N ? logits[i * N + e0] : kNegInf;
-        const float l1 = e1 < N ? logits[i * N + e1] : kNegInf;
         const bool v0 = e0 < N, v1 = e1 < N;
+        const float l0 = v0 ? logits[i * N + e0] : kNegInf;
+        const float l1 = v1 ? logits[i * N + e1] : kNegInf;
+        uint64_t key0 = v0 ? rank_key(l0, e0) : 0ull;
+        uint64_t key1 = v1 ? rank_key(l1, e1) : 0ull;
         const bool need_z = kOea ? (p < 1.0f) : (renorm == 0);
+        const int first = kOea ? k0 : k;
+        const int kept = select_ranked(key0, key1, first, selv, selj);
+        const float m = selv[0];   // the top logit
         float Z = 0.0f;
         if (need_z) {
-            float m = wave_max(fmaxf(l0, l1));
-            float s0 = v0 ? route_exp(l0 - m) : 0.0f;
-            float s1 = v1 ? route_exp(l1 - m) : 0.0f;
+            const float s0 = v0 ? route_exp(l0 - m) : 0.0f;
+            const float s1 = v1 ? route_exp(l1 - m) : 0.0f;
             Z = wave_tree_sum(s0 + s1);
         }
         if (!kOea) {
-            int kept = select_ranked(l0, l1, v0, v1, e0, e1, k, selv, selj);
-            write_token(lane, i, k, kept, selv[0], renorm != 0, Z, selv, selj, idx, w);
+            write_token(lane, i, k, kept, m, renorm != 0, Z, selv, selj, idx, w);
         } else {
-            int kept = select_ranked(l0, l1, v0, v1, e0, e1, k0, selv, selj);
             int n = kept;
             if (p < 1.0f) {
-                const float m = selv[0];
                 const float pz = p * Z;
                 float c = 0.0f;
+                bool reached = false;
 #pragma unroll
                 for (int r = 0; r < kMaxTopK; ++r) {
-                    if (r >= kept) break;
-                    c = c + route_exp(selv[r] - m);
-                    if (c >= pz) { n = r + 1; break; }
+                    if (r < kept && !reached) {
+                        c = c + route_exp(selv[r] - m);
+                        if (c >= pz) { n = r + 1; reached = true; }
+                    }
                 }
             }
             if (lane == 0 && n_base != nullptr) n_base[i] = n;
@@ -218,11 +247,11 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
     // order -- its baseline first (the top-ranked experts are in S_base), then
     // lower-ranked experts that other tokens already activated.
     for (int i = wave; i < B; i += nwaves) {
-        const float l0 = e0 < N ? logits[i * N + e0] : kNegInf;
-        const float l1 = e1 < N ? logits[i * N + e1] : kNegInf;
         const bool a0 = e0 < N && ((sbase[e0 >> 5] >> (e0 & 31)) & 1u);
         const bool a1 = e1 < N && ((sbase[e1 >> 5] >> (e1 & 31)) & 1u);
-        int kept = select_ranked(l0, l1, a0, a1, e0, e1, keep, selv, selj);
+        uint64_t key0 = a0 ? rank_key(logits[i * N + e0], e0) : 0ull;
+        uint64_t key1 = a1 ? rank_key(logits[i * N + e1], e1) : 0ull;
+        const int kept = select_ranked(key0, key1, keep, selv, selj);
         write_token(lane, i, k, kept, selv[0], true, 0.0f, selv, selj, idx, w);
     }
 }
@@ -314,9 +343,14 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
     }
 }
 
-// Router logits: one wavefront per (expert, group of up to 16 tokens); lanes
-// stride over the hidden dimension 8 columns at a time; fp32 accumulation.
+// Router logits: one workgroup per expert; its 4 waves split the hidden
+// dimension (lane l of wave w owns columns 8l + 512w + 2048i), and every lane
+// issues its router-weight and activation loads for a group of 16 tokens at
+// once, so the whole product costs about one memory round trip.  Partial sums
+// are reduced over the 16 lanes of a row with DPP, then over rows and waves
+// through LDS.  fp32 accumulation.
 constexpr int kGemvTok = 16;
+constexpr int kGemvThreads = 256;
 
 template <typename XT>
 __device__ __forceinline__ void load_x8(const XT* x, float (&v)[8]);
@@ -340,39 +374,57 @@ __device__ __forceinline__ void load_x8<uint16_t>(const uint16_t* x, float (&v)[
     }
 }
 
+__device__ __forceinline__ float row16_sum_f(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 template <typename XT>
-__global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict__ x,
-                                                            const float* __restrict__ w_r, int B,
-                                                            int H, int N,
-                                                            float* __restrict__ logits) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const int t0 = blockIdx.y * kGemvTok;
-    if (e >= N) return;
-    const int nt = min(kGemvTok, B - t0);
-    float acc[kGemvTok];
-#pragma unroll
-    for (int t = 0; t < kGemvTok; ++t) acc[t] = 0.0f;
+__global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(const XT* __restrict__ x,
+                                                                     const float* __restrict__ w_r,
+                                                                     int B, int H, int N,
+                                                                     float* __restrict__ logits) {
+    __shared__ float part[kGemvThreads / 16][kGemvTok];   // [row of 16 lanes][token]
+    const int e = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int col0 = 8 * lane + 512 * (tid / kWave);     // this lane's first column
+    const int stride = 8 * kGemvThreads;                  // 2048 columns per sweep
     const float* wrow = w_r + static_cast<size_t>(e) * H;
-    for (int c = 8 * lane; c < H; c += 8 * kWave) {
-        float wv[8];
-        load_x8<float>(wrow + c, wv);
+    for (int t0 = 0; t0 < B; t0 += kGemvTok) {
+        const int nt = min(kGemvTok, B - t0);
+        float acc[kGemvTok];
+#pragma unroll
+        for (int t = 0; t < kGemvTok; ++t) acc[t] = 0.0f;
+        for (int c = col0; c < H; c += stride) {
+            float wv[8];
+            load_x8<float>(wrow + c, wv);
+            float xv[kGemvTok][8];
+#pragma unroll
+            for (int t = 0; t < kGemvTok; ++t)
+                if (t < nt) load_x8<XT>(x + static_cast<size_t>(t0 + t) * H + c, xv[t]);
+#pragma unroll
+            for (int t = 0; t < kGemvTok; ++t)
+                if (t < nt)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) acc[t] = __builtin_fmaf(wv[q], xv[t][q], acc[t]);
+        }
 #pragma unroll
         for (int t = 0; t < kGemvTok; ++t) {
-            if (t < nt) {
-                float xv[8];
-                load_x8<XT>(x + static_cast<size_t>(t0 + t) * H + c, xv);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) acc[t] = __builtin_fmaf(wv[q], xv[q], acc[t]);
-            }
+            const float s = row16_sum_f(acc[t]);
+            if ((tid & 15) == 0) part[tid / 16][t] = s;
         }
-    }
+        __syncthreads();
+        if (tid < nt) {
+            float s = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kGemvTok; ++t) {
-        float s = acc[t];
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) s = s + __shfl_xor(s, off, kWave);
-        if (lane == 0 && t < nt) logits[static_cast<size_t>(t0 + t) * N + e] = s;
+            for (int r = 0; r < kGemvThreads / 16; ++r) s += part[r][tid];
+            logits[static_cast<size_t>(t0 + tid) * N + e] = s;
+        }
+        __syncthreads();
     }
 }
 
@@ -389,13 +441,12 @@ __global__ void publish_kernel(moe_expert_handle* table, int e, moe_expert_handl
 
 hipError_t launch_router_logits(const void* x, int x_dtype, const float* w_r, int B, int H, int N,
                                 float* logits, hipStream_t s) {
-    dim3 grid((N + 3) / 4, (B + kGemvTok - 1) / kGemvTok);
     if (x_dtype == MOE_DT_BF16)
-        router_logits_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), w_r,
-                                                            B, H, N, logits);
+        router_logits_kernel<uint16_t><<<N, kGemvThreads, 0, s>>>(static_cast<const uint16_t*>(x), w_r,
+                                                                  B, H, N, logits);
     else
-        router_logits_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), w_r, B, H,
-                                                         N, logits);
+        router_logits_kernel<float><<<N, kGemvThreads, 0, s>>>(static_cast<const float*>(x), w_r, B, H,
+                                                               N, logits);
     return hipGetLastError();
 }
 

@@ -76,7 +76,7 @@ class MoELayer:
                          T=torch.empty(1, **i32))
             disp = dict(cnt=torch.empty(N, **i32), offsets=torch.empty(N + 1, **i32),
                         perm=torch.empty(B * k, **i32), active=torch.empty(N, **i32), T=torch.empty(1, **i32))
-            ws = torch.empty(L.ffn_workspace_bytes(B, k, self.H, self.I), device=dev, dtype=torch.uint8)
+            ws = torch.zeros(L.ffn_workspace_bytes(B, k, self.H, self.I), device=dev, dtype=torch.uint8)
             b = Buffers(B, torch.empty(B, N, device=dev, dtype=torch.float32), route, disp,
                         torch.empty(B, self.H, device=dev, dtype=torch.float32), ws)
             self._bufs[B] = b

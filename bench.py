@@ -121,14 +121,19 @@ def main():
             if timed:
                 ev1[i].record(stream)
 
+        # whole-layer steps, no events in the stream
         for i in range(args.warmup):
             step(i, False)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(i, True)
+            step(i, False)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        # the same steps again with HIP events around the expert FFN call
+        for i in range(args.steps):
+            step(i, True)
+        torch.cuda.synchronize()
         ffn_ms = [ev0[i].elapsed_time(ev1[i]) for i in range(args.steps)]
         Tsteps = [Ts[i % len(Ts)] for i in range(args.steps)]
         layer_bytes = sum(t * W_e + fixed_layer for t in Tsteps)

@@ -153,9 +153,11 @@ size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
  *   idx, w : routing output [B, k]; offsets, perm, active, T: dispatch output
  *   y      : [B, H] fp32, overwritten
  *   ws     : workspace of at least moe_ffn_workspace_bytes(B, k, H, I) bytes
+ *            (scratch; calls that share a workspace must be ordered, e.g. on
+ *            one stream).
  * Accumulation is fp32.  H and I must be multiples of 8 (of 128 when any
  * expert is INT4).  Each active expert's weights are streamed from HBM once
- * per call (tokens are processed in groups of up to 16 per pass).
+ * per pass of up to 8 of its tokens (up to 2 for INT4 experts).
  */
 int moe_expert_ffn(const moe_expert_handle *table, int N, int H, int I, const void *x,
                    int x_dtype, const int32_t *idx, const float *w, const int32_t *offsets,
