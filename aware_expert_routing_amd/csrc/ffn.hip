@@ -19,7 +19,8 @@
 //   * phase B (down + routing weight): items are (active expert, 32 rows of
 //     H); a lane owns two rows.
 //   * combine: y[i] = sum over token i's filled slots, in slot order.
-// Each 256-thread workgroup takes a contiguous range of items.  A wave keeps
+// Each 256-thread workgroup takes a contiguous range of items of about equal
+// streaming cost (every workgroup first prices the active experts).  A wave keeps
 // the weight loads of its next block of chunks in flight while it computes
 // the current block, and at the end of an item it has already issued the
 // loads of the next item's first block, so the weight stream does not stop
@@ -42,7 +43,7 @@ constexpr int kWaves = kThreads / kWave;               // 4
 constexpr int kChunkBytes = kLanesPerRow * 16;          // 256 row bytes per chunk
 constexpr int kMaxTok = 8;                              // tokens per pass
 constexpr int kMaxTokInt4 = 2;                          // INT4: fewer live registers
-constexpr int kLdsBytes = 64 * 1024 - 256;              // staged activations (dynamic LDS)
+constexpr int kLdsBytes = 56 * 1024;   // staged activations (dynamic LDS; static LDS adds ~6.7 KB)
 
 // phase A: 2 rows per lane (gate, up), 16 rows per item, 4 chunks per block
 constexpr int kNrA = 2, kRowsA = kWaves * kRowsPerInstr, kCbA = 4;
@@ -194,6 +195,29 @@ __device__ void stage_rows(int fmt, bool split, const void* base, int dtype, int
 }
 
 // ---------------------------------------------------------------------------
+// Cost-balanced partition.  Each workgroup first prices every active expert
+// (one thread per active slot, records kept in LDS): the cost of a row tile
+// is the sum over the expert's token passes of (16 + tokens), since for the
+// same weight bytes a pass of 8 tokens takes about 1.4x a pass of one
+// (measured) and every extra pass streams the tile again.  Workgroup b then
+// takes the items whose cost ranges start in [b*C/G, (b+1)*C/G) of the total
+// cost C, so experts with many tokens are spread over more workgroups.
+// ---------------------------------------------------------------------------
+struct SlotRec {                  // one phase's view of an active expert
+    const char* m0;               // phase A: gate, phase B: down
+    const char* m1;               // phase A: up
+    const uint16_t* s0;           // INT4 scales (or null)
+    const uint16_t* s1;
+    int32_t fmt, first, cnt, pad;
+};
+
+__device__ __forceinline__ int tile_cost(int cnt, int per_pass) {
+    int c = 0;
+    for (int t0 = 0; t0 < cnt; t0 += per_pass) c += 16 + min(per_pass, cnt - t0);
+    return c;
+}
+
+// ---------------------------------------------------------------------------
 // One unit of work of a workgroup: an item (active expert, row tile) and one
 // pass of that expert's tokens.  All fields are wave-uniform.
 // ---------------------------------------------------------------------------
@@ -209,30 +233,23 @@ struct Unit {
 };
 
 template <int PHASE>
-__device__ __forceinline__ Unit make_unit(const FfnArgs& a, long item, int t0, int tiles, int cols) {
+__device__ __forceinline__ Unit make_unit(const SlotRec* recs, int x_dtype, long item, int t0, int tiles,
+                                          int cols, int& cnt) {
     Unit u;
     u.slot = uni(static_cast<int>(item / tiles));
     u.tile = uni(static_cast<int>(item - static_cast<long>(u.slot) * tiles));
-    const int e = uni(a.active[u.slot]);
-    const moe_expert_handle& h = a.table[e];
-    u.fmt = uni(h.fmt);
-    u.split = u.fmt != MOE_W_F32 && (PHASE == 1 || a.x_dtype == MOE_DT_F32);
-    u.first = uni(a.offsets[e]);
-    const int cnt = uni(a.offsets[e + 1]) - u.first;
+    const SlotRec& r = recs[u.slot];
+    u.fmt = uni(r.fmt);
+    u.split = u.fmt != MOE_W_F32 && (PHASE == 1 || x_dtype == MOE_DT_F32);
+    u.first = uni(r.first);
+    cnt = uni(r.cnt);
     const int per_pass = tokens_per_pass(u.fmt, cols, u.split);
     u.t0 = uni(t0);
     u.ct = uni(min(per_pass, cnt - t0));
-    if (PHASE == 0) {
-        u.m0 = static_cast<const char*>(h.w_gate);
-        u.m1 = static_cast<const char*>(h.w_up);
-        u.s0 = h.s_gate;
-        u.s1 = h.s_up;
-    } else {
-        u.m0 = static_cast<const char*>(h.w_down);
-        u.m1 = nullptr;
-        u.s0 = h.s_down;
-        u.s1 = nullptr;
-    }
+    u.m0 = r.m0;
+    u.m1 = r.m1;
+    u.s0 = r.s0;
+    u.s1 = r.s1;
     return u;
 }
 
@@ -493,7 +510,60 @@ __device__ __forceinline__ void run_unit_mt(const FfnArgs& a, const Unit& u, con
 #undef MOE_RUN
 }
 
-// Persistent workgroups; workgroup b takes items [b*total/G, (b+1)*total/G)
+// Prologue of both phases: thread s < T reads active slot s's expert, its
+// handle and token range into recs[s]; pref[s] receives the inclusive prefix
+// of the slots' costs (slots >= T cost 0, so pref[127] is the total).
+template <int PHASE>
+__device__ __forceinline__ void price_slots(const FfnArgs& a, int T, int tiles, int cols, SlotRec* recs,
+                                            int* pref, int* wave_total) {
+    const int s = threadIdx.x;
+    const int lane = s & (kWave - 1);
+    int cost = 0;
+    if (s < T) {
+        const int e = a.active[s];
+        const moe_expert_handle& h = a.table[e];
+        SlotRec r;
+        r.fmt = h.fmt;
+        r.m0 = static_cast<const char*>(PHASE == 0 ? h.w_gate : h.w_down);
+        r.m1 = PHASE == 0 ? static_cast<const char*>(h.w_up) : nullptr;
+        r.s0 = PHASE == 0 ? h.s_gate : h.s_down;
+        r.s1 = PHASE == 0 ? h.s_up : nullptr;
+        r.first = a.offsets[e];
+        r.cnt = a.offsets[e + 1] - r.first;
+        r.pad = 0;
+        recs[s] = r;
+        const bool split = r.fmt != MOE_W_F32 && (PHASE == 1 || a.x_dtype == MOE_DT_F32);
+        cost = tiles * tile_cost(r.cnt, tokens_per_pass(r.fmt, cols, split));
+    }
+    if (s < kMaxExperts) {              // waves 0 and 1: inclusive scan of 64 slots each
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(cost, off);
+            if (lane >= off) cost += v;
+        }
+        if (lane == kWave - 1) wave_total[s / kWave] = cost;
+    }
+    __syncthreads();
+    if (s < kMaxExperts) pref[s] = cost + (s >= kWave ? wave_total[0] : 0);
+    __syncthreads();
+}
+
+// The item whose cost range holds position P: slot = number of prefix entries
+// <= P (one ballot per 64 slots), tile = offset in the slot / per-tile cost.
+__device__ __forceinline__ long item_at(const int* pref, int T, int tiles, long P) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int slot = 0;
+    for (int base = 0; base < kMaxExperts; base += kWave)
+        slot += __popcll(__ballot(pref[base + lane] <= P));
+    slot = uni(slot);
+    if (slot >= T) return static_cast<long>(T) * tiles;
+    const int lo = slot > 0 ? pref[slot - 1] : 0;
+    const int per_tile = (pref[slot] - lo) / tiles;
+    return static_cast<long>(slot) * tiles + (P - lo) / per_tile;
+}
+
+// Persistent workgroups; workgroup b takes the items (active expert, row
+// tile) whose cost ranges start in [b*C/G, (b+1)*C/G) of the total cost C
 // and, within each item, the passes of up to 8 tokens of its expert.
 template <int PHASE>
 __global__ __launch_bounds__(kThreads, 2) void ffn_kernel(FfnArgs a) {
@@ -502,21 +572,26 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_kernel(FfnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ int lds_pair[kMaxTok];
     __shared__ float lds_wt[kMaxTok];
-    const int T = *a.T;
+    __shared__ int pref[kMaxExperts];
+    __shared__ int wave_total[2];
+    __shared__ SlotRec recs[kMaxExperts];
+    const int T = uni(*a.T);
     const int rows = PHASE == 0 ? a.I : a.H;
     const int cols = PHASE == 0 ? a.H : a.I;
     const int rows_per_item = PHASE == 0 ? kRowsA : kRowsB;
     const int tiles = (rows + rows_per_item - 1) / rows_per_item;
-    const long total = static_cast<long>(T) * tiles;
-    const long begin = total * blockIdx.x / gridDim.x;
-    const long end = total * (blockIdx.x + 1) / gridDim.x;
+    price_slots<PHASE>(a, T, tiles, cols, recs, pref, wave_total);
+    const long C = pref[kMaxExperts - 1];
+    const long begin = item_at(pref, T, tiles, C * blockIdx.x / gridDim.x);
+    const long end = item_at(pref, T, tiles, C * (blockIdx.x + 1) / gridDim.x);
     if (begin >= end) return;
     const void* src = PHASE == 0 ? a.x : static_cast<const void*>(a.hbuf);
     const int src_dtype = PHASE == 0 ? a.x_dtype : MOE_DT_F32;
     const int by_token = PHASE == 0 ? a.k : 0;
 
     long item = begin;
-    Unit u = make_unit<PHASE>(a, item, 0, tiles, cols);
+    int cnt = 0;
+    Unit u = make_unit<PHASE>(recs, a.x_dtype, item, 0, tiles, cols, cnt);
     Rows<NR> R = unit_rows<PHASE, NR>(u, rows, cols);
     Block<NR, CB> pre;
     load_block<NR, CB>(R, 0, pre);
@@ -527,10 +602,10 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_kernel(FfnArgs a) {
         // the unit after u: the next pass of this item, else the next item
         long nitem = item;
         int nt0 = u.t0 + u.ct;
-        const int cnt = a.offsets[a.active[u.slot] + 1] - u.first;
         if (nt0 >= cnt) { nitem = item + 1; nt0 = 0; }
         const bool has_next = nitem < end;
-        const Unit nu = has_next ? make_unit<PHASE>(a, nitem, nt0, tiles, cols) : u;
+        int ncnt = cnt;
+        const Unit nu = has_next ? make_unit<PHASE>(recs, a.x_dtype, nitem, nt0, tiles, cols, ncnt) : u;
         const Rows<NR> NRws = unit_rows<PHASE, NR>(nu, rows, cols);
         if (u.fmt == MOE_W_BF16) {
             if (u.split) run_unit_mt<PHASE, MOE_W_BF16, true, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
@@ -551,6 +626,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_kernel(FfnArgs a) {
         u = nu;
         R = NRws;
         item = nitem;
+        cnt = ncnt;
     }
 }
 

@@ -148,13 +148,15 @@ size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
  *     g = W_gate,e x_i, u = W_up,e x_i, a = silu(g) * u, d = W_down,e a,
  *     y_i = sum over token i's filled slots of w[i, s] * d.
  *   table  : [N] moe_expert_handle (device); each expert's format may differ
- *   x      : [B, H] (x_dtype); with bf16/INT4 experts activations are used in
- *            bf16 (fp32 inputs are rounded to nearest even)
+ *   x      : [B, H] (x_dtype); with bf16/INT4 experts an fp32 activation a
+ *            enters the products as hi = bf16(a) plus lo = bf16(a - hi)
+ *            (about 16 significant bits); bf16 inputs are used exactly
  *   idx, w : routing output [B, k]; offsets, perm, active, T: dispatch output
  *   y      : [B, H] fp32, overwritten
- *   ws     : workspace of at least moe_ffn_workspace_bytes(B, k, H, I) bytes
- *            (scratch; calls that share a workspace must be ordered, e.g. on
- *            one stream).
+ *   ws     : workspace of at least moe_ffn_workspace_bytes(B, k, H, I) bytes,
+ *            256-byte aligned (scratch: the SwiGLU activations and the
+ *            weighted down projections; no contents need be preset; calls
+ *            that share a workspace must be ordered, e.g. on one stream).
  * Accumulation is fp32.  H and I must be multiples of 8 (of 128 when any
  * expert is INT4).  Each active expert's weights are streamed from HBM once
  * per pass of up to 8 of its tokens (up to 2 for INT4 experts).
