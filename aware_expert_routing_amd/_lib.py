@@ -50,6 +50,7 @@ _SIGNATURES = [
     ("moe_expert_ffn", [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _S, _P], _I),
     ("moe_handle_publish", [_P, _I, ctypes.POINTER(ExpertHandle), _P], _I),
     ("moe_quantize_int4_g128", [_P, _I, _I, _P, _P, _P], _I),
+    ("moe_pack_weights", [_I, _P, _P, _I, _I, _P, _P, _P], _I),
     ("moe_hotness_ema", [_P, _P, _I, _F, _P], _I),
     ("moe_status_str", [_I], ctypes.c_char_p),
     ("moe_last_error", [], ctypes.c_char_p),
@@ -188,6 +189,19 @@ def quantize_int4_g128(w_bf16, q=None, scales=None, stream=None):
     _check("moe_quantize_int4_g128", lib().moe_quantize_int4_g128(_ptr(w_bf16), rows, cols, _ptr(q),
                                                                   _ptr(scales), _stream(stream)))
     return q, scales
+
+
+def pack_weights(fmt: int, src, scales=None, dst=None, dst_scales=None, stream=None):
+    """Pack a row-major [rows, cols] matrix (INT4: the quantiser's bytes and
+    scales) into the tiled layout the expert FFN reads."""
+    rows = src.shape[0]
+    cols = {MOE_W_F32: src.shape[1], MOE_W_BF16: src.shape[1], MOE_W_INT4_G128: src.shape[1] * 2}[fmt]
+    dst = torch.empty_like(src) if dst is None else dst
+    if fmt == MOE_W_INT4_G128 and dst_scales is None:
+        dst_scales = torch.empty_like(scales)
+    _check("moe_pack_weights", lib().moe_pack_weights(fmt, _ptr(src), _ptr(scales), rows, cols, _ptr(dst),
+                                                      _ptr(dst_scales), _stream(stream)))
+    return dst, dst_scales
 
 
 def hotness_ema(S, cnt, alpha: float, stream=None):

@@ -106,7 +106,7 @@ MOE_API int moe_expert_ffn(const moe_expert_handle* table, int N, int H, int I, 
     int st = check_sizes(B, N, k);
     if (st) return st;
     if (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16) return fail(MOE_EINVAL, "bad x_dtype");
-    if (H < 8 || H % 8 || I < 8 || I % 8) return fail(MOE_EINVAL, "H and I must be positive multiples of 8");
+    if (H < 32 || H % 32 || I < 32 || I % 32) return fail(MOE_EINVAL, "H and I must be positive multiples of 32");
     if (H > 16384 || I > 16384) return fail(MOE_EUNSUPPORTED, "H and I above 16384 are not supported");
     if (ws_bytes < moe::ffn_workspace_bytes(B, k, H, I)) return fail(MOE_EINVAL, "workspace too small");
     if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
@@ -128,6 +128,11 @@ MOE_API int moe_handle_publish(moe_expert_handle* table, int e, const moe_expert
     if (!h->w_gate || !h->w_up || !h->w_down) return fail(MOE_EINVAL, "null weight pointer");
     if (h->fmt == MOE_W_INT4_G128 && (h->group != 128 || !h->s_gate || !h->s_up || !h->s_down))
         return fail(MOE_EINVAL, "INT4 handle needs group 128 and scale pointers");
+    auto misaligned = [](const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; };
+    if (misaligned(h->w_gate, 16) || misaligned(h->w_up, 16) || misaligned(h->w_down, 16))
+        return fail(MOE_EINVAL, "packed weights must be 16-byte aligned");
+    if (h->fmt == MOE_W_INT4_G128 && (misaligned(h->s_gate, 8) || misaligned(h->s_up, 8) || misaligned(h->s_down, 8)))
+        return fail(MOE_EINVAL, "packed scales must be 8-byte aligned");
     return hip_status(moe::launch_handle_publish(table, e, *h, as_stream(stream)), "moe_handle_publish");
 }
 
@@ -137,6 +142,25 @@ MOE_API int moe_quantize_int4_g128(const uint16_t* w, int rows, int cols, uint8_
     if (rows < 1 || cols < 128 || cols % 128) return fail(MOE_EINVAL, "cols must be a positive multiple of 128");
     return hip_status(moe::launch_quantize_int4(w, rows, cols, q, scales, as_stream(stream)),
                       "moe_quantize_int4_g128");
+}
+
+MOE_API int moe_pack_weights(int fmt, const void* src, const uint16_t* src_scales, int rows, int cols,
+                             void* dst, uint16_t* dst_scales, void* stream) {
+    if (fmt != MOE_W_F32 && fmt != MOE_W_BF16 && fmt != MOE_W_INT4_G128) return fail(MOE_EINVAL, "bad weight format");
+    if (!src || !dst) return fail(MOE_EINVAL, "null pointer");
+    if (fmt == MOE_W_INT4_G128 && (!src_scales || !dst_scales)) return fail(MOE_EINVAL, "INT4 needs scale pointers");
+    if (rows < 16 || rows % 16) return fail(MOE_EINVAL, "rows must be a positive multiple of 16");
+    const int tc = moe::tile_cols(fmt);
+    if (cols < tc || cols % tc) return fail(MOE_EINVAL, "cols must be a positive multiple of 16/32/128 (fp32/bf16/INT4)");
+    if (static_cast<long>(rows) * cols > (1L << 31)) return fail(MOE_EUNSUPPORTED, "matrix above 2^31 elements");
+    if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16)
+        return fail(MOE_EINVAL, "src and dst must be 16-byte aligned");
+    const size_t bytes = static_cast<size_t>(rows) * moe::weight_row_bytes(fmt, cols);
+    const char* s0 = static_cast<const char*>(src);
+    char* d0 = static_cast<char*>(dst);
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(MOE_EINVAL, "src and dst overlap");
+    return hip_status(moe::launch_pack_weights(fmt, src, src_scales, rows, cols, dst, dst_scales, as_stream(stream)),
+                      "moe_pack_weights");
 }
 
 MOE_API int moe_hotness_ema(float* S, const int32_t* cnt, int N, float alpha, void* stream) {

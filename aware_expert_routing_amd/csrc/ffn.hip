@@ -3,522 +3,272 @@
 // Page "Opportunistic Expert Activation (OEA) - L2", section 4 (Eq. 2 and
 // check 4): in decode each activated expert costs a fixed weight fetch b
 // plus a small per-token term a, and batched kernels must still load every
-// activated expert's weights.  This file streams each active expert's
-// gate/up/down weights from HBM once per call (per pass of up to 8 of the
-// expert's tokens) and applies every token of the pass to each loaded weight.
-// Page "DynaExq", section 2.2 / 3.2: each expert is reached through a handle
-// giving the active version's pointers and quantisation parameters, resolved
-// per work item, so one layer may mix bf16, fp32 and INT4 experts.
+// activated expert's weights.  Each active expert's gate/up/down weights are
+// streamed from HBM exactly once per call, whatever its token count, and
+// every one of its tokens is applied to each loaded tile.
+// Page "DynaExq", sections 2.2 / 3.2 / 3.4: each expert is reached through a
+// handle giving the active version's (prepacked) pointers and quantisation
+// parameters, resolved per work item, so one layer may mix formats.
 //
-// Work decomposition (a memory-bound GEMV, not a GEMM):
-//   * phase A (gate/up + SwiGLU): work items are (active expert, 16 rows of
-//     I); a lane owns the gate row and the up row of the same index, so the
-//     SwiGLU product needs no exchange.  16 lanes share a row: lane g reads
-//     bytes [256c + 16g, 256c + 16g + 16) of the row for chunks c, so one
-//     wave instruction reads four 256-byte row segments.
-//   * phase B (down + routing weight): items are (active expert, 32 rows of
-//     H); a lane owns two rows.
+// Work decomposition.  Weights are tiled (16 rows x 64 bytes per 1 KB tile,
+// in MFMA operand order; see pack.hip), so one wave load instruction reads a
+// whole contiguous kilobyte.  The contraction of a tile with the tokens uses
+// v_mfma_f32_16x16x32_bf16 (bf16 and INT4 weights) or
+// v_mfma_f32_16x16x4f32 (fp32 weights): A = the weight tile (row = lane%16),
+// B = 16 tokens' activations (token = lane%16), C = 16 rows x 16 tokens.
+// Its cost does not depend on how many of the 16 columns hold real tokens,
+// so one path serves experts with 1..16 tokens; up to 32 tokens use two
+// column tiles against the same weight tile (weights still read once), and
+// an expert with more tokens is handled in passes of 32 tokens (16 for
+// INT4 experts).  At these
+// token counts the MFMA units are nearly idle and the kernel is bound by HBM.
+//   * phase A: work items are (active expert, 2 row blocks of 16 rows of I);
+//     the wave streams the gate and up tiles of those rows over all of H and
+//     ends with h = silu(g) * u for every token of the expert.
+//   * phase B: items are (active expert, 4 row blocks of H) over all of I;
+//     the result is scaled by the pair's routing weight.
 //   * combine: y[i] = sum over token i's filled slots, in slot order.
-// Each 256-thread workgroup takes a contiguous range of items of about equal
-// streaming cost (every workgroup first prices the active experts).  A wave keeps
-// the weight loads of its next block of chunks in flight while it computes
-// the current block, and at the end of an item it has already issued the
-// loads of the next item's first block, so the weight stream does not stop
-// at item boundaries.  Activations of the pass's tokens are staged in LDS in
-// the weight format's layout (fp32 activations as bf16 hi/lo pairs for
-// bf16/INT4 weights); partial sums are reduced across the 16 lanes of a row
-// with DPP moves.  bf16 products use v_dot2_f32_bf16; INT4 nibbles become the
-// bf16 pair (128 + u, 128 + u') by bit operations, and the offset is removed
-// with the staged sum of the activations of each 32-column block.
+// Items belong to single waves (no barriers, no LDS staging): each wave owns
+// an equal share of the total streaming cost, keeps several tiles of loads
+// in flight (a register ring of D stages) and reads its tokens' activation
+// fragments straight from global memory (they stay in L1/L2).
+// INT4 tiles are one quantisation group: nibbles become the bf16 values
+// 128 + u by bit operations, one MFMA per 32 columns accumulates them, a
+// second MFMA with the constant -136 removes the offset (u - 8 = q), and the
+// group's per-row fp16 scale multiplies the result into the accumulator.
+// fp32 activations meeting bf16/INT4 weights enter as bf16 hi + lo pairs.
 #include "internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kLanesPerRow = 16;
-constexpr int kRowsPerInstr = kWave / kLanesPerRow;   // 4
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;               // 4
-constexpr int kChunkBytes = kLanesPerRow * 16;          // 256 row bytes per chunk
-constexpr int kMaxTok = 8;                              // tokens per pass
-constexpr int kMaxTokInt4 = 2;                          // INT4: fewer live registers
-constexpr int kLdsBytes = 56 * 1024;   // staged activations (dynamic LDS; static LDS adds ~6.7 KB)
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTileBytes = 1024;
+constexpr int kRbA = 2;   // row blocks per phase-A item
+constexpr int kRbB = 4;   // row blocks per phase-B item
 
-// phase A: 2 rows per lane (gate, up), 16 rows per item, 4 chunks per block
-constexpr int kNrA = 2, kRowsA = kWaves * kRowsPerInstr, kCbA = 4;
-// phase B: 2 rows per lane, 32 rows per item, 3 chunks per block
-constexpr int kNrB = 2, kRowsB = kWaves * kRowsPerInstr * kNrB, kCbB = 3;
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) u32x4* gptr_u32x4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) u32x2* gptr_u32x2;
 
-// 16-byte streaming load through the global (not flat) address space.
-__device__ __forceinline__ u32x4 load_nt16(const char* p) {
-    return __builtin_nontemporal_load((gptr_u32x4)(p));
+// Weight tiles: streamed once, non-temporal.  Activations: cached.
+__device__ __forceinline__ u32x4 load_w(const char* p) {
+    return __builtin_nontemporal_load((gptr_u32x4)p);
 }
-
-// Values that are equal across the wavefront, moved to scalar registers so
-// tests on them become scalar branches.
+__device__ __forceinline__ u32x4 load_a(const char* p) { return *(gptr_u32x4)p; }
+__device__ __forceinline__ u32x2 load_a8(const char* p) { return *(gptr_u32x2)p; }
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                           __builtin_bit_cast(bf16x2, b), c, false);
+template <typename T>
+__device__ __forceinline__ const T* uni_ptr(const T* p) {   // wave-uniform pointer into SGPRs
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Sum over the 16 lanes of a row group (DPP within each row of 16 lanes).
-__device__ __forceinline__ float row16_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)); // half-row mirror
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)); // row mirror
-    return v;
+__device__ __forceinline__ f32x4 mma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                  c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
+__device__ __forceinline__ uint32_t bf16_rne(float f) {   // finite inputs
+    const uint32_t u = __float_as_uint(f);
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
-
-__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, h));
-}
-
-// Bytes of one staged activation row and of one weight row, per format.
-// With `split`, an fp32 activation a is staged for bf16/INT4 weights as the
-// pair hi = bf16(a), lo = bf16(a - hi) (two bf16 rows), so products with bf16
-// weights keep about 16 significant bits of a; without it a is rounded to
-// bf16 once (exact for bf16 inputs).
-__host__ __device__ __forceinline__ int act_row_bytes(int fmt, int cols, bool split) {
-    return fmt == MOE_W_F32 ? cols * 4 : cols * 2 * (split ? 2 : 1);
-}
-__host__ __device__ __forceinline__ int act_sum_bytes(int fmt, int cols) {
-    return fmt == MOE_W_INT4_G128 ? (cols / 32) * 4 : 0;
-}
-__host__ __device__ __forceinline__ int weight_row_bytes(int fmt, int cols) {
-    return fmt == MOE_W_F32 ? cols * 4 : (fmt == MOE_W_BF16 ? cols * 2 : cols / 2);
-}
-__host__ __device__ __forceinline__ int tokens_per_pass(int fmt, int cols, bool split) {
-    const int per = act_row_bytes(fmt, cols, split) + act_sum_bytes(fmt, cols);
-    const int t = kLdsBytes / per;
-    const int cap = fmt == MOE_W_INT4_G128 ? kMaxTokInt4 : kMaxTok;
-    return t < cap ? t : cap;
-}
-
-// ---------------------------------------------------------------------------
-// Staging of one pass's activations into LDS.
-//   F32 : fp32 row;  BF16 : bf16 row (pairs (c, c+1));
-//   INT4: bf16 row with each 8-column block stored as pairs (c, c+4), plus
-//         the fp32 sum of every 32-column block (after the rows).
-// Phase A reads x rows (x_dtype) of token pair / k; phase B reads fp32 rows
-// of the SwiGLU buffer indexed by pair.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void load8_as_f32(const void* base, int dtype, int row, int cols, int c,
-                                             float (&v)[8]) {
-    if (dtype == MOE_DT_BF16) {
-        const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) +
-                                                        static_cast<size_t>(row) * cols + c);
-        const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+// 8 fp32 (two 16-byte chunks) -> bf16x8 hi and lo with hi + lo ~= f.
+__device__ __forceinline__ void split8(u32x4 c0, u32x4 c1, u32x4& hi, u32x4& lo) {
+    const uint32_t v[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    uint32_t h[4], l[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            v[2 * q] = __uint_as_float(u[q] << 16);
-            v[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
-        }
-    } else {
-        const float* p = static_cast<const float*>(base) + static_cast<size_t>(row) * cols + c;
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    for (int j = 0; j < 4; ++j) {
+        const float f0 = __uint_as_float(v[2 * j]), f1 = __uint_as_float(v[2 * j + 1]);
+        const uint32_t a = bf16_rne(f0), b = bf16_rne(f1);
+        h[j] = a | (b << 16);
+        l[j] = bf16_rne(f0 - __uint_as_float(a << 16)) | (bf16_rne(f1 - __uint_as_float(b << 16)) << 16);
     }
+    hi = u32x4{h[0], h[1], h[2], h[3]};
+    lo = u32x4{l[0], l[1], l[2], l[3]};
 }
-
-__device__ void stage_rows(int fmt, bool split, const void* base, int dtype, int by_token_k,
-                           const int32_t* pairs_g, int ct, int cols, char* lds, const float* wts_g,
-                           int* lds_pair, float* lds_wt) {
-    const int tid = threadIdx.x;
-    if (tid < ct) {
-        const int pr = pairs_g[tid];
-        lds_pair[tid] = pr;
-        lds_wt[tid] = wts_g[pr];
-    }
-    const int arow = act_row_bytes(fmt, cols, split);
-    const int half = cols * 2;   // byte offset of the lo row when split
-    const int blocks = cols / 8;
-    float* sums = reinterpret_cast<float*>(lds + ct * arow);
-    for (int j = tid; j < ct * blocks; j += kThreads) {
-        const int t = j / blocks, b = j - t * blocks;
-        const int pair = pairs_g[t];
-        const int row = by_token_k > 0 ? pair / by_token_k : pair;
-        float v[8];
-        load8_as_f32(base, dtype, row, cols, 8 * b, v);
-        char* dst = lds + t * arow;
-        if (fmt == MOE_W_F32) {
-            float4* d = reinterpret_cast<float4*>(dst + b * 32);
-            d[0] = make_float4(v[0], v[1], v[2], v[3]);
-            d[1] = make_float4(v[4], v[5], v[6], v[7]);
-            continue;
-        }
-        uint32_t h[8], l[8];
-        float s = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            h[q] = f32_to_bf16_rne(v[q]);
-            const float hv = __uint_as_float(h[q] << 16);
-            l[q] = split ? f32_to_bf16_rne(v[q] - hv) : 0u;
-            s += split ? hv + __uint_as_float(l[q] << 16) : hv;
-        }
-        const bool by4 = fmt == MOE_W_INT4_G128;
-        const uint4 oh = by4 ? make_uint4(h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16),
-                                          h[3] | (h[7] << 16))
-                             : make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                                          h[6] | (h[7] << 16));
-        *reinterpret_cast<uint4*>(dst + b * 16) = oh;
-        if (split) {
-            const uint4 ol = by4 ? make_uint4(l[0] | (l[4] << 16), l[1] | (l[5] << 16), l[2] | (l[6] << 16),
-                                              l[3] | (l[7] << 16))
-                                 : make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                                              l[6] | (l[7] << 16));
-            *reinterpret_cast<uint4*>(dst + half + b * 16) = ol;
-        }
-        if (by4) {
-            // a 32-column block is held by lanes j..j+3 (cols % 128 == 0)
-            s += __shfl_xor(s, 1, kWave);
-            s += __shfl_xor(s, 2, kWave);
-            if ((b & 3) == 0) sums[t * (cols / 32) + b / 4] = s;
-        }
-    }
+// INT4 dword (nibble i = column 2i, nibble i+4 = column 2i+1) -> bf16x8 of 128 + u.
+__device__ __forceinline__ u32x4 int4_as_bf16(uint32_t d) {
+    return u32x4{(d & 0x000F000Fu) | 0x43004300u, ((d >> 4) & 0x000F000Fu) | 0x43004300u,
+                 ((d >> 8) & 0x000F000Fu) | 0x43004300u, ((d >> 12) & 0x000F000Fu) | 0x43004300u};
 }
+constexpr uint32_t kBf16Neg136x2 = 0xC308C308u;   // bf16 pair (-136, -136)
 
 // ---------------------------------------------------------------------------
-// Cost-balanced partition.  Each workgroup first prices every active expert
-// (one thread per active slot, records kept in LDS): the cost of a row tile
-// is the sum over the expert's token passes of (16 + tokens), since for the
-// same weight bytes a pass of 8 tokens takes about 1.4x a pass of one
-// (measured) and every extra pass streams the tile again.  Workgroup b then
-// takes the items whose cost ranges start in [b*C/G, (b+1)*C/G) of the total
-// cost C, so experts with many tokens are spread over more workgroups.
+// Activation fragments.  For the tile covering input columns [c0, c0 + CT),
+// lane (n, q) needs columns c0 + q*CT/4 .. + CT/4 of token n: LANE_BYTES
+// bytes at byte offset s*TILE_BYTES + q*LANE_BYTES of the token's row, read
+// as NRAW 16-byte chunks (8 bytes for fp32 weights with bf16 activations).
 // ---------------------------------------------------------------------------
-struct SlotRec {                  // one phase's view of an active expert
-    const char* m0;               // phase A: gate, phase B: down
-    const char* m1;               // phase A: up
-    const uint16_t* s0;           // INT4 scales (or null)
-    const uint16_t* s1;
-    int32_t fmt, first, cnt, pad;
+template <int FMT, bool XF32>
+struct Act {
+    static constexpr int kCols = FMT == MOE_W_F32 ? 16 : (FMT == MOE_W_BF16 ? 32 : 128);
+    static constexpr int kLaneBytes = kCols / 4 * (XF32 ? 4 : 2);
+    static constexpr int kTileBytes = kLaneBytes * 4;
+    static constexpr int kRaw = kLaneBytes >= 16 ? kLaneBytes / 16 : 1;
 };
 
-__device__ __forceinline__ int tile_cost(int cnt, int per_pass) {
-    int c = 0;
-    for (int t0 = 0; t0 < cnt; t0 += per_pass) c += 16 + min(per_pass, cnt - t0);
-    return c;
+template <int PHASE, int FMT, bool XF32, int NT>
+constexpr int stages() {
+    constexpr int nmat = PHASE == 0 ? 2 : 1;
+    constexpr int rb = PHASE == 0 ? kRbA : kRbB;
+    constexpr int per = nmat * rb * (FMT == MOE_W_INT4_G128 ? 6 : 4) + NT * Act<FMT, XF32>::kRaw * 4;
+    constexpr int acc = nmat * rb * NT * 4;
+    // register budget for the ring (the rest holds addresses and temporaries;
+    // the split and INT4 paths need more temporaries)
+    constexpr int budget = (FMT == MOE_W_INT4_G128 || XF32) ? 150 : 200;
+    constexpr int fit = (budget - acc) / per;
+    if constexpr (FMT == MOE_W_INT4_G128 && (XF32 || NT > 1)) return 1;   // avoids spills
+    return fit >= 8 ? 8 : (fit >= 4 ? 4 : (fit >= 2 ? 2 : 1));
+}
+
+template <int PHASE, int FMT, bool XF32, int NT>
+struct Stage {
+    static constexpr int kMat = PHASE == 0 ? 2 : 1;
+    static constexpr int kRb = PHASE == 0 ? kRbA : kRbB;
+    u32x4 w[kMat][kRb];
+    u32x2 sc[kMat][kRb];                       // INT4 only
+    u32x4 x[NT][Act<FMT, XF32>::kRaw];
+};
+
+// Accumulate one tile (all row blocks, matrices and column tiles).  `keep`
+// is all ones, or zero for a padding position: the activation bits are
+// ANDed with it, so a padding tile adds exact zeros without a branch.
+template <int PHASE, int FMT, bool XF32, int NT>
+__device__ __forceinline__ void tile_mma(const Stage<PHASE, FMT, XF32, NT>& st_in, uint32_t keep,
+                                         f32x4 (&acc)[PHASE == 0 ? 2 : 1][PHASE == 0 ? kRbA : kRbB][NT]) {
+    using S = Stage<PHASE, FMT, XF32, NT>;
+    S st = st_in;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int c = 0; c < Act<FMT, XF32>::kRaw; ++c) st.x[t][c] &= keep;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if constexpr (FMT == MOE_W_BF16) {
+            if constexpr (!XF32) {
+#pragma unroll
+                for (int m = 0; m < S::kMat; ++m)
+#pragma unroll
+                    for (int r = 0; r < S::kRb; ++r) acc[m][r][t] = mma_bf16(st.w[m][r], st.x[t][0], acc[m][r][t]);
+            } else {
+                u32x4 hi, lo;
+                split8(st.x[t][0], st.x[t][1], hi, lo);
+#pragma unroll
+                for (int m = 0; m < S::kMat; ++m)
+#pragma unroll
+                    for (int r = 0; r < S::kRb; ++r) {
+                        acc[m][r][t] = mma_bf16(st.w[m][r], hi, acc[m][r][t]);
+                        acc[m][r][t] = mma_bf16(st.w[m][r], lo, acc[m][r][t]);
+                    }
+            }
+        } else if constexpr (FMT == MOE_W_F32) {
+            float xv[4];
+            if constexpr (XF32) {
+                xv[0] = __uint_as_float(st.x[t][0].x);
+                xv[1] = __uint_as_float(st.x[t][0].y);
+                xv[2] = __uint_as_float(st.x[t][0].z);
+                xv[3] = __uint_as_float(st.x[t][0].w);
+            } else {
+                xv[0] = __uint_as_float(st.x[t][0].x << 16);
+                xv[1] = __uint_as_float(st.x[t][0].x & 0xffff0000u);
+                xv[2] = __uint_as_float(st.x[t][0].y << 16);
+                xv[3] = __uint_as_float(st.x[t][0].y & 0xffff0000u);
+            }
+#pragma unroll
+            for (int m = 0; m < S::kMat; ++m)
+#pragma unroll
+                for (int r = 0; r < S::kRb; ++r) {
+                    const u32x4 wv = st.w[m][r];
+                    acc[m][r][t] = mma_f32(__uint_as_float(wv.x), xv[0], acc[m][r][t]);
+                    acc[m][r][t] = mma_f32(__uint_as_float(wv.y), xv[1], acc[m][r][t]);
+                    acc[m][r][t] = mma_f32(__uint_as_float(wv.z), xv[2], acc[m][r][t]);
+                    acc[m][r][t] = mma_f32(__uint_as_float(wv.w), xv[3], acc[m][r][t]);
+                }
+        } else {   // INT4: one tile = one group of 128 columns = 4 MFMA steps
+            constexpr int kParts = XF32 ? 2 : 1;
+            u32x4 xb[4][kParts];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (XF32) split8(st.x[t][2 * j], st.x[t][2 * j + 1], xb[j][0], xb[j][kParts - 1]);
+                else xb[j][0] = st.x[t][j];
+            }
+            const u32x4 neg = {kBf16Neg136x2, kBf16Neg136x2, kBf16Neg136x2, kBf16Neg136x2};
+            f32x4 corr = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int h = 0; h < kParts; ++h) corr = mma_bf16(neg, xb[j][h], corr);
+#pragma unroll
+            for (int m = 0; m < S::kMat; ++m)
+#pragma unroll
+                for (int r = 0; r < S::kRb; ++r) {
+                    const u32x4 wv = st.w[m][r];
+                    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+                    f32x4 tmp = corr;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const u32x4 av = int4_as_bf16(wd[j]);
+#pragma unroll
+                        for (int h = 0; h < kParts; ++h) tmp = mma_bf16(av, xb[j][h], tmp);
+                    }
+                    const u32x2 sc = st.sc[m][r];
+                    const float s0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sc.x)));
+                    const float s1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sc.x >> 16)));
+                    const float s2 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sc.y)));
+                    const float s3 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sc.y >> 16)));
+                    f32x4& c = acc[m][r][t];
+                    c.x = fmaf(s0, tmp.x, c.x);
+                    c.y = fmaf(s1, tmp.y, c.y);
+                    c.z = fmaf(s2, tmp.z, c.z);
+                    c.w = fmaf(s3, tmp.w, c.w);
+                }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
-// One unit of work of a workgroup: an item (active expert, row tile) and one
-// pass of that expert's tokens.  All fields are wave-uniform.
+// Active-expert records and the cost-balanced partition.  Every workgroup
+// prices the active experts first (one thread per active slot): an expert
+// has ceil(row_blocks / rb) items; an item's cost is its tile count times a
+// per-tile weight (INT4 tiles also carry 4x the activation traffic; every
+// extra 16-token column tile adds MFMA work).  Wave w of W takes the items
+// whose cost ranges start in [w*C/W, (w+1)*C/W) of the total cost C.
 // ---------------------------------------------------------------------------
-struct Unit {
-    int slot, tile, t0, ct;   // active slot, row tile, first token of the pass, tokens in it
-    int fmt;
-    bool split;
-    int first;                // first routed pair of the expert in perm
-    const char* m0;           // phase A: gate, phase B: down
-    const char* m1;           // phase A: up
-    const uint16_t* s0;
-    const uint16_t* s1;
+struct SlotRec {
+    const char* m0;          // phase A: gate, phase B: down (packed tiles)
+    const char* m1;          // phase A: up
+    const char* s0;          // INT4 packed scales (or null)
+    const char* s1;
+    int32_t fmt, first, cnt, ipp;   // ipp: items per token pass
 };
+
+// Tokens per pass: two 16-token column tiles (one for INT4, whose
+// activation fragments are four times larger).
+__host__ __device__ __forceinline__ int pass_tokens(int fmt) { return fmt == MOE_W_INT4_G128 ? 16 : 32; }
+
+__host__ __device__ __forceinline__ int col_tiles_for(int cnt) { return cnt <= 16 ? 1 : 2; }
 
 template <int PHASE>
-__device__ __forceinline__ Unit make_unit(const SlotRec* recs, int x_dtype, long item, int t0, int tiles,
-                                          int cols, int& cnt) {
-    Unit u;
-    u.slot = uni(static_cast<int>(item / tiles));
-    u.tile = uni(static_cast<int>(item - static_cast<long>(u.slot) * tiles));
-    const SlotRec& r = recs[u.slot];
-    u.fmt = uni(r.fmt);
-    u.split = u.fmt != MOE_W_F32 && (PHASE == 1 || x_dtype == MOE_DT_F32);
-    u.first = uni(r.first);
-    cnt = uni(r.cnt);
-    const int per_pass = tokens_per_pass(u.fmt, cols, u.split);
-    u.t0 = uni(t0);
-    u.ct = uni(min(per_pass, cnt - t0));
-    u.m0 = r.m0;
-    u.m1 = r.m1;
-    u.s0 = r.s0;
-    u.s1 = r.s1;
-    return u;
-}
-
-// Per-lane row addresses of a unit: phase A -> (gate r, up r); phase B ->
-// rows base + 4j of the down matrix.  Rows at or beyond `rows` are clamped to
-// row 0 so every load stays inside the matrix; their results are not stored.
-template <int NR>
-struct Rows {
-    const char* p[NR];
-    const uint16_t* s[NR];
-    int id[NR];
-    int rbytes;     // bytes per weight row
-    int nchunks;    // 256-byte chunks per row (the last may be partial)
-};
-
-template <int PHASE, int NR>
-__device__ __forceinline__ Rows<NR> unit_rows(const Unit& u, int rows, int cols) {
-    Rows<NR> R;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    R.rbytes = uni(weight_row_bytes(u.fmt, cols));
-    R.nchunks = uni((R.rbytes + kChunkBytes - 1) / kChunkBytes);
-    const int sgroups = cols / 128;
-    if constexpr (PHASE == 0) {
-        const int row = u.tile * kRowsA + wave * kRowsPerInstr + lane / kLanesPerRow;
-        const int rr = row < rows ? row : 0;
-        R.p[0] = u.m0 + static_cast<size_t>(rr) * R.rbytes;
-        R.p[1] = u.m1 + static_cast<size_t>(rr) * R.rbytes;
-        R.s[0] = u.s0 + static_cast<size_t>(rr) * sgroups;
-        R.s[1] = u.s1 + static_cast<size_t>(rr) * sgroups;
-        R.id[0] = R.id[1] = row;
-    } else {
-        const int base = u.tile * kRowsB + wave * (kRowsPerInstr * NR) + lane / kLanesPerRow;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const int row = base + r * kRowsPerInstr;
-            const int rr = row < rows ? row : 0;
-            R.p[r] = u.m0 + static_cast<size_t>(rr) * R.rbytes;
-            R.s[r] = u.s0 + static_cast<size_t>(rr) * sgroups;
-            R.id[r] = row;
-        }
-    }
-    return R;
-}
-
-// Weight block: CB chunks of NR rows, raw 16-byte loads.
-template <int NR, int CB>
-struct Block {
-    u32x4 w[CB][NR];
-};
-
-// Issue the loads of block `blk`, unconditionally: offsets are clamped to the
-// row's last 16 bytes, so chunks past the row (skipped when computing) and the
-// lanes past the end of a partial chunk (masked when computing) re-read bytes
-// of the same row instead of branching around the load.
-template <int NR, int CB>
-__device__ __forceinline__ void load_block(const Rows<NR>& R, int blk, Block<NR, CB>& b) {
-    const int g = threadIdx.x & (kLanesPerRow - 1);
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-        const int off = min((blk * CB + c) * kChunkBytes + g * 16, R.rbytes - 16);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) b.w[c][r] = load_nt16(R.p[r] + off);
-    }
-}
-
-// Multiply-accumulate one chunk of NR rows against the pass's MT tokens.
-template <int FMT, bool SPLIT, int NR, int MT>
-__device__ __forceinline__ void chunk_fma(const u32x4 (&wv)[NR], const float (&scale)[NR], int off,
-                                          int ct, const char* lds, int arow, int half,
-                                          const float* sums, int cols, float (&acc)[NR][MT]) {
-    if constexpr (FMT == MOE_W_F32) {
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t < ct) {
-                const uint4 xv = *reinterpret_cast<const uint4*>(lds + t * arow + off);
-#pragma unroll
-                for (int r = 0; r < NR; ++r) {
-                    float a = acc[r][t];
-                    a = __builtin_fmaf(__uint_as_float(wv[r].x), __uint_as_float(xv.x), a);
-                    a = __builtin_fmaf(__uint_as_float(wv[r].y), __uint_as_float(xv.y), a);
-                    a = __builtin_fmaf(__uint_as_float(wv[r].z), __uint_as_float(xv.z), a);
-                    a = __builtin_fmaf(__uint_as_float(wv[r].w), __uint_as_float(xv.w), a);
-                    acc[r][t] = a;
-                }
-            }
-        }
-    } else if constexpr (FMT == MOE_W_BF16) {
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t < ct) {
-                const uint4 xv = *reinterpret_cast<const uint4*>(lds + t * arow + off);
-                uint4 xl = make_uint4(0u, 0u, 0u, 0u);
-                if constexpr (SPLIT) xl = *reinterpret_cast<const uint4*>(lds + t * arow + half + off);
-#pragma unroll
-                for (int r = 0; r < NR; ++r) {
-                    float a = acc[r][t];
-                    a = dot2_bf16(wv[r].x, xv.x, a);
-                    a = dot2_bf16(wv[r].y, xv.y, a);
-                    a = dot2_bf16(wv[r].z, xv.z, a);
-                    a = dot2_bf16(wv[r].w, xv.w, a);
-                    if constexpr (SPLIT) {
-                        a = dot2_bf16(wv[r].x, xl.x, a);
-                        a = dot2_bf16(wv[r].y, xl.y, a);
-                        a = dot2_bf16(wv[r].z, xl.z, a);
-                        a = dot2_bf16(wv[r].w, xl.w, a);
-                    }
-                    acc[r][t] = a;
-                }
-            }
-        }
-    } else {
-        // INT4: 32 weights (columns col0 .. col0+31 of one 128-group) per lane.
-        // (w >> 4s) & 0x000f000f | 0x43004300 is the bf16 pair (128 + u_s,
-        // 128 + u_{s+4}) of the word's nibbles, matching the staged pairs (c, c+4).
-        const int col0 = off * 2;
-        uint32_t pk[NR][16];
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    pk[r][4 * q + s] = ((wv[r][q] >> (4 * s)) & 0x000f000fu) | 0x43004300u;
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t < ct) {
-                const char* xr = lds + t * arow + col0 * 2;
-                float d[NR];
-#pragma unroll
-                for (int r = 0; r < NR; ++r) d[r] = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint4 xv = *reinterpret_cast<const uint4*>(xr + 16 * q);
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        d[r] = dot2_bf16(pk[r][4 * q + 0], xv.x, d[r]);
-                        d[r] = dot2_bf16(pk[r][4 * q + 1], xv.y, d[r]);
-                        d[r] = dot2_bf16(pk[r][4 * q + 2], xv.z, d[r]);
-                        d[r] = dot2_bf16(pk[r][4 * q + 3], xv.w, d[r]);
-                    }
-                    if constexpr (SPLIT) {
-                        const uint4 xl = *reinterpret_cast<const uint4*>(xr + half + 16 * q);
-#pragma unroll
-                        for (int r = 0; r < NR; ++r) {
-                            d[r] = dot2_bf16(pk[r][4 * q + 0], xl.x, d[r]);
-                            d[r] = dot2_bf16(pk[r][4 * q + 1], xl.y, d[r]);
-                            d[r] = dot2_bf16(pk[r][4 * q + 2], xl.z, d[r]);
-                            d[r] = dot2_bf16(pk[r][4 * q + 3], xl.w, d[r]);
-                        }
-                    }
-                }
-                const float xs = sums[t * (cols / 32) + col0 / 32];
-#pragma unroll
-                for (int r = 0; r < NR; ++r)   // sum (128 + u) x - 136 sum x = sum (u - 8) x
-                    acc[r][t] = __builtin_fmaf(scale[r], __builtin_fmaf(-136.0f, xs, d[r]), acc[r][t]);
-                __builtin_amdgcn_sched_barrier(0);   // one token's LDS reads at a time
-            }
-        }
-    }
-}
-
-// Run one unit: blocks 0..nblk-1 with the next block's loads in flight while
-// the current one is computed; the last block issues the loads of the next
-// unit's first block into `pre`.  Then reduce across the 16 lanes of each row
-// and write the results.
-template <int PHASE, int FMT, bool SPLIT, int NR, int CB, int MT>
-__device__ __forceinline__ void run_unit(const FfnArgs& a, const Unit& u, const Rows<NR>& R,
-                                         const Rows<NR>& NRws, bool has_next, int rows, int cols,
-                                         const char* lds, const int* lds_pair, const float* lds_wt,
-                                         Block<NR, CB>& pre) {
-    const int g = threadIdx.x & (kLanesPerRow - 1);
-    const int nblk = (R.nchunks + CB - 1) / CB;
-    const int arow = act_row_bytes(FMT, cols, SPLIT);
-    const int half = cols * 2;
-    const float* sums = reinterpret_cast<const float*>(lds + u.ct * arow);
-    const bool partial = (R.rbytes % kChunkBytes) != 0;
-    float acc[NR][MT];
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[r][t] = 0.0f;
-    // the block after the unit's last one: the next unit's first, or (at the
-    // end of the range) a harmless re-read of this unit's first block
-    const Rows<NR>& after = has_next ? NRws : R;
-    for (int blk = 0; blk < nblk; ++blk) {
-        Block<NR, CB> cur = pre;
-        if (blk + 1 < nblk) load_block<NR, CB>(R, blk + 1, pre);
-        else load_block<NR, CB>(after, 0, pre);
-#pragma unroll
-        for (int c = 0; c < CB; ++c) {
-            const int chunk = blk * CB + c;
-            if (chunk >= R.nchunks) break;
-            const int off_raw = chunk * kChunkBytes + g * 16;
-            const bool lane_ok = off_raw < R.rbytes;
-            const int off = min(off_raw, R.rbytes - 16);
-            float sc[NR];
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                sc[r] = 1.0f;
-                if constexpr (FMT == MOE_W_INT4_G128) sc[r] = f16_bits_to_f32(R.s[r][(off * 2) / 128]);
-            }
-            u32x4 w[NR];
-#pragma unroll
-            for (int r = 0; r < NR; ++r) w[r] = cur.w[c][r];
-            if (partial && chunk == R.nchunks - 1) {   // wave-uniform test
-#pragma unroll
-                for (int r = 0; r < NR; ++r) {
-                    if constexpr (FMT == MOE_W_INT4_G128) sc[r] = lane_ok ? sc[r] : 0.0f;
-                    else w[r] = lane_ok ? w[r] : u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-            chunk_fma<FMT, SPLIT, NR, MT>(w, sc, off, u.ct, lds, arow, half, sums, cols, acc);
-        }
-    }
-    const bool writer = g < u.ct;
-    const int pair = writer ? lds_pair[g] : 0;
-    if constexpr (PHASE == 0) {
-        float mg = 0.0f, mu = 0.0f;
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const float sg = row16_sum(acc[0][t]);
-            const float su = row16_sum(acc[1][t]);
-            if (g == t) { mg = sg; mu = su; }
-        }
-        if (writer && R.id[0] < rows) a.hbuf[static_cast<size_t>(pair) * a.I + R.id[0]] = silu(mg) * mu;
-    } else {
-        const float wgt = writer ? lds_wt[g] : 0.0f;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            float mine = 0.0f;
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const float s = row16_sum(acc[r][t]);
-                if (g == t) mine = s;
-            }
-            if (writer && R.id[r] < rows)
-                a.dbuf[static_cast<size_t>(pair) * a.H + R.id[r]] = wgt * mine;
-        }
-    }
-}
-
-template <int PHASE, int FMT, bool SPLIT, int NR, int CB>
-__device__ __forceinline__ void run_unit_mt(const FfnArgs& a, const Unit& u, const Rows<NR>& R,
-                                            const Rows<NR>& NRws, bool has_next, int rows, int cols,
-                                            const char* lds, const int* lds_pair, const float* lds_wt,
-                                            Block<NR, CB>& pre) {
-#define MOE_RUN(MTV) \
-    run_unit<PHASE, FMT, SPLIT, NR, CB, MTV>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre)
-    if (u.ct <= 1) {
-        MOE_RUN(1);
-    } else if (u.ct <= 2) {
-        MOE_RUN(2);
-    } else if constexpr (FMT != MOE_W_INT4_G128) {   // INT4 passes hold at most 2 tokens
-        if (u.ct <= 4) MOE_RUN(4);
-        else MOE_RUN(8);
-    }
-#undef MOE_RUN
-}
-
-// Prologue of both phases: thread s < T reads active slot s's expert, its
-// handle and token range into recs[s]; pref[s] receives the inclusive prefix
-// of the slots' costs (slots >= T cost 0, so pref[127] is the total).
-template <int PHASE>
-__device__ __forceinline__ void price_slots(const FfnArgs& a, int T, int tiles, int cols, SlotRec* recs,
-                                            int* pref, int* wave_total) {
+__device__ __forceinline__ void price_slots(const FfnArgs& a, int T, SlotRec* recs, int* pref_cost,
+                                            int* pref_item, int* wave_tot) {
     const int s = threadIdx.x;
     const int lane = s & (kWave - 1);
-    int cost = 0;
+    const int rows = PHASE == 0 ? a.I : a.H, cols = PHASE == 0 ? a.H : a.I;
+    const int rb = PHASE == 0 ? kRbA : kRbB;
+    int cost = 0, items = 0;
     if (s < T) {
         const int e = a.active[s];
         const moe_expert_handle& h = a.table[e];
@@ -526,107 +276,272 @@ __device__ __forceinline__ void price_slots(const FfnArgs& a, int T, int tiles, 
         r.fmt = h.fmt;
         r.m0 = static_cast<const char*>(PHASE == 0 ? h.w_gate : h.w_down);
         r.m1 = PHASE == 0 ? static_cast<const char*>(h.w_up) : nullptr;
-        r.s0 = PHASE == 0 ? h.s_gate : h.s_down;
-        r.s1 = PHASE == 0 ? h.s_up : nullptr;
+        r.s0 = reinterpret_cast<const char*>(PHASE == 0 ? h.s_gate : h.s_down);
+        r.s1 = PHASE == 0 ? reinterpret_cast<const char*>(h.s_up) : nullptr;
         r.first = a.offsets[e];
         r.cnt = a.offsets[e + 1] - r.first;
-        r.pad = 0;
+        r.ipp = (rows / 16 + rb - 1) / rb;
         recs[s] = r;
-        const bool split = r.fmt != MOE_W_F32 && (PHASE == 1 || a.x_dtype == MOE_DT_F32);
-        cost = tiles * tile_cost(r.cnt, tokens_per_pass(r.fmt, cols, split));
+        const bool fits = (r.fmt == MOE_W_F32 || r.fmt == MOE_W_BF16 || r.fmt == MOE_W_INT4_G128) &&
+                          cols % tile_cols(r.fmt) == 0 && r.cnt > 0;
+        if (fits) {
+            const int pt = pass_tokens(r.fmt);
+            const int passes = (r.cnt + pt - 1) / pt;
+            const int nt = col_tiles_for(min(r.cnt, pt));
+            items = passes * r.ipp;
+            const int tiles = rb * (weight_row_bytes(r.fmt, cols) / 64);
+            const int per_tile = r.fmt == MOE_W_INT4_G128 ? 12 + 2 * nt : 8 + nt;
+            cost = items * tiles * per_tile;
+        }
     }
-    if (s < kMaxExperts) {              // waves 0 and 1: inclusive scan of 64 slots each
+    if (s < 2 * kWave) {   // waves 0 and 1: inclusive scans of 64 slots each
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
-            const int v = __shfl_up(cost, off);
-            if (lane >= off) cost += v;
+            const int vc = __shfl_up(cost, off);
+            const int vi = __shfl_up(items, off);
+            if (lane >= off) { cost += vc; items += vi; }
         }
-        if (lane == kWave - 1) wave_total[s / kWave] = cost;
+        if (lane == kWave - 1) { wave_tot[2 * (s / kWave)] = cost; wave_tot[2 * (s / kWave) + 1] = items; }
     }
     __syncthreads();
-    if (s < kMaxExperts) pref[s] = cost + (s >= kWave ? wave_total[0] : 0);
+    if (s < 2 * kWave) {
+        pref_cost[s] = cost + (s >= kWave ? wave_tot[0] : 0);
+        pref_item[s] = items + (s >= kWave ? wave_tot[1] : 0);
+    }
     __syncthreads();
 }
 
-// The item whose cost range holds position P: slot = number of prefix entries
-// <= P (one ballot per 64 slots), tile = offset in the slot / per-tile cost.
-__device__ __forceinline__ long item_at(const int* pref, int T, int tiles, long P) {
+// Number of prefix entries <= v (the slot whose range holds v), per wave.
+__device__ __forceinline__ int count_le(const int* pref, long v) {
     const int lane = threadIdx.x & (kWave - 1);
-    int slot = 0;
-    for (int base = 0; base < kMaxExperts; base += kWave)
-        slot += __popcll(__ballot(pref[base + lane] <= P));
-    slot = uni(slot);
-    if (slot >= T) return static_cast<long>(T) * tiles;
-    const int lo = slot > 0 ? pref[slot - 1] : 0;
-    const int per_tile = (pref[slot] - lo) / tiles;
-    return static_cast<long>(slot) * tiles + (P - lo) / per_tile;
+    int n = 0;
+#pragma unroll
+    for (int base = 0; base < kMaxExperts; base += kWave) n += __popcll(__ballot(pref[base + lane] <= v));
+    return uni(n);
 }
 
-// Persistent workgroups; workgroup b takes the items (active expert, row
-// tile) whose cost ranges start in [b*C/G, (b+1)*C/G) of the total cost C
-// and, within each item, the passes of up to 8 tokens of its expert.
+// The item whose cost range holds position P (the total item count past the end).
+__device__ __forceinline__ int item_at(const int* pref_cost, const int* pref_item, int T, long P) {
+    const int slot = count_le(pref_cost, P);
+    if (slot >= T) return pref_item[kMaxExperts - 1];
+    const int c_lo = slot > 0 ? pref_cost[slot - 1] : 0;
+    const int i_lo = slot > 0 ? pref_item[slot - 1] : 0;
+    const int n_items = pref_item[slot] - i_lo;
+    const int per_item = (pref_cost[slot] - c_lo) / n_items;
+    return i_lo + static_cast<int>((P - c_lo) / per_item);
+}
+
+// ---------------------------------------------------------------------------
+// One wave streams `count` consecutive items of one expert, starting at item
+// `local0` of that expert.  Positions (item, tile) run through a ring of D
+// stages: while tile p is multiplied, the loads of tile p + D are issued.
+// Each item's tile count is padded to a multiple of D; padding positions
+// re-load the item's last tile (cache hits) and skip the multiply.  Row
+// blocks past the matrix end are clamped to the last one and not stored.
+// ---------------------------------------------------------------------------
+// Arguments are plain values (no struct in private memory); every one is
+// wave-uniform and is moved to SGPRs, so the ring's loads and waits are
+// scheduled per stage rather than behind divergent branches.
+template <int PHASE, int FMT, bool XF32, int NT>
+__device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_in, const float* w_in,
+                                       float* hbuf_in, float* dbuf_in, int k_in, int H_in, int I_in,
+                                       const char* m0, const char* m1, const char* s0, const char* s1,
+                                       int first_in, int cnt_in, int local0_in, int count_in) {
+    const int local0 = uni(local0_in), count = uni(count_in);
+    const int k = uni(k_in), H = uni(H_in), I = uni(I_in);
+    const char* xg = uni_ptr(x_in);
+    const int32_t* perm = uni_ptr(perm_in);
+    const float* wg = uni_ptr(w_in);
+    float* hbuf = const_cast<float*>(uni_ptr(hbuf_in));
+    float* dbuf = const_cast<float*>(uni_ptr(dbuf_in));
+    using St = Stage<PHASE, FMT, XF32, NT>;
+    using Ac = Act<FMT, XF32>;
+    constexpr int kMat = St::kMat, kRb = St::kRb;
+    constexpr int D = stages<PHASE, FMT, XF32, NT>();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int n = lane & 15, q = lane >> 4;
+    const int rows = PHASE == 0 ? I : H, cols = PHASE == 0 ? H : I;
+    const int nrb = rows / 16;
+    const int S = uni(weight_row_bytes(FMT, cols) / 64);     // tiles per row block
+    const int Sp = uni((S + D - 1) / D * D);
+    const int first = uni(first_in), cnt = uni(cnt_in);
+    const char* mb[kMat];
+    const char* sb[kMat];
+    mb[0] = uni_ptr(m0);
+    sb[0] = uni_ptr(s0);
+    if constexpr (kMat == 2) { mb[1] = uni_ptr(m1); sb[1] = uni_ptr(s1); }
+
+    // activation rows of this lane's tokens (column tile t: token 16 t + n)
+    const char* arow[NT];
+    int pair[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int tok = 16 * t + n;
+        pair[t] = perm[first + (tok < cnt ? tok : 0)];
+        if constexpr (PHASE == 0)
+            arow[t] = xg + static_cast<size_t>(pair[t] / k) * H * (XF32 ? 4 : 2);
+        else
+            arow[t] = reinterpret_cast<const char*>(hbuf + static_cast<size_t>(pair[t]) * I);
+        arow[t] += q * Ac::kLaneBytes;
+    }
+
+    St ring[D];
+    auto issue = [&](St& st, int item, int s) {
+        const int se = s < S ? s : S - 1;
+#pragma unroll
+        for (int m = 0; m < kMat; ++m)
+#pragma unroll
+            for (int r = 0; r < kRb; ++r) {
+                int rb = (local0 + item) * kRb + r;
+                rb = rb < nrb ? rb : nrb - 1;
+                const long tile = static_cast<long>(rb) * S + se;
+                st.w[m][r] = load_w(mb[m] + tile * kTileBytes + lane * 16);
+                if constexpr (FMT == MOE_W_INT4_G128) st.sc[m][r] = load_a8(sb[m] + (tile * 16 + 4 * q) * 2);
+            }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int c = 0; c < Ac::kRaw; ++c) {
+                const char* p = arow[t] + static_cast<long>(se) * Ac::kTileBytes + 16 * c;
+                if constexpr (Ac::kLaneBytes == 8) {
+                    const u32x2 v = load_a8(p);
+                    st.x[t][c] = u32x4{v.x, v.y, 0u, 0u};
+                } else {
+                    st.x[t][c] = load_a(p);
+                }
+            }
+    };
+
+    f32x4 acc[kMat][kRb][NT];
+    auto zero = [&]() {
+#pragma unroll
+        for (int m = 0; m < kMat; ++m)
+#pragma unroll
+            for (int r = 0; r < kRb; ++r)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[m][r][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+    zero();
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(ring[d], 0, d);
+
+    const int nblk = count * (Sp / D);
+    int ci = 0, cs = 0;   // item and first tile of the block being multiplied
+    int ii = 0, is = 0;   // item and first tile of the block being issued
+    // The stage loop has no branches (padding is masked, the last block is
+    // peeled), so the waits before each multiply cover only that stage.
+    for (int blk = 0; blk < nblk; ++blk) {
+        const bool last = blk + 1 == nblk;
+        is += D;
+        if (is == Sp) { is = 0; ++ii; }
+        if (!last) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                tile_mma<PHASE, FMT, XF32, NT>(ring[d], cs + d < S ? ~0u : 0u, acc);
+                issue(ring[d], ii, is + d);
+            }
+        } else {
+#pragma unroll
+            for (int d = 0; d < D; ++d) tile_mma<PHASE, FMT, XF32, NT>(ring[d], cs + d < S ? ~0u : 0u, acc);
+        }
+        cs += D;
+        if (cs == Sp) {   // item done: write its rows for every real token
+            const int rb0 = (local0 + ci) * kRb;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (16 * t + n >= cnt) continue;
+                if constexpr (PHASE == 0) {
+                    float* hrow = hbuf + static_cast<size_t>(pair[t]) * I;
+#pragma unroll
+                    for (int r = 0; r < kRb; ++r) {
+                        if (rb0 + r >= nrb) continue;
+                        const f32x4 g = acc[0][r][t], u = acc[kMat - 1][r][t];
+                        const float4 hv = make_float4(silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z,
+                                                      silu(g.w) * u.w);
+                        *reinterpret_cast<float4*>(hrow + (rb0 + r) * 16 + 4 * q) = hv;
+                    }
+                } else {
+                    const float wt = wg[pair[t]];
+                    float* drow = dbuf + static_cast<size_t>(pair[t]) * H;
+#pragma unroll
+                    for (int r = 0; r < kRb; ++r) {
+                        if (rb0 + r >= nrb) continue;
+                        const f32x4 v = acc[0][r][t];
+                        *reinterpret_cast<float4*>(drow + (rb0 + r) * 16 + 4 * q) =
+                            make_float4(wt * v.x, wt * v.y, wt * v.z, wt * v.w);
+                    }
+                }
+            }
+            zero();
+            cs = 0;
+            ++ci;
+        }
+    }
+}
+
+// Out-of-line copy for the formats off the hot path (fp32, INT4, bf16 with
+// fp32 activations in phase A): a call keeps their register needs apart
+// from the inlined bf16 path.
+template <int PHASE, int FMT, bool XF32, int NT>
+__device__ __noinline__ void run_items_call(const char* x, const int32_t* perm, const float* w, float* hbuf,
+                                            float* dbuf, int k, int H, int I, const char* m0, const char* m1,
+                                            const char* s0, const char* s1, int first, int cnt, int local0,
+                                            int count) {
+    run_items<PHASE, FMT, XF32, NT>(x, perm, w, hbuf, dbuf, k, H, I, m0, m1, s0, s1, first, cnt, local0, count);
+}
+
+template <int PHASE, int FMT, bool XF32>
+__device__ __forceinline__ void run_nt(const FfnArgs& a, const SlotRec& rec, int local0, int count) {
+    // bf16 weights with bf16 activations (phase A) or fp32 h (phase B) run inline
+    constexpr bool hot = FMT == MOE_W_BF16 && XF32 == (PHASE == 1);
+#define MOE_RUN(FN, NTV)                                                                                  \
+    FN<PHASE, FMT, XF32, NTV>(static_cast<const char*>(a.x), a.perm, a.w, a.hbuf, a.dbuf, a.k, a.H, a.I,  \
+                              rec.m0, rec.m1, rec.s0, rec.s1, rec.first, rec.cnt, local0, count)
+    if constexpr (hot) {
+        if (rec.cnt <= 16) MOE_RUN(run_items, 1);
+        else MOE_RUN(run_items, 2);
+    } else {
+        if (FMT == MOE_W_INT4_G128 || rec.cnt <= 16) MOE_RUN(run_items_call, 1);
+        else MOE_RUN(run_items_call, FMT == MOE_W_INT4_G128 ? 1 : 2);
+    }
+#undef MOE_RUN
+}
+
+template <int PHASE, bool XF32>
+__device__ __forceinline__ void run_fmt(const FfnArgs& a, const SlotRec& rec, int local0, int count) {
+    if (rec.fmt == MOE_W_BF16) run_nt<PHASE, MOE_W_BF16, XF32>(a, rec, local0, count);
+    else if (rec.fmt == MOE_W_INT4_G128) run_nt<PHASE, MOE_W_INT4_G128, XF32>(a, rec, local0, count);
+    else run_nt<PHASE, MOE_W_F32, XF32>(a, rec, local0, count);
+}
+
 template <int PHASE>
 __global__ __launch_bounds__(kThreads, 2) void ffn_kernel(FfnArgs a) {
-    constexpr int NR = PHASE == 0 ? kNrA : kNrB;
-    constexpr int CB = PHASE == 0 ? kCbA : kCbB;
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    __shared__ int lds_pair[kMaxTok];
-    __shared__ float lds_wt[kMaxTok];
-    __shared__ int pref[kMaxExperts];
-    __shared__ int wave_total[2];
     __shared__ SlotRec recs[kMaxExperts];
+    __shared__ int pref_cost[kMaxExperts];
+    __shared__ int pref_item[kMaxExperts];
+    __shared__ int wave_tot[4];
     const int T = uni(*a.T);
-    const int rows = PHASE == 0 ? a.I : a.H;
-    const int cols = PHASE == 0 ? a.H : a.I;
-    const int rows_per_item = PHASE == 0 ? kRowsA : kRowsB;
-    const int tiles = (rows + rows_per_item - 1) / rows_per_item;
-    price_slots<PHASE>(a, T, tiles, cols, recs, pref, wave_total);
-    const long C = pref[kMaxExperts - 1];
-    const long begin = item_at(pref, T, tiles, C * blockIdx.x / gridDim.x);
-    const long end = item_at(pref, T, tiles, C * (blockIdx.x + 1) / gridDim.x);
-    if (begin >= end) return;
-    const void* src = PHASE == 0 ? a.x : static_cast<const void*>(a.hbuf);
-    const int src_dtype = PHASE == 0 ? a.x_dtype : MOE_DT_F32;
-    const int by_token = PHASE == 0 ? a.k : 0;
-
-    long item = begin;
-    int cnt = 0;
-    Unit u = make_unit<PHASE>(recs, a.x_dtype, item, 0, tiles, cols, cnt);
-    Rows<NR> R = unit_rows<PHASE, NR>(u, rows, cols);
-    Block<NR, CB> pre;
-    load_block<NR, CB>(R, 0, pre);
-    stage_rows(u.fmt, u.split, src, src_dtype, by_token, a.perm + u.first + u.t0, u.ct, cols, lds, a.w,
-               lds_pair, lds_wt);
-    __syncthreads();
-    while (true) {
-        // the unit after u: the next pass of this item, else the next item
-        long nitem = item;
-        int nt0 = u.t0 + u.ct;
-        if (nt0 >= cnt) { nitem = item + 1; nt0 = 0; }
-        const bool has_next = nitem < end;
-        int ncnt = cnt;
-        const Unit nu = has_next ? make_unit<PHASE>(recs, a.x_dtype, nitem, nt0, tiles, cols, ncnt) : u;
-        const Rows<NR> NRws = unit_rows<PHASE, NR>(nu, rows, cols);
-        if (u.fmt == MOE_W_BF16) {
-            if (u.split) run_unit_mt<PHASE, MOE_W_BF16, true, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
-            else run_unit_mt<PHASE, MOE_W_BF16, false, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
-        } else if (u.fmt == MOE_W_INT4_G128) {
-            if (u.split) run_unit_mt<PHASE, MOE_W_INT4_G128, true, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
-            else run_unit_mt<PHASE, MOE_W_INT4_G128, false, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
-        } else {
-            run_unit_mt<PHASE, MOE_W_F32, false, NR, CB>(a, u, R, NRws, has_next, rows, cols, lds, lds_pair, lds_wt, pre);
-        }
-        if (!has_next) break;
-        if (nu.slot != u.slot || nu.t0 != u.t0) {
-            __syncthreads();
-            stage_rows(nu.fmt, nu.split, src, src_dtype, by_token, a.perm + nu.first + nu.t0, nu.ct, cols, lds,
-                       a.w, lds_pair, lds_wt);
-            __syncthreads();
-        }
-        u = nu;
-        R = NRws;
-        item = nitem;
-        cnt = ncnt;
+    price_slots<PHASE>(a, T, recs, pref_cost, pref_item, wave_tot);
+    const int Wn = gridDim.x * kWaves;
+    const int gw = blockIdx.x * kWaves + threadIdx.x / kWave;
+    const long C = pref_cost[kMaxExperts - 1];
+    const int begin = item_at(pref_cost, pref_item, T, C * gw / Wn);
+    const int end = item_at(pref_cost, pref_item, T, C * (gw + 1) / Wn);
+    int it = begin;
+    while (it < end) {   // one run per (expert, pass) touched by the range
+        const int slot = count_le(pref_item, it);   // < T because it < total items
+        const int i_lo = slot > 0 ? pref_item[slot - 1] : 0;
+        SlotRec rec = recs[slot];
+        const int ipp = uni(rec.ipp);
+        const int pass = (it - i_lo) / ipp;
+        const int local0 = it - i_lo - pass * ipp;
+        const int count = uni(min(end, i_lo + (pass + 1) * ipp) - it);
+        const int pt = pass_tokens(rec.fmt);
+        rec.first += pass * pt;
+        rec.cnt = min(pt, rec.cnt - pass * pt);
+        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) run_fmt<PHASE, true>(a, rec, local0, count);
+        else run_fmt<PHASE, false>(a, rec, local0, count);
+        it += count;
     }
 }
 
@@ -676,10 +591,10 @@ hipError_t launch_expert_ffn(const FfnArgs& in, void* ws, hipStream_t s) {
     a.hbuf = reinterpret_cast<float*>(p);
     a.dbuf = reinterpret_cast<float*>(p + align256(pairs * a.I * sizeof(float)));
     const int G = 2 * device_cus();
-    ffn_kernel<0><<<G, kThreads, kLdsBytes, s>>>(a);
+    ffn_kernel<0><<<G, kThreads, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    ffn_kernel<1><<<G, kThreads, kLdsBytes, s>>>(a);
+    ffn_kernel<1><<<G, kThreads, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 cg((a.H / 4 + 255) / 256, a.B);

@@ -26,6 +26,17 @@ hipError_t launch_handle_publish(moe_expert_handle* table, int e, moe_expert_han
                                  hipStream_t s);
 hipError_t launch_quantize_int4(const uint16_t* w, int rows, int cols, uint8_t* q,
                                 uint16_t* scales, hipStream_t s);
+hipError_t launch_pack_weights(int fmt, const void* src, const uint16_t* src_scales, int rows, int cols,
+                               void* dst, uint16_t* dst_scales, hipStream_t s);
+
+// Bytes of one weight row of `cols` input columns in format fmt.
+__host__ __device__ inline int weight_row_bytes(int fmt, int cols) {
+    return fmt == MOE_W_F32 ? cols * 4 : (fmt == MOE_W_BF16 ? cols * 2 : cols / 2);
+}
+// Input columns covered by one 64-byte tile row segment.
+__host__ __device__ inline int tile_cols(int fmt) {
+    return fmt == MOE_W_F32 ? 16 : (fmt == MOE_W_BF16 ? 32 : 128);
+}
 
 struct FfnArgs {
     const moe_expert_handle* table;

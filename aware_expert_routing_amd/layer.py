@@ -18,6 +18,7 @@ from . import _lib as L
 
 @dataclass
 class ExpertTensors:
+    """One expert version in the packed layout the FFN reads (moe_pack_weights)."""
     fmt: int
     gate: torch.Tensor
     up: torch.Tensor
@@ -25,6 +26,15 @@ class ExpertTensors:
     s_gate: torch.Tensor | None = None
     s_up: torch.Tensor | None = None
     s_down: torch.Tensor | None = None
+
+    @classmethod
+    def pack(cls, fmt: int, gate, up, down, s_gate=None, s_up=None, s_down=None, stream=None):
+        """Pack row-major device matrices ([I,H], [I,H], [H,I]; INT4: the
+        quantiser's bytes and scales) into a new version."""
+        g, sg = L.pack_weights(fmt, gate, s_gate, stream=stream)
+        u, su = L.pack_weights(fmt, up, s_up, stream=stream)
+        d, sd = L.pack_weights(fmt, down, s_down, stream=stream)
+        return cls(fmt, g, u, d, sg, su, sd)
 
     def handle(self) -> L.ExpertHandle:
         h = L.ExpertHandle()

@@ -81,7 +81,9 @@ def main():
     def to_dev(a):
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
 
-    g0, u0, d0 = to_dev(gate), to_dev(up), to_dev(down)
+    # pack each matrix into the tiled layout once; further layer copies are clones
+    g0, u0, d0 = (moe.pack_weights(moe.MOE_W_BF16, to_dev(m).view(N * m.shape[1], m.shape[2]))[0]
+                  .view(N, m.shape[1], m.shape[2]) for m in (gate, up, down))
     wr_dev = torch.from_numpy(w_r).to(dev)
     layers = []
     for c in range(args.copies):

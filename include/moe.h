@@ -56,13 +56,18 @@ enum {
  * active version's pointer and quantisation parameters, so a version change
  * rewrites the handle and never the kernel arguments].
  *
- * Layouts (row-major, [out, in]):
- *   w_gate, w_up : [I, H]     w_down : [H, I]
- *   MOE_W_F32/BF16: one element per weight.
- *   MOE_W_INT4_G128: bytes [rows, cols/2]; each byte holds two weights, the
- *     even column in the low nibble, as the unsigned nibble q + 8 with
- *     q in [-8, 7]; weight = q * s where s (fp16 bits) is scales[row, col/128].
- *     s_gate, s_up : [I, H/128]   s_down : [H, I/128]; NULL for other formats.
+ * Matrices are [out, in]: w_gate, w_up : [I, H]   w_down : [H, I].  The
+ * forward path reads them in the PACKED layout written by moe_pack_weights
+ * (16-byte aligned), not row-major:
+ *   Each matrix of `rows` x `cols` is cut into tiles of 16 rows x 64 bytes
+ *   of row data (16 fp32, 32 bf16 or 128 INT4 columns); tile (rb, s) -- row
+ *   block rb, column segment s, S = row_bytes / 64 -- is the 1 KB block at
+ *   (rb * S + s) KB.  Inside a tile, the 16 bytes at 16 * l hold row m =
+ *   l % 16, bytes [16 * (l / 16), + 16) of that row's segment (the operand
+ *   order of the 16x16 MFMA instructions).  fp32/bf16 bytes are unchanged;
+ *   INT4 bytes are re-ordered within each 4-byte word (see moe_pack_weights).
+ *   MOE_W_INT4_G128 scales (fp16 bits, 8-byte aligned) are packed as
+ *   [rows/16][cols/128][16]; s_gate, s_up, s_down are NULL for other formats.
  * The table is an array of N handles in device memory.  64 bytes each.
  */
 typedef struct moe_expert_handle {
@@ -157,9 +162,10 @@ size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
  *            256-byte aligned (scratch: the SwiGLU activations and the
  *            weighted down projections; no contents need be preset; calls
  *            that share a workspace must be ordered, e.g. on one stream).
- * Accumulation is fp32.  H and I must be multiples of 8 (of 128 when any
- * expert is INT4).  Each active expert's weights are streamed from HBM once
- * per pass of up to 8 of its tokens (up to 2 for INT4 experts).
+ * Accumulation is fp32.  H and I must be multiples of 32, and of 128 for
+ * INT4 experts (an expert whose format does not fit contributes nothing to
+ * y; its pairs' outputs are undefined).  Each active expert's weights are
+ * streamed from HBM once per pass of up to 32 of its tokens (16 for INT4).
  */
 int moe_expert_ffn(const moe_expert_handle *table, int N, int H, int I, const void *x,
                    int x_dtype, const int32_t *idx, const float *w, const int32_t *offsets,
@@ -184,7 +190,8 @@ int moe_handle_publish(moe_expert_handle *table, int e, const moe_expert_handle 
  * each expert keeps a high- and a low-precision version; section 3.4:
  * versions are prepacked in kernel-ready form].
  *   w      : [rows, cols] bf16 bits, cols a multiple of 128
- *   q      : [rows, cols/2] packed nibbles (layout as in moe_expert_handle)
+ *   q      : [rows, cols/2] row-major nibbles: each byte holds two weights,
+ *            the even column in the low nibble, as the unsigned value q + 8
  *   scales : [rows, cols/128] fp16 bits
  *   Per row and group of 128 columns: s = fp16(absmax / 7) (fp32 quotient,
  *   rounded to nearest even), q = clamp(rint(w / s), -8, 7) with the fp32
@@ -192,6 +199,23 @@ int moe_handle_publish(moe_expert_handle *table, int e, const moe_expert_handle 
  */
 int moe_quantize_int4_g128(const uint16_t *w, int rows, int cols, uint8_t *q, uint16_t *scales,
                            void *stream);
+
+/*
+ * Pack one row-major matrix into the layout the expert FFN reads [DYN
+ * section 3.4: expert versions are prepacked once into kernel-ready form].
+ *   fmt        : MOE_W_F32, MOE_W_BF16 or MOE_W_INT4_G128
+ *   src        : [rows, cols] row-major (INT4: the bytes moe_quantize_int4_g128
+ *                writes); dst receives the same number of bytes, packed.
+ *   src_scales : INT4 only: [rows, cols/128] fp16 bits; dst_scales receives
+ *                them as [rows/16][cols/128][16].  NULL for other formats.
+ *   rows must be a multiple of 16 and cols of 16 (fp32), 32 (bf16) or 128
+ *   (INT4); src and dst 16-byte aligned and not overlapping.
+ *   INT4: in each 4-byte word of a packed tile (8 consecutive columns c..c+7
+ *   of one row), nibble i holds column c + 2i and nibble i + 4 holds column
+ *   c + 2i + 1 (i = 0..3), each as the unsigned value q + 8.
+ */
+int moe_pack_weights(int fmt, const void *src, const uint16_t *src_scales, int rows, int cols,
+                     void *dst, uint16_t *dst_scales, void *stream);
 
 /*
  * Hotness estimate [DYN section 2.5: per-expert counters c folded into a

@@ -28,13 +28,14 @@ def build_layer(N, k, H, I, seed, fmt="bf16", int4_experts=(), with_router=True)
     oracle's quantiser for the host copy.
     """
     host, dev = [], []
+    rowmajor_int4 = {}   # the quantiser's row-major output per INT4 expert, before packing
     int4 = set(int4_experts)
     for e in range(N):
         if fmt == "f32":
             g, u, d = synth.expert_weights_f32(seed, e, H, I)
             host.append(dict(fmt=oracle.FMT_F32, gate=g, up=u, down=d))
-            dev.append(moe.ExpertTensors(moe.MOE_W_F32, torch.from_numpy(g).to(DEV),
-                                         torch.from_numpy(u).to(DEV), torch.from_numpy(d).to(DEV)))
+            dev.append(moe.ExpertTensors.pack(moe.MOE_W_F32, torch.from_numpy(g).to(DEV),
+                                              torch.from_numpy(u).to(DEV), torch.from_numpy(d).to(DEV)))
             continue
         mats = synth.expert_weights_bf16(seed, e, H, I)
         if e in int4:
@@ -46,15 +47,17 @@ def build_layer(N, k, H, I, seed, fmt="bf16", int4_experts=(), with_router=True)
                 gq, gs = moe.quantize_int4_g128(bf16_dev(m))
                 qd[name], qd["s_" + name] = gq, gs
             host.append(he)
-            dev.append(moe.ExpertTensors(moe.MOE_W_INT4_G128, qd["gate"], qd["up"], qd["down"],
-                                         qd["s_gate"], qd["s_up"], qd["s_down"]))
+            rowmajor_int4[e] = qd
+            dev.append(moe.ExpertTensors.pack(moe.MOE_W_INT4_G128, qd["gate"], qd["up"], qd["down"],
+                                              qd["s_gate"], qd["s_up"], qd["s_down"]))
         else:
             host.append(dict(fmt=oracle.FMT_BF16, gate=mats[0], up=mats[1], down=mats[2]))
-            dev.append(moe.ExpertTensors(moe.MOE_W_BF16, *[bf16_dev(m) for m in mats]))
+            dev.append(moe.ExpertTensors.pack(moe.MOE_W_BF16, *[bf16_dev(m) for m in mats]))
     w_r = None
     if with_router:
         w_r = torch.from_numpy(synth.router_weight(seed, N, H)).to(DEV)
     layer = moe.MoELayer(H, I, N, k, w_r, dev, DEV)
+    layer.rowmajor_int4 = rowmajor_int4
     torch.cuda.synchronize()
     return layer, host
 

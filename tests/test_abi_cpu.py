@@ -111,3 +111,35 @@ def test_publish_rejects_bad_handles():
 def test_quantizer_rejects_ragged_groups():
     lib = moe.lib()
     assert lib.moe_quantize_int4_g128(FAKE, 4, 200, FAKE, FAKE, None) == -1
+
+
+def test_pack_rejects_bad_arguments():
+    lib = moe.lib()
+    dst = ctypes.c_void_p(1 << 30)
+    ok = (moe.MOE_W_BF16, FAKE, None, 32, 64, dst, None, None)
+
+    def call(**kw):
+        names = ["fmt", "src", "src_scales", "rows", "cols", "dst", "dst_scales", "stream"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return lib.moe_pack_weights(*[args[n] for n in names])
+
+    assert call(fmt=7) == -1
+    assert call(src=None) == -1
+    assert call(rows=24) == -1                                   # rows % 16
+    assert call(cols=48) == -1                                   # bf16 needs cols % 32
+    assert call(fmt=moe.MOE_W_F32, cols=40) == -1                # fp32 needs cols % 16
+    assert call(fmt=moe.MOE_W_INT4_G128, cols=128) == -1         # INT4 needs scale pointers
+    assert call(fmt=moe.MOE_W_INT4_G128, cols=64, src_scales=FAKE, dst_scales=dst) == -1
+    assert call(src=ctypes.c_void_p((1 << 20) + 8)) == -1       # 16-byte alignment
+    assert call(dst=ctypes.c_void_p((1 << 20) + 1024)) == -1    # overlapping buffers
+    assert "overlap" in lib.moe_last_error().decode()
+
+
+def test_publish_rejects_misaligned_weights():
+    lib = moe.lib()
+    h = moe.ExpertHandle()
+    h.fmt = moe.MOE_W_BF16
+    h.w_gate, h.w_up, h.w_down = 1 << 20, (1 << 20) + 8, 1 << 21
+    assert lib.moe_handle_publish(FAKE, 0, ctypes.byref(h), None) == -1
+    assert "aligned" in lib.moe_last_error().decode()

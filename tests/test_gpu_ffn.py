@@ -52,10 +52,10 @@ def test_tiny_fp32_layer_vanilla_and_oea():
 
 
 @pytest.mark.parametrize("N,k,H,I,B,mode,k0,p", [
-    (16, 4, 520, 136, 24, "topk", 0, 1.0),    # ragged chunks and ragged row tiles
-    (16, 4, 520, 136, 24, "oea", 2, 0.7),
-    (8, 4, 256, 128, 64, "topk", 0, 1.0),     # > 16 tokens per expert: several passes
-    (32, 16, 384, 264, 9, "topk", 0, 1.0),    # k = 16
+    (16, 4, 544, 224, 24, "topk", 0, 1.0),    # odd tile counts; last phase-B item ragged
+    (16, 4, 544, 224, 24, "oea", 2, 0.7),
+    (8, 4, 256, 128, 64, "topk", 0, 1.0),     # > 32 tokens per expert: several passes
+    (32, 16, 384, 288, 9, "topk", 0, 1.0),    # k = 16
     (128, 8, 256, 128, 128, "oea", 3, 1.0),   # B = 128
     (128, 8, 256, 128, 1, "oea", 3, 1.0),     # B = 1
     (12, 3, 1024, 640, 5, "oea", 1, 0.9),
@@ -81,12 +81,12 @@ def test_int4_and_mixed_experts(int4):
     N, k, H, I, B = 16, 4, 512, 256, 32
     which = range(N) if int4 == "all" else range(4, N)       # 4 hot bf16, 12 cold INT4
     layer, host = build_layer(N, k, H, I, 4, fmt="bf16", int4_experts=which, with_router=False)
-    # the GPU's INT4 bytes equal the oracle's, bit for bit
+    # the GPU quantiser's INT4 bytes equal the oracle's, bit for bit (before packing)
     for e in which:
+        q = layer.rowmajor_int4[e]
         for name in ("gate", "up", "down"):
-            assert np.array_equal(getattr(layer.experts[e], name).cpu().numpy(), host[e][name])
-            assert np.array_equal(getattr(layer.experts[e], "s_" + name).cpu().numpy().view(np.uint16),
-                                  host[e]["s_" + name])
+            assert np.array_equal(q[name].cpu().numpy(), host[e][name])
+            assert np.array_equal(q["s_" + name].cpu().numpy().view(np.uint16), host[e]["s_" + name])
     x, xd = _x(4, B, H, "bf16")
     logits = (synth.logits(4, B, N, 1.0) + synth.zipf_bias(N, 1.1)[None, :]).astype(np.float32)
     _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL["int4"])
@@ -106,8 +106,8 @@ def test_publish_switches_version():
     for name, m in zip(("gate", "up", "down"), mats):
         qd[name], qd["s_" + name] = moe.quantize_int4_g128(bf16_dev(m))
         he[name], he["s_" + name] = oracle.quantize_int4(m)
-    layer.publish(e, moe.ExpertTensors(moe.MOE_W_INT4_G128, qd["gate"], qd["up"], qd["down"],
-                                       qd["s_gate"], qd["s_up"], qd["s_down"]))
+    layer.publish(e, moe.ExpertTensors.pack(moe.MOE_W_INT4_G128, qd["gate"], qd["up"], qd["down"],
+                                            qd["s_gate"], qd["s_up"], qd["s_down"]))
     host = list(host)
     host[e] = he
     _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL["int4"])
