@@ -546,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_kernel(FfnArgs a) {
 }
 
 // y[i, o] = sum over filled slots s of token i (slot order) of dbuf[i*k+s, o].
-__global__ __launch_bounds__(256) void combine_kernel(FfnArgs a) {
+__global__ __launch_bounds__(64) void combine_kernel(FfnArgs a) {
     const int i = blockIdx.y;
     const int o = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (o >= a.H) return;
@@ -597,8 +597,8 @@ hipError_t launch_expert_ffn(const FfnArgs& in, void* ws, hipStream_t s) {
     ffn_kernel<1><<<G, kThreads, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 cg((a.H / 4 + 255) / 256, a.B);
-    combine_kernel<<<cg, 256, 0, s>>>(a);
+    dim3 cg((a.H / 4 + 63) / 64, a.B);
+    combine_kernel<<<cg, 64, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -47,7 +47,53 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["oea", "topk"], default=None,
                     help="time only this routing (for profiler runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 20 plain device copies of MIB MiB (the "
+                         "reference kernel for scaling HBM byte counters) and exit")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_ffn_traffic_qwen30b_b16_oea3.txt")
+FFN_SOURCES = [os.path.join(ROOT, "aware_expert_routing_amd", "csrc", f) for f in ("ffn.hip", "pack.hip")]
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in FFN_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per expert-FFN call from the committed counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("sources_sha256") != sources_sha256():
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_call"]) + float(kv["write_bytes_per_call"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda:0", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4,
+                                           "copies": 20}}), flush=True)
 
 
 def main():
@@ -56,6 +102,9 @@ def main():
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -201,7 +250,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(head["ffn_gbps"] / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic() if (args.config == "qwen30b" and B == 16 and args.k0 == 3) else None,
         },
         "linearity": sweep,
         "cpu_baseline": cpu,
