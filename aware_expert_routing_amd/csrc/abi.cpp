@@ -110,6 +110,7 @@ MOE_API int moe_expert_ffn(const moe_expert_handle* table, int N, int H, int I, 
     if (H > 16384 || I > 16384) return fail(MOE_EUNSUPPORTED, "H and I above 16384 are not supported");
     if (ws_bytes < moe::ffn_workspace_bytes(B, k, H, I)) return fail(MOE_EINVAL, "workspace too small");
     if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+    if (reinterpret_cast<uintptr_t>(table) % 16 != 0) return fail(MOE_EINVAL, "handle table must be 16-byte aligned");
     moe::FfnArgs a{};
     a.table = table;
     a.N = N; a.H = H; a.I = I; a.B = B; a.k = k;

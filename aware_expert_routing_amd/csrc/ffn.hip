@@ -25,7 +25,7 @@
 //   * phase A: work items are (active expert, 2 row blocks of 16 rows of I);
 //     the wave streams the gate and up tiles of those rows over all of H and
 //     ends with h = silu(g) * u for every token of the expert.
-//   * phase B: items are (active expert, 4 row blocks of H) over all of I;
+//   * phase B: items are (active expert, 2 row blocks of H) over all of I;
 //     the result is scaled by the pair's routing weight.
 //   * combine: y[i] = sum over token i's filled slots, in slot order.
 // Items belong to single waves (no barriers, no LDS staging): each wave owns
@@ -47,7 +47,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTileBytes = 1024;
 constexpr int kRbA = 2;   // row blocks per phase-A item
-constexpr int kRbB = 4;   // row blocks per phase-B item
+constexpr int kRbB = 2;   // row blocks per phase-B item
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -128,7 +128,7 @@ constexpr int stages() {
     constexpr int acc = nmat * rb * NT * 4;
     // register budget for the ring (the rest holds addresses and temporaries;
     // the split and INT4 paths need more temporaries)
-    constexpr int budget = (FMT == MOE_W_INT4_G128 || XF32) ? 150 : 200;
+    constexpr int budget = PHASE == 1 ? 90 : ((FMT == MOE_W_INT4_G128 || XF32) ? 150 : 200);
     constexpr int fit = (budget - acc) / per;
     if constexpr (FMT == MOE_W_INT4_G128 && (XF32 || NT > 1)) return 1;   // avoids spills
     return fit >= 8 ? 8 : (fit >= 4 ? 4 : (fit >= 2 ? 2 : 1));
@@ -262,7 +262,8 @@ __host__ __device__ __forceinline__ int pass_tokens(int fmt) { return fmt == MOE
 __host__ __device__ __forceinline__ int col_tiles_for(int cnt) { return cnt <= 16 ? 1 : 2; }
 
 template <int PHASE>
-__device__ __forceinline__ void price_slots(const FfnArgs& a, int T, SlotRec* recs, int* pref_cost,
+__device__ __forceinline__ void price_slots(const FfnArgs& a, int T, const moe_expert_handle* table,
+                                            const int* active, const int* offsets, SlotRec* recs, int* pref_cost,
                                             int* pref_item, int* wave_tot) {
     const int s = threadIdx.x;
     const int lane = s & (kWave - 1);
@@ -270,16 +271,16 @@ __device__ __forceinline__ void price_slots(const FfnArgs& a, int T, SlotRec* re
     const int rb = PHASE == 0 ? kRbA : kRbB;
     int cost = 0, items = 0;
     if (s < T) {
-        const int e = a.active[s];
-        const moe_expert_handle& h = a.table[e];
+        const int e = active[s];
+        const moe_expert_handle& h = table[e];
         SlotRec r;
         r.fmt = h.fmt;
         r.m0 = static_cast<const char*>(PHASE == 0 ? h.w_gate : h.w_down);
         r.m1 = PHASE == 0 ? static_cast<const char*>(h.w_up) : nullptr;
         r.s0 = reinterpret_cast<const char*>(PHASE == 0 ? h.s_gate : h.s_down);
         r.s1 = PHASE == 0 ? reinterpret_cast<const char*>(h.s_up) : nullptr;
-        r.first = a.offsets[e];
-        r.cnt = a.offsets[e + 1] - r.first;
+        r.first = offsets[e];
+        r.cnt = offsets[e + 1] - r.first;
         r.ipp = (rows / 16 + rb - 1) / rb;
         recs[s] = r;
         const bool fits = (r.fmt == MOE_W_F32 || r.fmt == MOE_W_BF16 || r.fmt == MOE_W_INT4_G128) &&
@@ -514,14 +515,30 @@ __device__ __forceinline__ void run_fmt(const FfnArgs& a, const SlotRec& rec, in
     else run_nt<PHASE, MOE_W_F32, XF32>(a, rec, local0, count);
 }
 
+// Resident waves per SIMD: phase A keeps 2 (deep rings of gate+up tiles),
+// phase B 3 (more waves with smaller items).
 template <int PHASE>
-__global__ __launch_bounds__(kThreads, 2) void ffn_kernel(FfnArgs a) {
+constexpr int waves_per_simd() { return PHASE == 0 ? 2 : 3; }
+
+template <int PHASE>
+__global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(FfnArgs a) {
     __shared__ SlotRec recs[kMaxExperts];
     __shared__ int pref_cost[kMaxExperts];
     __shared__ int pref_item[kMaxExperts];
     __shared__ int wave_tot[4];
+    __shared__ u32x4 table_l[kMaxExperts * 4];   // the N handles, 4 x 16 bytes each
+    __shared__ int active_l[kMaxExperts];
+    __shared__ int offsets_l[kMaxExperts + 1];
+    // Stage the handle table, active list and offsets with independent loads
+    // (one round trip) instead of following active -> handle per slot.
     const int T = uni(*a.T);
-    price_slots<PHASE>(a, T, recs, pref_cost, pref_item, wave_tot);
+    for (int c = threadIdx.x; c < a.N * 4; c += kThreads)
+        table_l[c] = load_a(reinterpret_cast<const char*>(a.table) + 16 * c);
+    if (threadIdx.x < a.N) active_l[threadIdx.x] = a.active[threadIdx.x];
+    if (threadIdx.x <= a.N) offsets_l[threadIdx.x] = a.offsets[threadIdx.x];
+    __syncthreads();
+    price_slots<PHASE>(a, T, reinterpret_cast<const moe_expert_handle*>(table_l), active_l, offsets_l, recs,
+                       pref_cost, pref_item, wave_tot);
     const int Wn = gridDim.x * kWaves;
     const int gw = blockIdx.x * kWaves + threadIdx.x / kWave;
     const long C = pref_cost[kMaxExperts - 1];
@@ -590,11 +607,11 @@ hipError_t launch_expert_ffn(const FfnArgs& in, void* ws, hipStream_t s) {
     char* p = static_cast<char*>(ws);
     a.hbuf = reinterpret_cast<float*>(p);
     a.dbuf = reinterpret_cast<float*>(p + align256(pairs * a.I * sizeof(float)));
-    const int G = 2 * device_cus();
-    ffn_kernel<0><<<G, kThreads, 0, s>>>(a);
+    const int cus = device_cus();
+    ffn_kernel<0><<<waves_per_simd<0>() * cus, kThreads, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    ffn_kernel<1><<<G, kThreads, 0, s>>>(a);
+    ffn_kernel<1><<<waves_per_simd<1>() * cus, kThreads, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 cg((a.H / 4 + 63) / 64, a.B);

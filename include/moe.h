@@ -152,7 +152,8 @@ size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
  *   For every active expert e and each routed pair (token i, slot s):
  *     g = W_gate,e x_i, u = W_up,e x_i, a = silu(g) * u, d = W_down,e a,
  *     y_i = sum over token i's filled slots of w[i, s] * d.
- *   table  : [N] moe_expert_handle (device); each expert's format may differ
+ *   table  : [N] moe_expert_handle (device, 16-byte aligned); each expert's
+ *            format may differ
  *   x      : [B, H] (x_dtype); with bf16/INT4 experts an fp32 activation a
  *            enters the products as hi = bf16(a) plus lo = bf16(a - hi)
  *            (about 16 significant bits); bf16 inputs are used exactly
