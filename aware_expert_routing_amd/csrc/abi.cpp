@@ -92,6 +92,24 @@ MOE_API int moe_dispatch(const int32_t* idx, int B, int N, int k, int32_t* cnt, 
                       "moe_dispatch");
 }
 
+MOE_API int moe_route_dispatch(const float* logits, int B, int N, int k, int mode, int k0, float p, int renorm,
+                               int32_t* idx, float* w, int32_t* n_base, uint32_t* sbase_mask, int32_t* cnt,
+                               int32_t* offsets, int32_t* perm, int32_t* active, int32_t* T, void* stream) {
+    if (!logits || !idx || !w || !cnt || !offsets || !perm || !active || !T) return fail(MOE_EINVAL, "null pointer");
+    int st = check_sizes(B, N, k);
+    if (st) return st;
+    if (mode != MOE_ROUTE_TOPK && mode != MOE_ROUTE_OEA) return fail(MOE_EINVAL, "bad routing mode");
+    if (mode == MOE_ROUTE_OEA) {
+        if (k0 < 1 || k0 > k) return fail(MOE_EINVAL, "k0 must be in [1, k]");
+        if (!(p > 0.0f)) return fail(MOE_EINVAL, "p must be > 0 (p >= 1 disables top-p)");
+    }
+    return hip_status(moe::launch_route_dispatch(logits, B, N, k, k0, p, mode == MOE_ROUTE_OEA, renorm, idx, w,
+                                                 mode == MOE_ROUTE_OEA ? n_base : nullptr,
+                                                 mode == MOE_ROUTE_OEA ? sbase_mask : nullptr, cnt, offsets, perm,
+                                                 active, T, as_stream(stream)),
+                      "moe_route_dispatch");
+}
+
 MOE_API size_t moe_ffn_workspace_bytes(int B, int k, int H, int I) {
     if (B < 1 || k < 1 || H < 1 || I < 1) return 0;
     return moe::ffn_workspace_bytes(B, k, H, I);

@@ -52,22 +52,19 @@ __device__ __forceinline__ float route_exp(float x) {
     return q * __int_as_float((ni + 127) << 23);
 }
 
-// Rank order is (logit descending, expert index ascending).  A candidate is
-// encoded as a 64-bit key whose unsigned order is that rank order: the high
-// word maps the logit's bits to an order-preserving unsigned value (-0 is
-// folded to +0 first, so equal logits compare equal as floats do), the low
-// word is ~index.  Key 0 means "no candidate".
-__device__ __forceinline__ uint64_t rank_key(float l, int j) {
+// Rank order is (logit descending, expert index ascending).  A lane holds its
+// two candidates as 32-bit order keys: the logit's bits mapped to an
+// order-preserving unsigned value (-0 is folded to +0 first, so equal logits
+// compare equal as floats do); key 0 means "no candidate" (no finite or
+// infinite logit maps to 0).  The index tie-break is taken separately: among
+// the lanes holding the maximum key the lowest lane wins, and inside a lane
+// expert 2l comes before 2l+1.
+__device__ __forceinline__ uint32_t order_key(float l) {
     const uint32_t b = __float_as_uint(l == 0.0f ? 0.0f : l);
-    const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(j));
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-__device__ __forceinline__ float key_logit(uint64_t key) {
-    const uint32_t o = static_cast<uint32_t>(key >> 32);
+__device__ __forceinline__ float key_logit(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
-}
-__device__ __forceinline__ int key_index(uint64_t key) {
-    return static_cast<int>(~static_cast<uint32_t>(key));
 }
 
 // DPP cross-lane moves (all 64 lanes active).  Row masks select which rows of
@@ -77,28 +74,18 @@ __device__ __forceinline__ uint32_t dpp32(uint32_t old, uint32_t v) {
     return static_cast<uint32_t>(
         __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROWS, 0xF, false));
 }
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint64_t dpp64(uint64_t old, uint64_t v) {
-    const uint32_t lo = dpp32<CTRL, ROWS>(static_cast<uint32_t>(old), static_cast<uint32_t>(v));
-    const uint32_t hi = dpp32<CTRL, ROWS>(static_cast<uint32_t>(old >> 32), static_cast<uint32_t>(v >> 32));
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// Wavefront maximum of a key; returned uniform (read from lane 63).
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-    v = umax64(v, dpp64<kQuadXor1, 0xF>(v, v));
-    v = umax64(v, dpp64<kQuadXor2, 0xF>(v, v));
-    v = umax64(v, dpp64<kHalfMirror, 0xF>(v, v));
-    v = umax64(v, dpp64<kMirror, 0xF>(v, v));
-    v = umax64(v, dpp64<kRowBcast15, 0xA>(v, v));   // rows 1, 3 take rows 0, 2
-    v = umax64(v, dpp64<kRowBcast31, 0xC>(v, v));   // rows 2, 3 take row 1
-    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
-    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
-    return (static_cast<uint64_t>(hi) << 32) | lo;
+// Wavefront maximum of a 32-bit key; returned uniform (read from lane 63).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp32<kQuadXor1, 0xF>(v, v));
+    v = max(v, dpp32<kQuadXor2, 0xF>(v, v));
+    v = max(v, dpp32<kHalfMirror, 0xF>(v, v));
+    v = max(v, dpp32<kMirror, 0xF>(v, v));
+    v = max(v, dpp32<kRowBcast15, 0xA>(v, v));   // rows 1, 3 take rows 0, 2
+    v = max(v, dpp32<kRowBcast31, 0xC>(v, v));   // rows 2, 3 take row 1
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
 // Normaliser Z from the lane sums of experts (2l, 2l+1).  The DPP steps pair
@@ -121,20 +108,27 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // Select up to `count` of the token's experts in rank order from the lane's
 // two candidate keys (0 = unavailable); a selected key is cleared by its
 // owner.  Results are uniform.  Stops early when nothing is left.
-__device__ __forceinline__ int select_ranked(uint64_t& key0, uint64_t& key1, int count,
-                                             float (&selv)[kMaxTopK], int (&selj)[kMaxTopK]) {
+__device__ __forceinline__ int select_ranked(uint32_t& o0, uint32_t& o1, int count, float (&selv)[kMaxTopK],
+                                             int (&selj)[kMaxTopK]) {
+    const int lane = threadIdx.x & (kWave - 1);
     int got = 0;
 #pragma unroll
     for (int r = 0; r < kMaxTopK; ++r) {
         selv[r] = 0.0f;
         selj[r] = -1;
         if (r < count && got == r) {   // wave-uniform
-            const uint64_t best = wave_max_key(umax64(key0, key1));
-            if (best != 0) {
-                selv[r] = key_logit(best);
-                selj[r] = key_index(best);
-                if (key0 == best) key0 = 0;
-                if (key1 == best) key1 = 0;
+            const uint32_t m = wave_max_u32(max(o0, o1));
+            if (m != 0) {
+                const uint64_t holders = __ballot(o0 == m || o1 == m);
+                const int L = __ffsll(static_cast<unsigned long long>(holders)) - 1;
+                const uint32_t oL = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(o0), L));
+                const int j = 2 * L + (oL == m ? 0 : 1);
+                selv[r] = key_logit(m);
+                selj[r] = j;
+                if (lane == L) {
+                    if (j & 1) o1 = 0;
+                    else o0 = 0;
+                }
                 got = r + 1;
             }
         }
@@ -155,7 +149,8 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // expert -1 and weight 0.
 __device__ __forceinline__ void write_token(int lane, int i, int k, int kept, float m, bool renorm,
                                             float Z, const float (&selv)[kMaxTopK],
-                                            const int (&selj)[kMaxTopK], int32_t* idx, float* w) {
+                                            const int (&selj)[kMaxTopK], int32_t* idx, float* w,
+                                            int32_t* idx_copy) {
     float my_l = 0.0f;
     int my_j = -1;
 #pragma unroll
@@ -166,20 +161,105 @@ __device__ __forceinline__ void write_token(int lane, int i, int k, int kept, fl
     const double denom = renorm ? wave_sum_f64(ev) : static_cast<double>(Z);
     if (lane < k) {
         idx[i * k + lane] = mine ? my_j : -1;
+        if (idx_copy != nullptr) idx_copy[i * k + lane] = mine ? my_j : -1;
         w[i * k + lane] = mine ? static_cast<float>(ev / denom) : 0.0f;
     }
 }
 
-template <bool kOea>
-__global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ logits, int B,
-                                                     int N, int k, int k0, float p, int renorm,
-                                                     int32_t* __restrict__ idx,
-                                                     float* __restrict__ w,
-                                                     int32_t* __restrict__ n_base,
-                                                     uint32_t* __restrict__ mask_out,
-                                                     int32_t* __restrict__ T_out) {
+// Dispatch of one workgroup: histogram, exclusive scan, (expert, token)-
+// ordered permutation and the active list.  A token's position inside its
+// expert's bucket is the number of lower-numbered tokens routed to the same
+// expert, read off a per-expert token bitmask, so the result needs no
+// ordering of atomics.  `idx` may live in LDS or in global memory.
+__device__ __forceinline__ void dispatch_block(const int32_t* idx, int B, int N, int k, int32_t* cnt,
+                                               int32_t* offsets, int32_t* perm, int32_t* active,
+                                               int32_t* T_out) {
+    __shared__ int cnt_s[kMaxExperts];
+    __shared__ int off_s[kMaxExperts + 1];
+    __shared__ unsigned long long tokmask[kMaxExperts][kMaxBatch / 64];
+    const int tid = threadIdx.x;
+    const int pairs = B * k;
+    for (int e = tid; e < kMaxExperts; e += blockDim.x) {
+        cnt_s[e] = 0;
+        tokmask[e][0] = 0ull;
+        tokmask[e][1] = 0ull;
+    }
+    __syncthreads();
+    for (int q = tid; q < pairs; q += blockDim.x) {
+        const int e = idx[q];
+        if (e >= 0 && e < N) {
+            const int t = q / k;
+            atomicAdd(&cnt_s[e], 1);
+            atomicOr(&tokmask[e][t >> 6], 1ull << (t & 63));
+        }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        const int lane = tid;
+        const int c0 = 2 * lane < N ? cnt_s[2 * lane] : 0;
+        const int c1 = 2 * lane + 1 < N ? cnt_s[2 * lane + 1] : 0;
+        int sum = c0 + c1;
+        int act = (c0 > 0) + (c1 > 0);
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {   // inclusive scans over lanes
+            const int os = __shfl_up(sum, off, kWave);
+            const int oa = __shfl_up(act, off, kWave);
+            if (lane >= off) { sum += os; act += oa; }
+        }
+        const int excl = sum - (c0 + c1);
+        const int aexcl = act - ((c0 > 0) + (c1 > 0));
+        if (2 * lane < N) {
+            off_s[2 * lane] = excl;
+            offsets[2 * lane] = excl;
+            cnt[2 * lane] = c0;
+        }
+        if (2 * lane + 1 < N) {
+            off_s[2 * lane + 1] = excl + c0;
+            offsets[2 * lane + 1] = excl + c0;
+            cnt[2 * lane + 1] = c1;
+        }
+        const int total = __shfl(sum, kWave - 1, kWave);
+        const int tact = __shfl(act, kWave - 1, kWave);
+        if (lane == 0) {
+            off_s[N] = total;
+            offsets[N] = total;
+            *T_out = tact;
+        }
+        int pos = aexcl;   // active list, ascending, then -1
+        if (2 * lane < N && c0 > 0) active[pos++] = 2 * lane;
+        if (2 * lane + 1 < N && c1 > 0) active[pos++] = 2 * lane + 1;
+        for (int e = tact + lane; e < N; e += kWave) active[e] = -1;
+    }
+    __syncthreads();
+    const int total = off_s[N];
+    for (int q = tid; q < pairs; q += blockDim.x) {
+        const int e = idx[q];
+        if (e >= 0 && e < N) {
+            const int t = q / k;
+            const unsigned long long lo = tokmask[e][0], hi = tokmask[e][1];
+            const int below = t < 64 ? __popcll(lo & ((1ull << t) - 1ull))
+                                     : __popcll(lo) + __popcll(hi & ((1ull << (t - 64)) - 1ull));
+            perm[off_s[e] + below] = q;
+        }
+        if (q >= total) perm[q] = -1;
+    }
+}
+
+// Routing of a batch by one workgroup of min(B, 16) wavefronts, one token per
+// wavefront at a time.  kOea: OEA Phase 1, the union S_base (LDS bitmask
+// built with integer OR, independent of the order tokens finish), Phase 2;
+// otherwise vanilla top-k.  kDispatch: the same workgroup then dispatches
+// the routed pairs from LDS (one launch instead of two).
+template <bool kOea, bool kDispatch>
+__global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ logits, int B, int N, int k,
+                                                     int k0, float p, int renorm, int32_t* __restrict__ idx,
+                                                     float* __restrict__ w, int32_t* __restrict__ n_base,
+                                                     uint32_t* __restrict__ mask_out, int32_t* __restrict__ T_out,
+                                                     int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ active) {
     __shared__ uint32_t sbase[kMaxExperts / 32];
     __shared__ int sbase_count;
+    __shared__ int32_t idx_l[kDispatch ? kMaxBatch * kMaxTopK : 1];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nwaves = blockDim.x / kWave;
@@ -189,14 +269,15 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
 
     float selv[kMaxTopK];
     int selj[kMaxTopK];
+    int32_t* idx_copy = kDispatch ? idx_l : nullptr;
 
     // Vanilla top-k, or OEA Phase 1.
     for (int i = wave; i < B; i += nwaves) {
         const bool v0 = e0 < N, v1 = e1 < N;
         const float l0 = v0 ? logits[i * N + e0] : kNegInf;
         const float l1 = v1 ? logits[i * N + e1] : kNegInf;
-        uint64_t key0 = v0 ? rank_key(l0, e0) : 0ull;
-        uint64_t key1 = v1 ? rank_key(l1, e1) : 0ull;
+        uint32_t key0 = v0 ? order_key(l0) : 0u;
+        uint32_t key1 = v1 ? order_key(l1) : 0u;
         const bool need_z = kOea ? (p < 1.0f) : (renorm == 0);
         const int first = kOea ? k0 : k;
         const int kept = select_ranked(key0, key1, first, selv, selj);
@@ -208,7 +289,7 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
             Z = wave_tree_sum(s0 + s1);
         }
         if (!kOea) {
-            write_token(lane, i, k, kept, m, renorm != 0, Z, selv, selj, idx, w);
+            write_token(lane, i, k, kept, m, renorm != 0, Z, selv, selj, idx, w, idx_copy);
         } else {
             int n = kept;
             if (p < 1.0f) {
@@ -230,117 +311,43 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
             }
         }
     }
-    if (!kOea) return;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int c = 0;
-        for (int wd = 0; wd < kMaxExperts / 32; ++wd) c += __popc(sbase[wd]);
-        sbase_count = c;
-        if (T_out != nullptr) *T_out = c;
-    }
-    if (mask_out != nullptr && threadIdx.x < (N + 31) / 32) mask_out[threadIdx.x] = sbase[threadIdx.x];
-    __syncthreads();
-    const int T = sbase_count;
-    const int keep = T < k ? T : k;
+    if constexpr (kOea) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int c = 0;
+            for (int wd = 0; wd < kMaxExperts / 32; ++wd) c += __popc(sbase[wd]);
+            sbase_count = c;
+            if (T_out != nullptr && !kDispatch) *T_out = c;   // with dispatch, T comes from there
+        }
+        if (mask_out != nullptr && threadIdx.x < (N + 31) / 32) mask_out[threadIdx.x] = sbase[threadIdx.x];
+        __syncthreads();
+        const int T = sbase_count;
+        const int keep = T < k ? T : k;
 
-    // Phase 2: token i keeps the first min(k, T) members of S_base in its rank
-    // order -- its baseline first (the top-ranked experts are in S_base), then
-    // lower-ranked experts that other tokens already activated.
-    for (int i = wave; i < B; i += nwaves) {
-        const bool a0 = e0 < N && ((sbase[e0 >> 5] >> (e0 & 31)) & 1u);
-        const bool a1 = e1 < N && ((sbase[e1 >> 5] >> (e1 & 31)) & 1u);
-        uint64_t key0 = a0 ? rank_key(logits[i * N + e0], e0) : 0ull;
-        uint64_t key1 = a1 ? rank_key(logits[i * N + e1], e1) : 0ull;
-        const int kept = select_ranked(key0, key1, keep, selv, selj);
-        write_token(lane, i, k, kept, selv[0], true, 0.0f, selv, selj, idx, w);
+        // Phase 2: token i keeps the first min(k, T) members of S_base in its
+        // rank order -- its baseline first (the top-ranked experts are in
+        // S_base), then lower-ranked experts that other tokens already activated.
+        for (int i = wave; i < B; i += nwaves) {
+            const bool a0 = e0 < N && ((sbase[e0 >> 5] >> (e0 & 31)) & 1u);
+            const bool a1 = e1 < N && ((sbase[e1 >> 5] >> (e1 & 31)) & 1u);
+            uint32_t key0 = a0 ? order_key(logits[i * N + e0]) : 0u;
+            uint32_t key1 = a1 ? order_key(logits[i * N + e1]) : 0u;
+            const int kept = select_ranked(key0, key1, keep, selv, selj);
+            write_token(lane, i, k, kept, selv[0], true, 0.0f, selv, selj, idx, w, idx_copy);
+        }
+    }
+    if constexpr (kDispatch) {
+        __syncthreads();
+        dispatch_block(idx_l, B, N, k, cnt, offsets, perm, active, T_out);
     }
 }
 
-// Dispatch: histogram, exclusive scan, (expert, token)-ordered permutation and
-// the active list.  A token's position inside its expert's bucket is the
-// number of lower-numbered tokens routed to the same expert, read off a
-// per-expert token bitmask, so the result needs no ordering of atomics.
-__global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restrict__ idx, int B,
-                                                        int N, int k, int32_t* __restrict__ cnt,
-                                                        int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ perm,
-                                                        int32_t* __restrict__ active,
-                                                        int32_t* __restrict__ T_out) {
-    __shared__ int cnt_s[kMaxExperts];
-    __shared__ int off_s[kMaxExperts + 1];
-    __shared__ unsigned long long tokmask[kMaxExperts][kMaxBatch / 64];
-    const int tid = threadIdx.x;
-    const int pairs = B * k;
-    for (int e = tid; e < kMaxExperts; e += blockDim.x) {
-        cnt_s[e] = 0;
-        tokmask[e][0] = 0ull;
-        tokmask[e][1] = 0ull;
-    }
-    __syncthreads();
-    for (int q = tid; q < pairs; q += blockDim.x) {
-        int e = idx[q];
-        if (e >= 0 && e < N) {
-            int t = q / k;
-            atomicAdd(&cnt_s[e], 1);
-            atomicOr(&tokmask[e][t >> 6], 1ull << (t & 63));
-        }
-    }
-    __syncthreads();
-    if (tid < kWave) {
-        const int lane = tid;
-        const int c0 = 2 * lane < N ? cnt_s[2 * lane] : 0;
-        const int c1 = 2 * lane + 1 < N ? cnt_s[2 * lane + 1] : 0;
-        int s = c0 + c1;
-        int a = (c0 > 0) + (c1 > 0);
-        // inclusive scans over lanes
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            int os = __shfl_up(s, off, kWave);
-            int oa = __shfl_up(a, off, kWave);
-            if (lane >= off) { s += os; a += oa; }
-        }
-        const int excl = s - (c0 + c1);
-        const int aexcl = a - ((c0 > 0) + (c1 > 0));
-        if (2 * lane < N) {
-            off_s[2 * lane] = excl;
-            offsets[2 * lane] = excl;
-            cnt[2 * lane] = c0;
-        }
-        if (2 * lane + 1 < N) {
-            off_s[2 * lane + 1] = excl + c0;
-            offsets[2 * lane + 1] = excl + c0;
-            cnt[2 * lane + 1] = c1;
-        }
-        const int total = __shfl(s, kWave - 1, kWave);
-        const int tact = __shfl(a, kWave - 1, kWave);
-        if (lane == 0) {
-            off_s[N] = total;
-            offsets[N] = total;
-            *T_out = tact;
-        }
-        // active list, ascending, then -1
-        int pos = aexcl;
-        if (2 * lane < N && c0 > 0) active[pos++] = 2 * lane;
-        if (2 * lane + 1 < N && c1 > 0) active[pos++] = 2 * lane + 1;
-        for (int e = tact + lane; e < N; e += kWave) active[e] = -1;
-    }
-    __syncthreads();
-    const int total = off_s[N];
-    for (int q = tid; q < pairs; q += blockDim.x) {
-        int e = idx[q];
-        if (e >= 0 && e < N) {
-            int t = q / k;
-            unsigned long long lo = tokmask[e][0], hi = tokmask[e][1];
-            int below;
-            if (t < 64) {
-                below = __popcll(lo & ((1ull << t) - 1ull));
-            } else {
-                below = __popcll(lo) + __popcll(hi & ((1ull << (t - 64)) - 1ull));
-            }
-            perm[off_s[e] + below] = q;
-        }
-        if (q >= total) perm[q] = -1;
-    }
+// Dispatch on its own (idx from global memory).
+__global__ __launch_bounds__(512) void dispatch_kernel(const int32_t* __restrict__ idx, int B, int N, int k,
+                                                       int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ perm, int32_t* __restrict__ active,
+                                                       int32_t* __restrict__ T_out) {
+    dispatch_block(idx, B, N, k, cnt, offsets, perm, active, T_out);
 }
 
 // Router logits: one workgroup per expert; its 4 waves split the hidden
@@ -455,10 +462,24 @@ hipError_t launch_route(const float* logits, int B, int N, int k, int k0, float 
                         int32_t* T, hipStream_t s) {
     const int threads = kWave * (B < 16 ? B : 16);
     if (oea)
-        route_kernel<true><<<1, threads, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, mask, T);
+        route_kernel<true, false><<<1, threads, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, mask, T,
+                                                        nullptr, nullptr, nullptr, nullptr);
     else
-        route_kernel<false><<<1, threads, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w,
-                                                  nullptr, nullptr, nullptr);
+        route_kernel<false, false><<<1, threads, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w, nullptr,
+                                                         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int k0, float p, int oea, int renorm,
+                                 int32_t* idx, float* w, int32_t* n_base, uint32_t* mask, int32_t* cnt,
+                                 int32_t* offsets, int32_t* perm, int32_t* active, int32_t* T, hipStream_t s) {
+    const int threads = kWave * (B < 16 ? B : 16);
+    if (oea)
+        route_kernel<true, true><<<1, threads, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, mask, T, cnt,
+                                                       offsets, perm, active);
+    else
+        route_kernel<false, true><<<1, threads, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w, nullptr,
+                                                        nullptr, T, cnt, offsets, perm, active);
     return hipGetLastError();
 }
 

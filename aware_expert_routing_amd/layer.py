@@ -96,13 +96,9 @@ class MoELayer:
               buf: Buffers | None = None, stream=None) -> Buffers:
         B = logits.shape[0]
         buf = buf or self.buffers(B)
-        if mode == "topk":
-            L.route_topk(logits, self.k, True, buf.route["idx"], buf.route["w"], stream)
-        elif mode == "oea":
-            L.route_oea(logits, k0, p, self.k, buf.route, stream)
-        else:
+        if mode not in ("topk", "oea"):
             raise ValueError(mode)
-        L.dispatch(buf.route["idx"], self.N, buf.disp, stream)
+        L.route_dispatch(logits, self.k, mode, k0, p, True, buf.route, buf.disp, stream)
         return buf
 
     def ffn(self, x: torch.Tensor, buf: Buffers, stream=None) -> torch.Tensor:

@@ -143,6 +143,20 @@ int moe_route_oea(const float *logits, int B, int N, int k0, float p, int k, int
 int moe_dispatch(const int32_t *idx, int B, int N, int k, int32_t *cnt, int32_t *offsets,
                  int32_t *perm, int32_t *active, int32_t *T, void *stream);
 
+/*
+ * Routing and dispatch in one launch: exactly moe_route_topk (mode
+ * MOE_ROUTE_TOPK, with `renorm`) or moe_route_oea (mode MOE_ROUTE_OEA, with
+ * k0 and p) followed by moe_dispatch on its idx, with the same outputs and
+ * the same validation ([OEA] sections 2 Q1/Q2, 3 and 4, Eq. 2).  The routed
+ * pairs stay on chip between the two steps.
+ *   n_base, sbase_mask : OEA only, may be NULL (ignored for top-k)
+ *   T                  : number of active experts (for OEA also |S_base|)
+ */
+enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_OEA = 1 };
+int moe_route_dispatch(const float *logits, int B, int N, int k, int mode, int k0, float p, int renorm,
+                       int32_t *idx, float *w, int32_t *n_base, uint32_t *sbase_mask, int32_t *cnt,
+                       int32_t *offsets, int32_t *perm, int32_t *active, int32_t *T, void *stream);
+
 /* Workspace bytes moe_expert_ffn needs for these sizes (host call). */
 size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
 

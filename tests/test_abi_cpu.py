@@ -143,3 +143,17 @@ def test_publish_rejects_misaligned_weights():
     h.w_gate, h.w_up, h.w_down = 1 << 20, (1 << 20) + 8, 1 << 21
     assert lib.moe_handle_publish(FAKE, 0, ctypes.byref(h), None) == -1
     assert "aligned" in lib.moe_last_error().decode()
+
+
+def test_route_dispatch_rejects_bad_arguments():
+    lib = moe.lib()
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("logits", FAKE), ("B", 16), ("N", 128), ("k", 8), ("mode", 1), ("k0", 3), ("p", 1.0), ("renorm", 1),
+        ("idx", FAKE), ("w", FAKE), ("n_base", None), ("mask", None), ("cnt", FAKE), ("offsets", FAKE),
+        ("perm", FAKE), ("active", FAKE), ("T", FAKE), ("stream", None))]
+    assert lib.moe_route_dispatch(*args(mode=2)) == -1
+    assert lib.moe_route_dispatch(*args(k0=9)) == -1
+    assert lib.moe_route_dispatch(*args(p=0.0)) == -1
+    assert lib.moe_route_dispatch(*args(perm=None)) == -1
+    assert lib.moe_route_dispatch(*args(B=129)) == -2
+    assert lib.moe_route_dispatch(*args(N=0)) == -1

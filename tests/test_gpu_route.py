@@ -115,6 +115,33 @@ def test_dispatch_parity(B, N, k, mode):
         assert int(d["T"].item()) == ref["T"]
 
 
+@pytest.mark.parametrize("B,N,k,mode,k0,p,kind,scale,zipf", [
+    (4, 16, 4, "topk", 0, 1.0, "normal", 1.0, 0.0), (16, 128, 8, "topk", 0, 1.0, "normal", 0.9, 0.0),
+    (128, 128, 16, "topk", 0, 1.0, "normal", 4.0, 1.1), (9, 33, 16, "topk", 0, 1.0, "tied", 1.0, 0.0),
+    (4, 16, 4, "oea", 2, 0.7, "normal", 8.0, 0.0), (16, 128, 8, "oea", 3, 1.0, "normal", 0.9, 0.0),
+    (16, 128, 8, "oea", 5, 1.0, "tied", 1.0, 0.0), (64, 128, 8, "oea", 3, 0.9, "normal", 4.0, 1.1),
+    (128, 128, 16, "oea", 7, 0.8, "normal", 6.0, 1.1), (1, 128, 8, "oea", 3, 0.7, "normal", 4.0, 0.0),
+    (3, 5, 5, "oea", 1, 0.9, "normal", 1.0, 0.0),
+])
+def test_fused_route_dispatch_parity(B, N, k, mode, k0, p, kind, scale, zipf):
+    # moe_route_dispatch = the routing call followed by moe_dispatch, in one launch
+    for seed in range(3):
+        l = _logits(kind, seed, B, N, scale, zipf)
+        route, disp = moe.route_dispatch(torch.from_numpy(l).to(DEV), k, mode, k0, p, True)
+        ref = oracle.route(l, k, oea=(mode == "oea"), k0=k0 if mode == "oea" else 0, p=p)
+        assert np.array_equal(route["idx"].cpu().numpy(), ref["idx"])
+        assert np.abs(route["w"].cpu().numpy().astype(np.float64) - ref["w"]).max() <= 1e-6
+        if mode == "oea":
+            assert np.array_equal(route["n_base"].cpu().numpy(), ref["n_base"])
+            assert np.array_equal(route["mask"].cpu().numpy().view(np.uint32), ref["mask"])
+        dref = oracle.dispatch(ref["idx"], N)
+        for key in ("cnt", "offsets", "perm", "active"):
+            assert np.array_equal(disp[key].cpu().numpy(), dref[key]), key
+        assert int(disp["T"].item()) == dref["T"]
+        if mode == "oea":
+            assert dref["T"] == ref["T"]
+
+
 def test_dispatch_with_empty_slots_and_rows():
     B, N, k = 6, 16, 4
     idx = np.array([[3, 5, -1, -1], [-1, -1, -1, -1], [15, 0, 3, -1], [7, -1, -1, -1],
