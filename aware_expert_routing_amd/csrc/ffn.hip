@@ -48,6 +48,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kTileBytes = 1024;
 constexpr int kRbA = 2;   // row blocks per phase-A item
 constexpr int kRbB = 2;   // row blocks per phase-B item
+constexpr int kXcds = 8;  // MI355X: 8 XCDs; the grid is a multiple of 8 workgroups
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -540,7 +541,17 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     price_slots<PHASE>(a, T, reinterpret_cast<const moe_expert_handle*>(table_l), active_l, offsets_l, recs,
                        pref_cost, pref_item, wave_tot);
     const int Wn = gridDim.x * kWaves;
-    const int gw = blockIdx.x * kWaves + threadIdx.x / kWave;
+    // XCD- and CU-aware numbering.  Workgroups are dealt to the 8 XCDs
+    // round-robin (blockIdx % 8) and, inside an XCD, to its CUs round-robin,
+    // so workgroup b sits on CU (b / 8) % cus_per_xcd of XCD b % 8.  The
+    // virtual order runs XCD by XCD and, inside an XCD, CU by CU: each XCD
+    // takes 1/8 of the total cost, the waves of one CU take consecutive items
+    // (usually one expert, whose activation rows they share in L1/L2), and
+    // when items are fewer than waves the idle waves spread evenly over CUs.
+    const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds, lb = blockIdx.x / kXcds;
+    constexpr int wps = waves_per_simd<PHASE>();   // workgroups per CU
+    const int slot = per_xcd % wps == 0 ? (lb % (per_xcd / wps)) * wps + lb / (per_xcd / wps) : lb;
+    const int gw = (xcd * per_xcd + slot) * kWaves + threadIdx.x / kWave;
     const long C = pref_cost[kMaxExperts - 1];
     const int begin = item_at(pref_cost, pref_item, T, C * gw / Wn);
     const int end = item_at(pref_cost, pref_item, T, C * (gw + 1) / Wn);
@@ -608,10 +619,13 @@ hipError_t launch_expert_ffn(const FfnArgs& in, void* ws, hipStream_t s) {
     a.hbuf = reinterpret_cast<float*>(p);
     a.dbuf = reinterpret_cast<float*>(p + align256(pairs * a.I * sizeof(float)));
     const int cus = device_cus();
-    ffn_kernel<0><<<waves_per_simd<0>() * cus, kThreads, 0, s>>>(a);
+    // grids are whole multiples of kXcds workgroups (the virtual numbering needs it)
+    const int g0 = (waves_per_simd<0>() * cus) / kXcds * kXcds;
+    const int g1 = (waves_per_simd<1>() * cus) / kXcds * kXcds;
+    ffn_kernel<0><<<g0 > 0 ? g0 : kXcds, kThreads, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    ffn_kernel<1><<<waves_per_simd<1>() * cus, kThreads, 0, s>>>(a);
+    ffn_kernel<1><<<g1 > 0 ? g1 : kXcds, kThreads, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 cg((a.H / 4 + 63) / 64, a.B);
