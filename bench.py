@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["oea", "topk"], default=None,
                     help="time only this routing (for profiler runs)")
+    ap.add_argument("--no-extended", action="store_true",
+                    help="skip the batch sweep, the 235B-shaped layer and the mixed INT4 layer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 20 plain device copies of MIB MiB (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -220,6 +222,14 @@ def main():
     if not args.no_sweep and args.only is None:
         sweep = forced_t_sweep(layers, xs[0], B, N, k, W_e, fixed_ffn)
 
+    extended = None
+    if not args.no_extended and args.only is None and args.config == "qwen30b":
+        extended = {"batch_sweep": batch_sweep(layers, wr_dev, N, k, H, I),
+                    "mixed_int4": mixed_int4(layers, wr_dev, N, k, H, I, gate, up, down)}
+        del layers[:]
+        torch.cuda.empty_cache()
+        extended["qwen235b"] = qwen235b_lines()
+
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
         cpu = cpu_baseline(args, N, k, H, I, B, gate, up, down, w_r, xs_bits, W_e, fixed_layer)
@@ -253,6 +263,7 @@ def main():
             "traffic": measured_traffic() if (args.config == "qwen30b" and B == 16 and args.k0 == 3) else None,
         },
         "linearity": sweep,
+        "extended": extended,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
@@ -304,6 +315,208 @@ def forced_t_sweep(layers, x, B, N, k, W_e, fixed_ffn, reps=40):
     r2 = 1.0 - float(((y - pred) ** 2).sum() / ((y - y.mean()) ** 2).sum())
     return {"fit": "us = b*T + c", "b_us_per_expert": round(float(coef[0]), 4), "c_us": round(float(coef[1]), 3),
             "r2": round(r2, 6), "points": [{"T": int(t), "ffn_us": round(u, 2), "gbps": round(g, 1)} for t, u, g in pts]}
+
+
+def _fit(T, y, extra=None):
+    """Least squares y = b*T (+ a*extra) + c; returns coefficients and R^2."""
+    import numpy as np
+    cols = [np.asarray(T, np.float64)] + ([np.asarray(extra, np.float64)] if extra is not None else [])
+    A = np.stack(cols + [np.ones(len(T))], 1)
+    y = np.asarray(y, np.float64)
+    coef, *_ = np.linalg.lstsq(A, y, rcond=None)
+    pred = A @ coef
+    r2 = 1.0 - float(((y - pred) ** 2).sum() / ((y - y.mean()) ** 2).sum())
+    return [round(float(c), 4) for c in coef], round(r2, 5)
+
+
+def _time_steps(step, n, warm=3):
+    import torch
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / n * 1e6
+
+
+def batch_sweep(layers, w_r, N, k, H, I, batches=5, steps=30):
+    """Routing + dispatch + expert FFN latency and T over B = 1..128 for
+    vanilla top-8, simplified OEA (k0 = 3, 5) and full OEA (k0 in {3, 5},
+    p in {0.5, 0.7, 0.9}), with router logits plus a Zipf(1.1) expert bias
+    and with the uniform control.  The router GEMV runs once per batch
+    outside the timed steps (the bias is added to its output); its own cost
+    is reported per B.  Fits latency = b*T + c and b*T + a*sum(cnt) + c
+    (page OEA section 4, Eq. 2) over all points of each routing family."""
+    import numpy as np
+    import torch
+
+    import aware_expert_routing_amd as moe
+    import synth
+
+    dev = layers[0].device
+    W_e = 3 * H * I * 2
+    routings = [("topk", 0, 1.0)] + [("oea", k0, p) for k0 in (3, 5) for p in (1.0, 0.5, 0.7, 0.9)]
+    points, router_us = [], {}
+    for B in (1, 2, 4, 8, 16, 32, 64, 128):
+        xs = [torch.from_numpy(synth.to_bf16_bits(synth.activations(100 + b, B, H)).view(np.int16)).to(dev)
+              .view(torch.bfloat16) for b in range(batches)]
+        base = [moe.router_logits(x, w_r) for x in xs]
+        router_us[B] = round(_time_steps(lambda i: moe.router_logits(xs[i % batches], w_r,
+                                                                         layers[0].buffers(B).logits), steps), 2)
+        for zipf in (1.1, 0.0):
+            beta = torch.from_numpy(synth.zipf_bias(N, zipf)).to(dev)
+            logits = [l + beta[None, :] for l in base]
+            for mode, k0, p in routings:
+                Ts, sc = [], []
+                for b in range(batches):
+                    buf = layers[0].buffers(B)
+                    layers[0].route(logits[b], mode, k0, p, buf)
+                    Ts.append(int(buf.disp["T"].item()))
+                    sc.append(int(buf.disp["offsets"][N].item()))
+
+                def step(i):
+                    lay = layers[i % len(layers)]
+                    buf = lay.buffers(B)
+                    lay.route(logits[i % batches], mode, k0, p, buf)
+                    lay.ffn(xs[i % batches], buf)
+                us = _time_steps(step, steps)
+                T = float(np.mean(Ts))
+                points.append(dict(B=B, routing=mode if mode == "topk" else f"oea_k0_{k0}_p{p}", zipf=zipf,
+                                   T=round(T, 2), sum_cnt=round(float(np.mean(sc)), 1), us=round(us, 2),
+                                   gbps=round(T * W_e / us / 1e3, 1)))
+    fits = {}
+    for fam in ("topk", "oea"):
+        sel = [q for q in points if q["routing"].startswith(fam)]
+        c1, r1 = _fit([q["T"] for q in sel], [q["us"] for q in sel])
+        c2, r2 = _fit([q["T"] for q in sel], [q["us"] for q in sel], [q["sum_cnt"] for q in sel])
+        fits[fam] = {"us = b*T + c": {"b": c1[0], "c": c1[1], "r2": r1},
+                     "us = b*T + a*sum_cnt + c": {"b": c2[0], "a": c2[1], "c": c2[2], "r2": r2}}
+    return {"what": "route+dispatch+expert FFN per step, logits given (router GEMV timed apart)",
+            "router_us": router_us, "fits": fits, "points": points}
+
+
+def mixed_int4(layers, w_r, N, k, H, I, gate, up, down, B=32, warm=64, hot=32, copies=8, steps=60):
+    """Qwen3-30B shape with a handle table of the `hot` hottest experts in
+    bf16 and the rest in INT4 (group 128), the hot set taken from an EMA of
+    vanilla top-8 routing counts (alpha 0.9) over `warm` Zipf-biased batches
+    (page DynaExq sections 2.5 / 3.2).  B = 32; vanilla top-8 vs OEA k0=5."""
+    import numpy as np
+    import torch
+
+    import aware_expert_routing_amd as moe
+    import synth
+
+    dev = layers[0].device
+    beta = torch.from_numpy(synth.zipf_bias(N, 1.1)).to(dev)
+    S = torch.zeros(N, device=dev)
+    lay0 = layers[0]
+    for b in range(warm):
+        x = torch.from_numpy(synth.to_bf16_bits(synth.activations(200 + b, B, H)).view(np.int16)).to(dev) \
+            .view(torch.bfloat16)
+        buf = lay0.buffers(B)
+        logits = moe.router_logits(x, w_r) + beta[None, :]
+        lay0.route(logits, "topk", 0, 1.0, buf)
+        moe.hotness_ema(S, buf.disp["cnt"], 0.9)
+    order = torch.argsort(S.cpu(), descending=True, stable=True).numpy()
+    hot_set = set(int(e) for e in order[:hot])
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    experts = []
+    for e in range(N):
+        mats = [dev_bf16(gate[e]), dev_bf16(up[e]), dev_bf16(down[e])]
+        if e in hot_set:
+            experts.append(moe.ExpertTensors.pack(moe.MOE_W_BF16, *mats))
+        else:
+            q = [moe.quantize_int4_g128(m) for m in mats]
+            experts.append(moe.ExpertTensors.pack(moe.MOE_W_INT4_G128, q[0][0], q[1][0], q[2][0],
+                                                  q[0][1], q[1][1], q[2][1]))
+    mlayers = [moe.MoELayer(H, I, N, k, w_r, experts, dev)]
+    for c in range(1, copies):
+        ex = [moe.ExpertTensors(t.fmt, t.gate.clone(), t.up.clone(), t.down.clone(),
+                                None if t.s_gate is None else t.s_gate.clone(),
+                                None if t.s_up is None else t.s_up.clone(),
+                                None if t.s_down is None else t.s_down.clone()) for t in experts]
+        mlayers.append(moe.MoELayer(H, I, N, k, w_r, ex, dev))
+    bf16_bytes = 3 * H * I * 2
+    int4_bytes = 3 * (H * I // 2 + H * I // 128 * 2)
+    xs = [torch.from_numpy(synth.to_bf16_bits(synth.activations(300 + b, B, H)).view(np.int16)).to(dev)
+          .view(torch.bfloat16) for b in range(10)]
+    logits = [moe.router_logits(x, w_r) + beta[None, :] for x in xs]
+    out = {"B": B, "hot_bf16": hot, "cold_int4": N - hot,
+           "layer_bytes": hot * bf16_bytes + (N - hot) * int4_bytes}
+    for mode, k0 in (("topk", 0), ("oea", 5)):
+        Ts, byts = [], []
+        for b in range(10):
+            buf = mlayers[0].buffers(B)
+            mlayers[0].route(logits[b], mode, k0, 1.0, buf)
+            act = buf.disp["active"].cpu().numpy()
+            T = int(buf.disp["T"].item())
+            Ts.append(T)
+            byts.append(sum(bf16_bytes if int(e) in hot_set else int4_bytes for e in act[:T]))
+
+        def step(i):
+            lay = mlayers[i % copies]
+            buf = lay.buffers(B)
+            lay.route(logits[i % 10], mode, k0, 1.0, buf)
+            lay.ffn(xs[i % 10], buf)
+        us = _time_steps(step, steps)
+        key = "top8" if mode == "topk" else "oea_k0_5"
+        out[key] = {"T": round(float(np.mean(Ts)), 2), "us": round(us, 2),
+                    "weight_bytes": round(float(np.mean(byts))),
+                    "gbps": round(float(np.mean(byts)) / us / 1e3, 1)}
+    del mlayers
+    return out
+
+
+def qwen235b_lines(copies=2, steps=30):
+    """Qwen3-235B-A22B-shaped layer (H=4096, I=1536, 37.7 MB per bf16 expert,
+    4.83 GB per layer) on one GPU; seeded N(0, 0.02) weights drawn on the
+    device.  B in {16, 32, 64}; vanilla top-8 vs OEA k0=5; router logits from
+    the layer's own router; whole-layer steps."""
+    import numpy as np
+    import torch
+
+    import aware_expert_routing_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    s = synth.SHAPES["qwen235b"]
+    N, k, H, I = s["N"], s["k"], s["H"], s["I"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(235)
+    layers = []
+    w_r = torch.randn(N, H, device=dev, generator=gen) * 0.02
+    for c in range(copies):
+        mats = []
+        for rows, cols in ((I, H), (I, H), (H, I)):
+            m = (torch.randn(N * rows, cols, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+            mats.append(moe.pack_weights(moe.MOE_W_BF16, m)[0].view(N, rows, cols))
+            del m
+        layers.append(moe.MoELayer(H, I, N, k, w_r, [moe.ExpertTensors(moe.MOE_W_BF16, mats[0][e], mats[1][e],
+                                                                       mats[2][e]) for e in range(N)], dev))
+    W_e = 3 * H * I * 2
+    out = {"H": H, "I": I, "expert_bytes": W_e, "points": []}
+    for B in (16, 32, 64):
+        xs = [torch.from_numpy(synth.to_bf16_bits(synth.activations(400 + b, B, H)).view(np.int16)).to(dev)
+              .view(torch.bfloat16) for b in range(4)]
+        for mode, k0 in (("topk", 0), ("oea", 5)):
+            Ts = []
+            for b in range(4):
+                Ts.append(int(layers[0].forward(xs[b], mode, k0, 1.0).disp["T"].item()))
+
+            def step(i):
+                layers[i % copies].forward(xs[i % 4], mode, k0, 1.0)
+            us = _time_steps(step, steps)
+            T = float(np.mean(Ts))
+            out["points"].append(dict(B=B, routing="top8" if mode == "topk" else "oea_k0_5", T=round(T, 2),
+                                      us=round(us, 2), gbps=round((T * W_e + N * H * 4) / us / 1e3, 1)))
+    del layers
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(args, N, k, H, I, B, gate, up, down, w_r, xs_bits, W_e, fixed_layer):
