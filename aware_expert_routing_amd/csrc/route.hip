@@ -350,7 +350,7 @@ __global__ __launch_bounds__(512) void dispatch_kernel(const int32_t* __restrict
     dispatch_block(idx, B, N, k, cnt, offsets, perm, active, T_out);
 }
 
-// Router logits: one workgroup per expert; its 4 waves split the hidden
+// Router logits: one workgroup per (expert, group of 16 tokens); its 4 waves split the hidden
 // dimension (lane l of wave w owns columns 8l + 512w + 2048i), and every lane
 // issues its router-weight and activation loads for a group of 16 tokens at
 // once, so the whole product costs about one memory round trip.  Partial sums
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(const XT* _
     const int col0 = 8 * lane + 512 * (tid / kWave);     // this lane's first column
     const int stride = 8 * kGemvThreads;                  // 2048 columns per sweep
     const float* wrow = w_r + static_cast<size_t>(e) * H;
-    for (int t0 = 0; t0 < B; t0 += kGemvTok) {
+    for (int t0 = blockIdx.y * kGemvTok; t0 < B; t0 += gridDim.y * kGemvTok) {
         const int nt = min(kGemvTok, B - t0);
         float acc[kGemvTok];
 #pragma unroll
@@ -448,12 +448,13 @@ __global__ void publish_kernel(moe_expert_handle* table, int e, moe_expert_handl
 
 hipError_t launch_router_logits(const void* x, int x_dtype, const float* w_r, int B, int H, int N,
                                 float* logits, hipStream_t s) {
+    const dim3 grid(N, (B + kGemvTok - 1) / kGemvTok);   // one workgroup per (expert, 16 tokens)
     if (x_dtype == MOE_DT_BF16)
-        router_logits_kernel<uint16_t><<<N, kGemvThreads, 0, s>>>(static_cast<const uint16_t*>(x), w_r,
-                                                                  B, H, N, logits);
+        router_logits_kernel<uint16_t><<<grid, kGemvThreads, 0, s>>>(static_cast<const uint16_t*>(x), w_r,
+                                                                     B, H, N, logits);
     else
-        router_logits_kernel<float><<<N, kGemvThreads, 0, s>>>(static_cast<const float*>(x), w_r, B, H,
-                                                               N, logits);
+        router_logits_kernel<float><<<grid, kGemvThreads, 0, s>>>(static_cast<const float*>(x), w_r, B, H,
+                                                                  N, logits);
     return hipGetLastError();
 }
 
