@@ -48,7 +48,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         build(force=True)
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
@@ -66,6 +66,7 @@ def _load():
     lib.orc_topp_count.argtypes = [P, ctypes.c_float, P, I, ctypes.c_float]
     lib.orc_topp_count.restype = I
     lib.orc_route.argtypes = [P, I, I, I, I, ctypes.c_float, I, I, P, P, P, P, P]
+    lib.orc_route_general.argtypes = [P, I, I, I, I, ctypes.c_float, I, I, I, I, P, P, P, P, P]
     lib.orc_dispatch.argtypes = [P, I, I, I, P, P, P, P, P]
     lib.orc_router_logits.argtypes = [P, P, I, I, I, P]
     lib.orc_expert_ffn.argtypes = [P, I, I, P, P, P, I, I, P]
@@ -128,9 +129,13 @@ def topp_count(logits_row, p: float) -> int:
                                       ctypes.c_float(p)))
 
 
-def route(logits, k: int, *, oea: bool, k0: int = 0, p: float = 1.0, renorm: bool = True):
+def route(logits, k: int, *, oea: bool, k0: int = 0, p: float = 1.0, renorm: bool = True,
+          pruned: bool = False, max_p: int | None = None, n_valid: int | None = None):
     """Vanilla top-k (oea=False) or OEA (oea=True) routing of fp32 logits [B, N].
 
+    pruned=True keeps only OEA's Phase 1 baseline; max_p limits Phase 2 to
+    the token's ranks up to max_p (default N); k is the slot count (the
+    page's k_max for OEA); tokens i >= n_valid (default B) are padding.
     Returns a dict: idx [B,k] int32 (-1 pad), w [B,k] float64 (0 pad),
     n_base [B] int32, mask [ceil(N/32)] uint32, T int.
     """
@@ -141,8 +146,10 @@ def route(logits, k: int, *, oea: bool, k0: int = 0, p: float = 1.0, renorm: boo
     n_base = np.zeros(B, np.int32)
     mask = np.zeros((N + 31) // 32, np.uint32)
     T = np.zeros(1, np.int32)
-    _load().orc_route(_ptr(l), B, N, k, k0, ctypes.c_float(p), int(oea), int(renorm),
-                      _ptr(idx), _ptr(w), _ptr(n_base), _ptr(mask), _ptr(T))
+    mode = 0 if not oea else (2 if pruned else 1)
+    _load().orc_route_general(_ptr(l), B, N, k, k0, ctypes.c_float(p), mode, N if max_p is None else int(max_p),
+                              int(renorm), B if n_valid is None else int(n_valid),
+                              _ptr(idx), _ptr(w), _ptr(n_base), _ptr(mask), _ptr(T))
     return {"idx": idx, "w": w, "n_base": n_base, "mask": mask, "T": int(T[0])}
 
 

@@ -202,16 +202,31 @@ int orc_topp_count(const float *e, float Z, const int32_t *order, int N, float p
 /* the union of the kept sets), T[0] = number of experts in that union.       */
 /* Weights are the plain softmax definition in double with libm exp.           */
 /* ------------------------------------------------------------------------- */
-void orc_route(const float *logits, int B, int N, int k, int k0, float p, int oea, int renorm,
-               int32_t *idx, double *w, int32_t *n_base, uint32_t *mask, int32_t *T)
+/*
+ * General routing.  mode 0 = vanilla top-k, 1 = OEA, 2 = pruned (OEA Phase 1
+ * only: each token keeps just its baseline).  For OEA, Phase 2 scans the
+ * token's ranks n_i+1 .. max_p (page OEA section 5: "maxP", the deepest rank
+ * that may be piggybacked; max_p = N is the simplified router) and keeps an
+ * expert only if it is in S_base, until the token holds k experts (k plays
+ * the page's k_max).  Tokens i >= n_valid are padding: they route to no
+ * expert and add nothing to S_base (page OEA section 7: padding tokens must
+ * not inflate T).
+ */
+void orc_route_general(const float *logits, int B, int N, int k, int k0, float p, int mode, int max_p,
+                       int renorm, int n_valid, int32_t *idx, double *w, int32_t *n_base, uint32_t *mask,
+                       int32_t *T)
 {
     int32_t order[128];
     float e[128];
     unsigned char in_base[128];
     memset(in_base, 0, sizeof in_base);
+    const int oea = mode != 0;
+    if (n_valid > B) n_valid = B;
+    if (n_valid < 0) n_valid = 0;
 
-    /* Phase 1 for every token (for vanilla: the k kept experts). */
+    /* Phase 1 for every real token (for vanilla: the k kept experts). */
     for (int i = 0; i < B; ++i) {
+        if (i >= n_valid) { n_base[i] = 0; continue; }
         const float *l = logits + (size_t)i * N;
         orc_rank(l, N, order);
         int n;
@@ -233,27 +248,31 @@ void orc_route(const float *logits, int B, int N, int k, int k0, float p, int oe
         if (in_base[j]) { mask[j / 32] |= 1u << (j % 32); ++count; }
     *T = count;
 
-    /* Phase 2 (OEA) or the vanilla selection, then the weights. */
+    /* Phase 2 (OEA), the baseline alone (pruned) or the vanilla selection,
+       then the weights. */
     for (int i = 0; i < B; ++i) {
-        const float *l = logits + (size_t)i * N;
-        orc_rank(l, N, order);
         int32_t sel[128];
         int ns = 0;
-        if (oea) {
-            int n = n_base[i];
-            for (int r = 0; r < n; ++r) sel[ns++] = order[r];
-            /* literal scan: ranks n+1..N, keep an expert only if in S_base */
-            for (int r = n; r < N && ns < k; ++r)
-                if (in_base[order[r]]) sel[ns++] = order[r];
-        } else {
-            for (int r = 0; r < k; ++r) sel[ns++] = order[r];
+        const float *l = logits + (size_t)i * N;
+        if (i < n_valid) {
+            orc_rank(l, N, order);
+            if (oea) {
+                int n = n_base[i];
+                for (int r = 0; r < n; ++r) sel[ns++] = order[r];
+                if (mode == 1) {
+                    /* literal scan: ranks n+1..max_p, keep an expert only if in S_base */
+                    for (int r = n; r < max_p && r < N && ns < k; ++r)
+                        if (in_base[order[r]]) sel[ns++] = order[r];
+                }
+            } else {
+                for (int r = 0; r < k; ++r) sel[ns++] = order[r];
+            }
         }
-        /* plain softmax in double */
-        double m = (double)l[order[0]];
+        double m = ns > 0 ? (double)l[order[0]] : 0.0;
         double denom = 0.0;
         if (oea || renorm) {
             for (int s = 0; s < ns; ++s) denom += exp((double)l[sel[s]] - m);
-        } else {
+        } else if (ns > 0) {
             for (int j = 0; j < N; ++j) denom += exp((double)l[j] - m);
         }
         for (int s = 0; s < k; ++s) {
@@ -266,6 +285,13 @@ void orc_route(const float *logits, int B, int N, int k, int k0, float p, int oe
             }
         }
     }
+}
+
+/* Vanilla (oea = 0) or simplified-form OEA (oea = 1, max_p = N), all tokens real. */
+void orc_route(const float *logits, int B, int N, int k, int k0, float p, int oea, int renorm,
+               int32_t *idx, double *w, int32_t *n_base, uint32_t *mask, int32_t *T)
+{
+    orc_route_general(logits, B, N, k, k0, p, oea ? 1 : 0, N, renorm, B, idx, w, n_base, mask, T);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -442,3 +442,71 @@ def test_hotness_ema_closed_form():
     for _ in range(12):
         S = oracle.hotness_ema(S, c, 0.9)
     np.testing.assert_allclose(S, c * (1 - 0.9 ** 12), rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# OEA variants: pruned (Phase 1 only), maxP, k_max and the padding mask
+# (page "Opportunistic Expert Activation (OEA) - L2", sections 5 and 7)
+# --------------------------------------------------------------------------
+def _restricted_topk(l, allowed, kk):
+    """The first kk experts of `allowed` in rank order (logit desc, index asc)."""
+    order = sorted(range(len(l)), key=lambda j: (-float(l[j]), j))
+    return [j for j in order if j in allowed][:kk]
+
+
+@pytest.mark.parametrize("B,N,kmax,k0,p,max_p,scale", [
+    (16, 128, 8, 3, 1.0, 128, 0.9), (16, 128, 8, 3, 1.0, 8, 0.9), (16, 128, 10, 3, 0.7, 40, 4.0),
+    (32, 64, 12, 5, 0.5, 20, 2.0), (8, 16, 4, 2, 0.9, 3, 1.0), (5, 33, 16, 4, 1.0, 33, 8.0),
+])
+def test_general_oea_matches_restricted_topk_definition(B, N, kmax, k0, p, max_p, scale):
+    # Phase 2 limited to ranks <= max_p with k_max slots equals the top
+    # min(k_max, |S_base cap top-max_p|) of S_base within the token's top-max_p,
+    # computed here with Python's sort (an independent formulation)
+    for seed in range(4):
+        l = synth.logits(seed, B, N, scale)
+        r = oracle.route(l, kmax, oea=True, k0=k0, p=p, max_p=max_p)
+        base = set(np.flatnonzero(np.unpackbits(r["mask"].view(np.uint8), bitorder="little")[:N]))
+        for i in range(B):
+            order = sorted(range(N), key=lambda j: (-float(l[i, j]), j))
+            allowed = base & set(order[:max_p])
+            want = _restricted_topk(l[i], allowed, kmax)
+            got = [int(j) for j in r["idx"][i] if j >= 0]
+            assert got == want
+            assert got[:r["n_base"][i]] == order[:r["n_base"][i]]
+            assert abs(r["w"][i].sum() - 1.0) < 1e-12
+
+
+def test_max_p_equal_n_is_the_simplified_router():
+    l = synth.logits(3, 16, 128, 0.9)
+    a = oracle.route(l, 8, oea=True, k0=3, p=1.0)
+    b = oracle.route(l, 8, oea=True, k0=3, p=1.0, max_p=128)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["w"], b["w"])
+
+
+@pytest.mark.parametrize("k0,p", [(3, 1.0), (5, 0.5), (2, 0.9)])
+def test_pruned_keeps_the_baseline_and_the_same_union(k0, p):
+    for seed in range(4):
+        l = synth.logits(seed, 16, 128, 4.0)
+        pr = oracle.route(l, 8, oea=True, k0=k0, p=p, pruned=True)
+        full = oracle.route(l, 8, oea=True, k0=k0, p=p)
+        assert pr["T"] == full["T"] and np.array_equal(pr["mask"], full["mask"])
+        assert np.array_equal(pr["n_base"], full["n_base"])
+        for i in range(16):
+            n = pr["n_base"][i]
+            assert np.array_equal(pr["idx"][i, :n], full["idx"][i, :n])
+            assert np.all(pr["idx"][i, n:] == -1)
+        # pruning equals OEA whose Phase 2 may scan no rank past the baseline (max_p = k0, p >= 1)
+        if p >= 1.0:
+            cut = oracle.route(l, 8, oea=True, k0=k0, p=p, max_p=k0)
+            assert np.array_equal(cut["idx"], pr["idx"])
+
+
+@pytest.mark.parametrize("oea,pruned", [(False, False), (True, False), (True, True)])
+def test_padding_tokens_route_nowhere_and_leave_the_rest_unchanged(oea, pruned):
+    B, N, k, nv = 16, 128, 8, 11
+    l = synth.logits(5, B, N, 2.0)
+    full = oracle.route(l, k, oea=oea, k0=3, p=0.8, pruned=pruned, n_valid=nv)
+    alone = oracle.route(l[:nv], k, oea=oea, k0=3, p=0.8, pruned=pruned)
+    assert np.array_equal(full["idx"][:nv], alone["idx"]) and np.array_equal(full["w"][:nv], alone["w"])
+    assert np.all(full["idx"][nv:] == -1) and np.all(full["w"][nv:] == 0.0)
+    assert full["T"] == alone["T"]
