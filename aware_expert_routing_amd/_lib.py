@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
-MOE_ROUTE_TOPK, MOE_ROUTE_OEA = 0, 1
+MOE_ROUTE_TOPK, MOE_ROUTE_OEA, MOE_ROUTE_PRUNED = 0, 1, 2
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_W_F32, MOE_W_BF16, MOE_W_INT4_G128 = 0, 1, 2
 
@@ -47,7 +47,8 @@ _SIGNATURES = [
     ("moe_route_topk", [_P, _I, _I, _I, _I, _P, _P, _P], _I),
     ("moe_route_oea", [_P, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P], _I),
     ("moe_dispatch", [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
-    ("moe_route_dispatch", [_P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
+    ("moe_route_dispatch", [_P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+     _I),
     ("moe_ffn_workspace_bytes", [_I, _I, _I, _I], _S),
     ("moe_expert_ffn", [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _S, _P], _I),
     ("moe_handle_publish", [_P, _I, ctypes.POINTER(ExpertHandle), _P], _I),
@@ -161,8 +162,12 @@ def dispatch(idx, N: int, out=None, stream=None):
 
 
 def route_dispatch(logits, k: int, mode: str, k0: int = 0, p: float = 1.0, renorm: bool = True,
-                   route=None, disp=None, stream=None):
-    """Routing ("topk" or "oea") and dispatch in one launch.  Returns (route, disp) dicts."""
+                   route=None, disp=None, stream=None, max_p: int | None = None, n_valid=None):
+    """Routing ("topk", "oea" or "pruned") and dispatch in one launch.
+
+    max_p: OEA Phase 2 rank limit (default N); n_valid: optional device int32
+    tensor [1] with the number of real tokens.  Returns (route, disp) dicts.
+    """
     B, N = logits.shape
     dev = logits.device
     i32 = dict(device=dev, dtype=torch.int32)
@@ -172,11 +177,12 @@ def route_dispatch(logits, k: int, mode: str, k0: int = 0, p: float = 1.0, renor
     if disp is None:
         disp = dict(cnt=torch.empty(N, **i32), offsets=torch.empty(N + 1, **i32), perm=torch.empty(B * k, **i32),
                     active=torch.empty(N, **i32), T=torch.empty(1, **i32))
-    m = {"topk": MOE_ROUTE_TOPK, "oea": MOE_ROUTE_OEA}[mode]
+    m = {"topk": MOE_ROUTE_TOPK, "oea": MOE_ROUTE_OEA, "pruned": MOE_ROUTE_PRUNED}[mode]
     _check("moe_route_dispatch", lib().moe_route_dispatch(
-        _ptr(logits), B, N, k, m, int(k0), float(p), int(bool(renorm)), _ptr(route["idx"]), _ptr(route["w"]),
-        _ptr(route.get("n_base")), _ptr(route.get("mask")), _ptr(disp["cnt"]), _ptr(disp["offsets"]),
-        _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]), _stream(stream)))
+        _ptr(logits), B, N, k, m, int(k0), float(p), N if max_p is None else int(max_p), int(bool(renorm)),
+        _ptr(n_valid), _ptr(route["idx"]), _ptr(route["w"]), _ptr(route.get("n_base")), _ptr(route.get("mask")),
+        _ptr(disp["cnt"]), _ptr(disp["offsets"]), _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]),
+        _stream(stream)))
     return route, disp
 
 

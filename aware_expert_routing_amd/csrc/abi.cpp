@@ -92,21 +92,25 @@ MOE_API int moe_dispatch(const int32_t* idx, int B, int N, int k, int32_t* cnt, 
                       "moe_dispatch");
 }
 
-MOE_API int moe_route_dispatch(const float* logits, int B, int N, int k, int mode, int k0, float p, int renorm,
-                               int32_t* idx, float* w, int32_t* n_base, uint32_t* sbase_mask, int32_t* cnt,
-                               int32_t* offsets, int32_t* perm, int32_t* active, int32_t* T, void* stream) {
+MOE_API int moe_route_dispatch(const float* logits, int B, int N, int k, int mode, int k0, float p, int max_p,
+                               int renorm, const int32_t* n_valid, int32_t* idx, float* w, int32_t* n_base,
+                               uint32_t* sbase_mask, int32_t* cnt, int32_t* offsets, int32_t* perm,
+                               int32_t* active, int32_t* T, void* stream) {
     if (!logits || !idx || !w || !cnt || !offsets || !perm || !active || !T) return fail(MOE_EINVAL, "null pointer");
     int st = check_sizes(B, N, k);
     if (st) return st;
-    if (mode != MOE_ROUTE_TOPK && mode != MOE_ROUTE_OEA) return fail(MOE_EINVAL, "bad routing mode");
-    if (mode == MOE_ROUTE_OEA) {
+    if (mode != MOE_ROUTE_TOPK && mode != MOE_ROUTE_OEA && mode != MOE_ROUTE_PRUNED)
+        return fail(MOE_EINVAL, "bad routing mode");
+    if (mode != MOE_ROUTE_TOPK) {
         if (k0 < 1 || k0 > k) return fail(MOE_EINVAL, "k0 must be in [1, k]");
         if (!(p > 0.0f)) return fail(MOE_EINVAL, "p must be > 0 (p >= 1 disables top-p)");
+        if (mode == MOE_ROUTE_OEA && (max_p < k0 || max_p > N)) return fail(MOE_EINVAL, "max_p must be in [k0, N]");
     }
-    return hip_status(moe::launch_route_dispatch(logits, B, N, k, k0, p, mode == MOE_ROUTE_OEA, renorm, idx, w,
-                                                 mode == MOE_ROUTE_OEA ? n_base : nullptr,
-                                                 mode == MOE_ROUTE_OEA ? sbase_mask : nullptr, cnt, offsets, perm,
-                                                 active, T, as_stream(stream)),
+    const bool oea_like = mode != MOE_ROUTE_TOPK;
+    return hip_status(moe::launch_route_dispatch(logits, B, N, k, mode, k0, p, mode == MOE_ROUTE_OEA ? max_p : N,
+                                                 renorm, n_valid, idx, w, oea_like ? n_base : nullptr,
+                                                 oea_like ? sbase_mask : nullptr, cnt, offsets, perm, active, T,
+                                                 as_stream(stream)),
                       "moe_route_dispatch");
 }
 

@@ -250,16 +250,49 @@ __device__ __forceinline__ void dispatch_block(const int32_t* idx, int B, int N,
 // built with integer OR, independent of the order tokens finish), Phase 2;
 // otherwise vanilla top-k.  kDispatch: the same workgroup then dispatches
 // the routed pairs from LDS (one launch instead of two).
+__device__ __forceinline__ void write_empty(int lane, int i, int k, int32_t* idx, float* w, int32_t* idx_copy) {
+    if (lane < k) {
+        idx[i * k + lane] = -1;
+        w[i * k + lane] = 0.0f;
+        if (idx_copy != nullptr) idx_copy[i * k + lane] = -1;
+    }
+}
+
+// Key and index of the token's kth-ranked expert (kth >= 1; fewer candidates:
+// the last one), by kth wavefront selections over copies of the keys.
+__device__ __forceinline__ void kth_ranked(uint32_t o0, uint32_t o1, int kth, uint32_t& th, int& jth) {
+    th = 0;
+    jth = -1;
+    for (int r = 0; r < kth; ++r) {   // uniform trip count
+        const uint32_t m = wave_max_u32(max(o0, o1));
+        if (m == 0) break;
+        const uint64_t holders = __ballot(o0 == m || o1 == m);
+        const int L = __ffsll(static_cast<unsigned long long>(holders)) - 1;
+        const uint32_t oL = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(o0), L));
+        const int j = 2 * L + (oL == m ? 0 : 1);
+        if ((threadIdx.x & (kWave - 1)) == L) {
+            if (j & 1) o1 = 0;
+            else o0 = 0;
+        }
+        th = m;
+        jth = j;
+    }
+}
+
 template <bool kOea, bool kDispatch>
 __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ logits, int B, int N, int k,
                                                      int k0, float p, int renorm, int32_t* __restrict__ idx,
                                                      float* __restrict__ w, int32_t* __restrict__ n_base,
                                                      uint32_t* __restrict__ mask_out, int32_t* __restrict__ T_out,
                                                      int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ perm, int32_t* __restrict__ active) {
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ active,
+                                                     int pruned, int max_p, const int32_t* __restrict__ n_valid) {
     __shared__ uint32_t sbase[kMaxExperts / 32];
     __shared__ int sbase_count;
+    __shared__ int n_l[kMaxBatch];
     __shared__ int32_t idx_l[kDispatch ? kMaxBatch * kMaxTopK : 1];
+    // tokens at or past n_valid are padding: no experts, nothing added to S_base
+    const int B_real = n_valid != nullptr ? min(max(*n_valid, 0), B) : B;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nwaves = blockDim.x / kWave;
@@ -273,6 +306,14 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
 
     // Vanilla top-k, or OEA Phase 1.
     for (int i = wave; i < B; i += nwaves) {
+        if (i >= B_real) {
+            if (!kOea) write_empty(lane, i, k, idx, w, idx_copy);
+            else if (lane == 0) {
+                n_l[i] = 0;
+                if (n_base != nullptr) n_base[i] = 0;
+            }
+            continue;
+        }
         const bool v0 = e0 < N, v1 = e1 < N;
         const float l0 = v0 ? logits[i * N + e0] : kNegInf;
         const float l1 = v1 ? logits[i * N + e1] : kNegInf;
@@ -304,7 +345,10 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
                     }
                 }
             }
-            if (lane == 0 && n_base != nullptr) n_base[i] = n;
+            if (lane == 0) {
+                n_l[i] = n;
+                if (n_base != nullptr) n_base[i] = n;
+            }
 #pragma unroll
             for (int r = 0; r < kMaxTopK; ++r) {
                 if (r < n && lane == r) atomicOr(&sbase[selj[r] >> 5], 1u << (selj[r] & 31));
@@ -326,13 +370,29 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
 
         // Phase 2: token i keeps the first min(k, T) members of S_base in its
         // rank order -- its baseline first (the top-ranked experts are in
-        // S_base), then lower-ranked experts that other tokens already activated.
+        // S_base), then lower-ranked experts that other tokens already
+        // activated.  With max_p < N only the token's top-max_p ranks may be
+        // taken; pruned keeps the baseline alone (its n_i experts).
         for (int i = wave; i < B; i += nwaves) {
-            const bool a0 = e0 < N && ((sbase[e0 >> 5] >> (e0 & 31)) & 1u);
-            const bool a1 = e1 < N && ((sbase[e1 >> 5] >> (e1 & 31)) & 1u);
-            uint32_t key0 = a0 ? order_key(logits[i * N + e0]) : 0u;
-            uint32_t key1 = a1 ? order_key(logits[i * N + e1]) : 0u;
-            const int kept = select_ranked(key0, key1, keep, selv, selj);
+            if (i >= B_real) {
+                write_empty(lane, i, k, idx, w, idx_copy);
+                continue;
+            }
+            const float l0 = e0 < N ? logits[i * N + e0] : kNegInf;
+            const float l1 = e1 < N ? logits[i * N + e1] : kNegInf;
+            bool a0 = e0 < N && ((sbase[e0 >> 5] >> (e0 & 31)) & 1u);
+            bool a1 = e1 < N && ((sbase[e1 >> 5] >> (e1 & 31)) & 1u);
+            if (!pruned && max_p < N) {
+                uint32_t th;
+                int jth;
+                kth_ranked(e0 < N ? order_key(l0) : 0u, e1 < N ? order_key(l1) : 0u, max_p, th, jth);
+                const uint32_t q0 = order_key(l0), q1 = order_key(l1);
+                a0 = a0 && (q0 > th || (q0 == th && e0 <= jth));
+                a1 = a1 && (q1 > th || (q1 == th && e1 <= jth));
+            }
+            uint32_t key0 = a0 ? order_key(l0) : 0u;
+            uint32_t key1 = a1 ? order_key(l1) : 0u;
+            const int kept = select_ranked(key0, key1, pruned ? n_l[i] : keep, selv, selj);
             write_token(lane, i, k, kept, selv[0], true, 0.0f, selv, selj, idx, w, idx_copy);
         }
     }
@@ -464,23 +524,26 @@ hipError_t launch_route(const float* logits, int B, int N, int k, int k0, float 
     const int threads = kWave * (B < 16 ? B : 16);
     if (oea)
         route_kernel<true, false><<<1, threads, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, mask, T,
-                                                        nullptr, nullptr, nullptr, nullptr);
+                                                        nullptr, nullptr, nullptr, nullptr, 0, N, nullptr);
     else
         route_kernel<false, false><<<1, threads, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w, nullptr,
-                                                         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+                                                         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                                                         N, nullptr);
     return hipGetLastError();
 }
 
-hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int k0, float p, int oea, int renorm,
-                                 int32_t* idx, float* w, int32_t* n_base, uint32_t* mask, int32_t* cnt,
-                                 int32_t* offsets, int32_t* perm, int32_t* active, int32_t* T, hipStream_t s) {
+hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int mode, int k0, float p, int max_p,
+                                 int renorm, const int32_t* n_valid, int32_t* idx, float* w, int32_t* n_base,
+                                 uint32_t* mask, int32_t* cnt, int32_t* offsets, int32_t* perm, int32_t* active,
+                                 int32_t* T, hipStream_t s) {
     const int threads = kWave * (B < 16 ? B : 16);
-    if (oea)
+    if (mode != MOE_ROUTE_TOPK)
         route_kernel<true, true><<<1, threads, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, mask, T, cnt,
-                                                       offsets, perm, active);
+                                                       offsets, perm, active, mode == MOE_ROUTE_PRUNED, max_p,
+                                                       n_valid);
     else
         route_kernel<false, true><<<1, threads, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w, nullptr,
-                                                        nullptr, T, cnt, offsets, perm, active);
+                                                        nullptr, T, cnt, offsets, perm, active, 0, N, n_valid);
     return hipGetLastError();
 }
 

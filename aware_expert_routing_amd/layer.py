@@ -93,12 +93,14 @@ class MoELayer:
         return b
 
     def route(self, logits: torch.Tensor, mode: str, k0: int = 0, p: float = 1.0,
-              buf: Buffers | None = None, stream=None) -> Buffers:
+              buf: Buffers | None = None, stream=None, max_p: int | None = None, n_valid=None) -> Buffers:
+        """Routing ("topk", "oea" or "pruned") and dispatch in one launch; n_valid
+        (device int32 [1]) marks trailing tokens as padding."""
         B = logits.shape[0]
         buf = buf or self.buffers(B)
-        if mode not in ("topk", "oea"):
+        if mode not in ("topk", "oea", "pruned"):
             raise ValueError(mode)
-        L.route_dispatch(logits, self.k, mode, k0, p, True, buf.route, buf.disp, stream)
+        L.route_dispatch(logits, self.k, mode, k0, p, True, buf.route, buf.disp, stream, max_p, n_valid)
         return buf
 
     def ffn(self, x: torch.Tensor, buf: Buffers, stream=None) -> torch.Tensor:
@@ -106,12 +108,13 @@ class MoELayer:
                             buf.disp, buf.y, buf.ws, stream)
 
     def forward(self, x: torch.Tensor, mode: str = "oea", k0: int = 3, p: float = 1.0,
-                logits: torch.Tensor | None = None, stream=None) -> Buffers:
+                logits: torch.Tensor | None = None, stream=None, max_p: int | None = None,
+                n_valid=None) -> Buffers:
         """Whole layer.  If `logits` is given the router GEMV is skipped."""
         B = x.shape[0]
         buf = self.buffers(B)
         if logits is None:
             logits = L.router_logits(x, self.w_r, buf.logits, stream)
-        self.route(logits, mode, k0, p, buf, stream)
+        self.route(logits, mode, k0, p, buf, stream, max_p, n_valid)
         self.ffn(x, buf, stream)
         return buf

@@ -144,18 +144,31 @@ int moe_dispatch(const int32_t *idx, int B, int N, int k, int32_t *cnt, int32_t 
                  int32_t *perm, int32_t *active, int32_t *T, void *stream);
 
 /*
- * Routing and dispatch in one launch: exactly moe_route_topk (mode
- * MOE_ROUTE_TOPK, with `renorm`) or moe_route_oea (mode MOE_ROUTE_OEA, with
- * k0 and p) followed by moe_dispatch on its idx, with the same outputs and
- * the same validation ([OEA] sections 2 Q1/Q2, 3 and 4, Eq. 2).  The routed
- * pairs stay on chip between the two steps.
- *   n_base, sbase_mask : OEA only, may be NULL (ignored for top-k)
- *   T                  : number of active experts (for OEA also |S_base|)
+ * Routing and dispatch in one launch, with the general OEA knobs [OEA
+ * sections 2 Q1/Q2, 3, 4 (Eq. 2), 5 (maxP, k_max, pruned vs OEA) and 7
+ * (padding tokens must not inflate T)].
+ *   mode MOE_ROUTE_TOPK   : vanilla top-k (renorm as in moe_route_topk)
+ *   mode MOE_ROUTE_OEA    : OEA; Phase 2 may take only experts the token
+ *                           ranks within its top max_p (k0 <= max_p <= N;
+ *                           max_p = N is the simplified router), until the
+ *                           token holds k experts (k plays k_max and may
+ *                           exceed the model's top-k)
+ *   mode MOE_ROUTE_PRUNED : OEA Phase 1 only: each token keeps its n_i
+ *                           baseline experts (same S_base and T as OEA)
+ *   n_valid : NULL, or a device int32: tokens i >= *n_valid are padding;
+ *             they get no experts (idx -1, w 0) and add nothing to S_base,
+ *             so a fixed-size (e.g. graph-captured) batch serves smaller
+ *             real batches without inflating T
+ *   Outputs as moe_route_oea (n_base, sbase_mask may be NULL; ignored for
+ *   top-k) followed by moe_dispatch on idx; T = number of active experts
+ *   (for OEA and pruned also |S_base|).  The routed pairs stay on chip
+ *   between routing and dispatch.
  */
-enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_OEA = 1 };
-int moe_route_dispatch(const float *logits, int B, int N, int k, int mode, int k0, float p, int renorm,
-                       int32_t *idx, float *w, int32_t *n_base, uint32_t *sbase_mask, int32_t *cnt,
-                       int32_t *offsets, int32_t *perm, int32_t *active, int32_t *T, void *stream);
+enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_OEA = 1, MOE_ROUTE_PRUNED = 2 };
+int moe_route_dispatch(const float *logits, int B, int N, int k, int mode, int k0, float p, int max_p,
+                       int renorm, const int32_t *n_valid, int32_t *idx, float *w, int32_t *n_base,
+                       uint32_t *sbase_mask, int32_t *cnt, int32_t *offsets, int32_t *perm, int32_t *active,
+                       int32_t *T, void *stream);
 
 /* Workspace bytes moe_expert_ffn needs for these sizes (host call). */
 size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);

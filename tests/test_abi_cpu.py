@@ -148,10 +148,12 @@ def test_publish_rejects_misaligned_weights():
 def test_route_dispatch_rejects_bad_arguments():
     lib = moe.lib()
     args = lambda **kw: [kw.get(n, d) for n, d in (
-        ("logits", FAKE), ("B", 16), ("N", 128), ("k", 8), ("mode", 1), ("k0", 3), ("p", 1.0), ("renorm", 1),
-        ("idx", FAKE), ("w", FAKE), ("n_base", None), ("mask", None), ("cnt", FAKE), ("offsets", FAKE),
-        ("perm", FAKE), ("active", FAKE), ("T", FAKE), ("stream", None))]
-    assert lib.moe_route_dispatch(*args(mode=2)) == -1
+        ("logits", FAKE), ("B", 16), ("N", 128), ("k", 8), ("mode", 1), ("k0", 3), ("p", 1.0), ("max_p", 128),
+        ("renorm", 1), ("n_valid", None), ("idx", FAKE), ("w", FAKE), ("n_base", None), ("mask", None),
+        ("cnt", FAKE), ("offsets", FAKE), ("perm", FAKE), ("active", FAKE), ("T", FAKE), ("stream", None))]
+    assert lib.moe_route_dispatch(*args(mode=3)) == -1
+    assert lib.moe_route_dispatch(*args(max_p=2)) == -1          # max_p < k0
+    assert lib.moe_route_dispatch(*args(max_p=129)) == -1        # max_p > N
     assert lib.moe_route_dispatch(*args(k0=9)) == -1
     assert lib.moe_route_dispatch(*args(p=0.0)) == -1
     assert lib.moe_route_dispatch(*args(perm=None)) == -1

@@ -142,6 +142,36 @@ def test_fused_route_dispatch_parity(B, N, k, mode, k0, p, kind, scale, zipf):
             assert dref["T"] == ref["T"]
 
 
+@pytest.mark.parametrize("B,N,k,mode,k0,p,max_p,nv,scale,zipf", [
+    (16, 128, 8, "pruned", 3, 1.0, None, None, 0.9, 0.0), (64, 128, 8, "pruned", 5, 0.5, None, None, 4.0, 1.1),
+    (16, 128, 8, "oea", 3, 1.0, 8, None, 0.9, 0.0),        # piggyback only within the token's top-8
+    (32, 128, 12, "oea", 3, 0.7, 40, None, 4.0, 1.1),      # k_max = 12 > top-8, maxP = 40
+    (16, 64, 16, "oea", 2, 0.9, 64, None, 2.0, 0.0),       # k_max = 16
+    (16, 128, 8, "oea", 3, 1.0, None, 11, 0.9, 0.0),       # padding mask: 5 padding tokens
+    (16, 128, 8, "topk", 0, 1.0, None, 7, 1.0, 1.1),
+    (128, 128, 8, "pruned", 3, 0.8, None, 100, 4.0, 1.1),
+    (8, 16, 4, "oea", 2, 1.0, 3, 0, 1.0, 0.0),            # every token padding
+])
+def test_route_variants_parity(B, N, k, mode, k0, p, max_p, nv, scale, zipf):
+    # page OEA section 5 (maxP, k_max, pruned) and section 7 (padding tokens)
+    for seed in range(3):
+        l = _logits("normal", seed, B, N, scale, zipf)
+        n_valid = None if nv is None else torch.tensor([nv], dtype=torch.int32, device=DEV)
+        route, disp = moe.route_dispatch(torch.from_numpy(l).to(DEV), k, mode, k0, p, True,
+                                         max_p=max_p, n_valid=n_valid)
+        ref = oracle.route(l, k, oea=(mode != "topk"), k0=k0, p=p, pruned=(mode == "pruned"), max_p=max_p,
+                           n_valid=nv)
+        assert np.array_equal(route["idx"].cpu().numpy(), ref["idx"])
+        assert np.abs(route["w"].cpu().numpy().astype(np.float64) - ref["w"]).max() <= 1e-6
+        if mode != "topk":
+            assert np.array_equal(route["n_base"].cpu().numpy(), ref["n_base"])
+            assert np.array_equal(route["mask"].cpu().numpy().view(np.uint32), ref["mask"])
+        dref = oracle.dispatch(ref["idx"], N)
+        for key in ("cnt", "offsets", "perm", "active"):
+            assert np.array_equal(disp[key].cpu().numpy(), dref[key]), key
+        assert int(disp["T"].item()) == dref["T"]
+
+
 def test_dispatch_with_empty_slots_and_rows():
     B, N, k = 6, 16, 4
     idx = np.array([[3, 5, -1, -1], [-1, -1, -1, -1], [15, 0, 3, -1], [7, -1, -1, -1],
