@@ -118,3 +118,22 @@ class MoELayer:
         self.route(logits, mode, k0, p, buf, stream, max_p, n_valid)
         self.ffn(x, buf, stream)
         return buf
+
+    def capture(self, x: torch.Tensor, mode: str = "oea", k0: int = 3, p: float = 1.0,
+                max_p: int | None = None, n_valid=None) -> torch.cuda.CUDAGraph:
+        """Capture forward(x, ...) into a HIP graph (every kernel of the layer, no
+        allocation or memset inside).  Replaying it recomputes the layer for
+        whatever `x` and `n_valid` hold at replay time; results land in
+        self.buffers(B).  Pair it with `n_valid` to serve real batches smaller
+        than B without padding tokens inflating T."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):   # warm-up outside capture (allocates the buffers)
+            self.forward(x, mode, k0, p, max_p=max_p, n_valid=n_valid)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x, mode, k0, p, max_p=max_p, n_valid=n_valid)
+        return graph
+

@@ -1,0 +1,49 @@
+"""A whole layer captured into a HIP graph: every replay must reproduce the
+eager result bit for bit, with the program's own eager work and device
+synchronisation between replays, and the device-side padding mask must let
+one captured batch size serve smaller real batches (page "Opportunistic
+Expert Activation (OEA) - L2", section 7: padding tokens must not inflate T).
+"""
+import numpy as np
+import pytest
+import torch
+
+import aware_expert_routing_amd as moe
+import synth
+from gpu_util import DEV, build_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _x(seed, B, H):
+    return torch.from_numpy(synth.to_bf16_bits(synth.activations(seed, B, H)).view(np.int16)).to(DEV) \
+        .view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode,k0", [("oea", 3), ("topk", 0), ("pruned", 3)])
+def test_graph_replays_match_eager(mode, k0):
+    N, k, H, I, B = 32, 8, 512, 256, 16
+    layer, _ = build_layer(N, k, H, I, 11, fmt="bf16")
+    x_static = _x(0, B, H).clone()
+    nv = torch.tensor([B], dtype=torch.int32, device=DEV)
+    graph = layer.capture(x_static, mode, k0, 1.0, n_valid=nv)
+    eager_layer, _ = build_layer(N, k, H, I, 11, fmt="bf16")   # same weights, separate buffers
+    for rep, (seed, n_real) in enumerate([(1, 16), (2, 16), (3, 9), (4, 1), (5, 16), (6, 12)]):
+        x_static.copy_(_x(seed, B, H))
+        nv.fill_(n_real)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {key: t.clone() for key, t in layer.buffers(B).disp.items()}
+        y_graph = layer.buffers(B).y.clone()
+        ref = eager_layer.forward(x_static, mode, k0, 1.0, n_valid=nv)
+        torch.cuda.synchronize()
+        assert torch.equal(y_graph, ref.y), rep
+        for key in got:
+            assert torch.equal(got[key], ref.disp[key]), (rep, key)
+        # padding rows produce exact zeros and the active set is that of the real tokens
+        if n_real < B:
+            assert torch.count_nonzero(y_graph[n_real:]).item() == 0
+            alone = eager_layer.forward(x_static[:n_real].clone(), mode, k0, 1.0)
+            torch.cuda.synchronize()
+            assert int(alone.disp["T"].item()) == int(got["T"].item())
+            assert torch.equal(alone.y, y_graph[:n_real])
