@@ -188,6 +188,21 @@ def main():
             step(i, True)
         torch.cuda.synchronize()
         ffn_ms = [ev0[i].elapsed_time(ev1[i]) for i in range(args.steps)]
+        # the same steps replayed from HIP graphs (one per layer copy and batch)
+        graphs = {}
+        for i in range(args.steps):
+            key = (i % len(layers), i % len(xs))
+            if key not in graphs:
+                graphs[key] = layers[key[0]].capture(xs[key[1]], mode, k0, 1.0)
+        for i in range(args.warmup):
+            graphs[(i % len(layers), i % len(xs))].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[(i % len(layers), i % len(xs))].replay()
+        torch.cuda.synchronize()
+        graph_wall = time.perf_counter() - t0
+        del graphs
         Tsteps = [Ts[i % len(Ts)] for i in range(args.steps)]
         layer_bytes = sum(t * W_e + fixed_layer for t in Tsteps)
         ffn_bytes = sum(t * W_e + fixed_ffn for t in Tsteps)
@@ -203,6 +218,8 @@ def main():
             ffn_us_p90=float(np.percentile(ffn_ms, 90) * 1e3),
             ffn_gbps=ffn_bytes / ffn_s / 1e9,
             ffn_bytes_per_launch=ffn_bytes / args.steps,
+            graph_us_per_layer=graph_wall / args.steps * 1e6,
+            graph_gbps=layer_bytes / graph_wall / 1e9,
         )
 
     results = {}
