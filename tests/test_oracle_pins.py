@@ -510,3 +510,123 @@ def test_padding_tokens_route_nowhere_and_leave_the_rest_unchanged(oea, pruned):
     assert np.array_equal(full["idx"][:nv], alone["idx"]) and np.array_equal(full["w"][:nv], alone["w"])
     assert np.all(full["idx"][nv:] == -1) and np.all(full["w"][nv:] == 0.0)
     assert full["T"] == alone["T"]
+
+
+# ---------------------------------------------------------------------------
+# online residency policy (page "DynaExq", sections 2.3 / 2.5 / 3.3 / 3.5)
+# ---------------------------------------------------------------------------
+from oracle import residency as res_oracle  # noqa: E402
+
+
+def _violations(S, members, margin):
+    """Pairs (outsider, member) that the hysteresis rule says must swap."""
+    S = np.asarray(S, np.float32)
+    m32 = np.float32(margin)
+    out = [o for o in range(len(S)) if o not in members and S[o] > 0]
+    return [(o, m) for o in out for m in members if S[o] > np.float32(S[m] + m32)]
+
+
+def test_residency_policy_golden_examples():
+    with open(os.path.join(GOLDEN, "residency_hysteresis.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        N = len(case["S"])
+        cur = np.zeros(N, bool)
+        cur[case["current"]] = True
+        target, promote, demote = res_oracle.select(np.array(case["S"], np.float32), cur, case["n_hi"],
+                                                    case["margin"])
+        assert promote == case["promote"], case["name"]
+        assert demote == case["demote"], case["name"]
+        assert target.sum() <= case["n_hi"]
+
+
+def test_residency_policy_margin_zero_is_the_top_n_set():
+    # From any full start with distinct positive scores, margin 0 reaches the
+    # plain top-n_hi set (numpy's sort), in one update.
+    r = synth.rng(71)
+    for trial in range(200):
+        N = int(r.integers(2, 40))
+        n_hi = int(r.integers(1, N + 1))
+        S = r.permutation(N).astype(np.float32) + 1.0
+        cur = np.zeros(N, bool)
+        cur[r.choice(N, n_hi, replace=False)] = True
+        target, _, _ = res_oracle.select(S, cur, n_hi, 0.0)
+        top = np.zeros(N, bool)
+        top[np.argsort(-S, kind="stable")[:n_hi]] = True
+        assert np.array_equal(target, top)
+
+
+def test_residency_policy_from_empty_fills_the_top_positive_scores():
+    r = synth.rng(72)
+    for trial in range(200):
+        N = int(r.integers(1, 40))
+        n_hi = int(r.integers(0, N + 1))
+        S = np.where(r.random(N) < 0.3, 0.0, r.integers(1, 6, N) / 4.0).astype(np.float32)   # ties, zeros
+        target, promote, demote = res_oracle.select(S, np.zeros(N, bool), n_hi, float(r.random()))
+        order = np.lexsort((np.arange(N), -S))          # score desc, index asc
+        want = [int(e) for e in order if S[e] > 0][:n_hi]
+        assert promote == want and demote == []
+        assert target.sum() == len(want)
+
+
+@pytest.mark.parametrize("N", [4, 6, 8])
+def test_residency_policy_is_a_fewest_swaps_fixpoint(N):
+    # Brute force over every set of the same size: the update leaves no pair
+    # that violates the margin, and no such set is reachable with fewer swaps.
+    r = synth.rng(73, N)
+    for trial in range(60):
+        n_hi = int(r.integers(1, N))
+        S = (r.integers(0, 9, N) / 8.0).astype(np.float32)   # coarse values: ties and near-ties
+        margin = float(r.choice([0.0, 0.125, 0.3, 0.5]))
+        cur_list = sorted(r.choice(N, n_hi, replace=False).tolist())
+        cur = np.zeros(N, bool)
+        cur[cur_list] = True
+        target, promote, demote = res_oracle.select(S, cur, n_hi, margin)
+        members = [e for e in range(N) if target[e]]
+        assert len(members) <= n_hi
+        assert len(promote) == len(demote)          # the set was full: swaps only
+        assert not _violations(S, members, margin)
+        best = min(len(set(c) - set(cur_list)) for c in itertools.combinations(range(N), n_hi)
+                   if not _violations(S, list(c), margin))
+        assert len(promote) == best
+
+
+def test_residency_policy_keeps_locked_experts_and_the_budget():
+    r = synth.rng(74)
+    for trial in range(200):
+        N = int(r.integers(2, 30))
+        n_hi = int(r.integers(0, N + 1))
+        S = r.random(N).astype(np.float32)
+        cur = r.random(N) < 0.5
+        locked = r.random(N) < 0.2
+        target, promote, demote = res_oracle.select(S, cur, n_hi, 0.05, locked)
+        assert np.array_equal(target[locked], cur[locked])
+        assert not (set(promote) & set(demote))
+        unlocked_members = int((cur & ~locked).sum())
+        # the set never ends above capacity unless locked members alone exceed it
+        assert target.sum() <= max(n_hi, int((cur & locked).sum()))
+        assert all(not cur[e] for e in promote) and all(cur[e] for e in demote)
+        assert unlocked_members >= len(demote)
+
+
+def test_residency_ema_fold_closed_form():
+    # S_t = alpha^t S_0 + (1 - alpha) sum_j alpha^(t-1-j) c_j, folding one
+    # interval at a time; an interval's counts add up before the fold.
+    alpha = 0.75
+    S = np.array([1.0, 0.0, 2.0])
+    intervals = [[[1, 0, 2], [3, 1, 0]], [[0, 0, 5]], [[2, 2, 2], [0, 1, 0], [1, 0, 0]]]
+    cur = S.copy()
+    for iv in intervals:
+        cur = res_oracle.ema_fold(cur, iv, alpha)
+    sums = [np.sum(iv, axis=0) for iv in intervals]
+    want = alpha ** 3 * S + (1 - alpha) * (alpha ** 2 * sums[0] + alpha * sums[1] + sums[2])
+    np.testing.assert_allclose(cur, want, rtol=1e-15, atol=0)
+
+
+def test_budget_model_admits_only_what_fits():
+    b = res_oracle.Budget(total=100, fixed=30)
+    assert b.capacity == 70
+    assert b.try_reserve(40) and b.try_reserve(30)
+    assert not b.try_reserve(1)
+    b.release(30)
+    assert b.try_reserve(25) and not b.try_reserve(6) and b.try_reserve(5)
