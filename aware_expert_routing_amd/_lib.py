@@ -15,7 +15,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_EFULL = 0, -1, -2, -3, -4
+MOE_RES_LO, MOE_RES_PROMOTING, MOE_RES_HI, MOE_RES_EVICTING = 0, 1, 2, 3
+MOE_RES_FORCE_UPDATE, MOE_RES_WAIT = 1, 2
 MOE_ROUTE_TOPK, MOE_ROUTE_OEA, MOE_ROUTE_PRUNED = 0, 1, 2
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_W_F32, MOE_W_BF16, MOE_W_INT4_G128 = 0, 1, 2
@@ -38,6 +40,27 @@ class ExpertHandle(ctypes.Structure):
 HANDLE_BYTES = ctypes.sizeof(ExpertHandle)
 assert HANDLE_BYTES == 64
 
+
+class ResidencyConfig(ctypes.Structure):
+    """Mirror of moe_residency_config (include/moe_residency.h)."""
+    _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("I", ctypes.c_int),
+                ("table", ctypes.c_void_p), ("lo", ctypes.POINTER(ExpertHandle)),
+                ("hi_src", ctypes.POINTER(ctypes.c_void_p)), ("pool_hi", ctypes.c_void_p),
+                ("budget", ctypes.c_void_p), ("S", ctypes.c_void_p), ("c", ctypes.c_void_p),
+                ("S_host", ctypes.c_void_p), ("n_hi", ctypes.c_int), ("alpha", ctypes.c_float),
+                ("margin", ctypes.c_float), ("interval_s", ctypes.c_double),
+                ("compute_stream", ctypes.c_void_p), ("mig_stream", ctypes.c_void_p)]
+
+
+class ResidencyStats(ctypes.Structure):
+    """Mirror of moe_residency_stats."""
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "steps", "updates", "decisions", "promotions_started", "promotions_published", "demotions",
+        "evictions", "deferred", "bytes_h2d")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
 _lib = None
 
 # (name, argtypes, restype)
@@ -55,6 +78,26 @@ _SIGNATURES = [
     ("moe_quantize_int4_g128", [_P, _I, _I, _P, _P, _P], _I),
     ("moe_pack_weights", [_I, _P, _P, _I, _I, _P, _P, _P], _I),
     ("moe_hotness_ema", [_P, _P, _I, _F, _P], _I),
+    ("moe_pool_create", [_P, _S, _S, ctypes.POINTER(_P)], _I),
+    ("moe_pool_destroy", [_P], None),
+    ("moe_pool_alloc", [_P, ctypes.POINTER(_P)], _I),
+    ("moe_pool_free", [_P, _P], _I),
+    ("moe_pool_free_blocks", [_P], _I),
+    ("moe_pool_total_blocks", [_P], _I),
+    ("moe_pool_block_bytes", [_P], _S),
+    ("moe_budget_create", [_S, _S, ctypes.POINTER(_P)], _I),
+    ("moe_budget_destroy", [_P], None),
+    ("moe_budget_try_reserve", [_P, _S], _I),
+    ("moe_budget_release", [_P, _S], _I),
+    ("moe_budget_used", [_P], _S),
+    ("moe_budget_capacity", [_P], _S),
+    ("moe_residency_select", [_P, _P, _P, _I, _I, _F, _P, _P, ctypes.POINTER(_I), _P, ctypes.POINTER(_I)], _I),
+    ("moe_residency_create", [ctypes.POINTER(ResidencyConfig), ctypes.POINTER(_P)], _I),
+    ("moe_residency_step", [_P, _P, _I], _I),
+    ("moe_residency_state", [_P, _I], _I),
+    ("moe_residency_pending", [_P], _I),
+    ("moe_residency_get_stats", [_P, ctypes.POINTER(ResidencyStats)], _I),
+    ("moe_residency_destroy", [_P], _I),
     ("moe_status_str", [_I], ctypes.c_char_p),
     ("moe_last_error", [], ctypes.c_char_p),
 ]
@@ -240,3 +283,76 @@ def hotness_ema(S, cnt, alpha: float, stream=None):
 
 def status_str(status: int) -> str:
     return lib().moe_status_str(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# residency (include/moe_residency.h): host objects behind opaque pointers
+# ---------------------------------------------------------------------------
+def pool_create(arena_ptr: int, arena_bytes: int, block_bytes: int) -> int:
+    out = ctypes.c_void_p()
+    _check("moe_pool_create", lib().moe_pool_create(arena_ptr, arena_bytes, block_bytes, ctypes.byref(out)))
+    return out.value
+
+
+def pool_alloc(pool: int) -> int | None:
+    blk = ctypes.c_void_p()
+    st = lib().moe_pool_alloc(pool, ctypes.byref(blk))
+    if st == MOE_EFULL:
+        return None
+    _check("moe_pool_alloc", st)
+    return blk.value
+
+
+def pool_free(pool: int, block: int):
+    _check("moe_pool_free", lib().moe_pool_free(pool, block))
+
+
+def budget_create(total: int, fixed: int) -> int:
+    out = ctypes.c_void_p()
+    _check("moe_budget_create", lib().moe_budget_create(total, fixed, ctypes.byref(out)))
+    return out.value
+
+
+def budget_try_reserve(budget: int, nbytes: int) -> bool:
+    st = lib().moe_budget_try_reserve(budget, nbytes)
+    if st < 0:
+        _check("moe_budget_try_reserve", st)
+    return st == 1
+
+
+def budget_release(budget: int, nbytes: int):
+    _check("moe_budget_release", lib().moe_budget_release(budget, nbytes))
+
+
+def residency_select(S, in_hi, n_hi: int, margin: float, locked=None):
+    """Host policy update on numpy arrays: returns (target, promote, demote)."""
+    import numpy as np
+    S = np.ascontiguousarray(S, dtype=np.float32)
+    N = S.shape[0]
+    in_hi = np.ascontiguousarray(in_hi, dtype=np.uint8)
+    lk = None if locked is None else np.ascontiguousarray(locked, dtype=np.uint8)
+    target = np.zeros(N, np.uint8)
+    pro = np.zeros(N, np.int32)
+    dem = np.zeros(N, np.int32)
+    npro, ndem = ctypes.c_int(), ctypes.c_int()
+    _check("moe_residency_select", lib().moe_residency_select(
+        S.ctypes.data, in_hi.ctypes.data, None if lk is None else lk.ctypes.data, N, n_hi, float(margin),
+        target.ctypes.data, pro.ctypes.data, ctypes.byref(npro), dem.ctypes.data, ctypes.byref(ndem)))
+    return target.astype(bool), pro[:npro.value].tolist(), dem[:ndem.value].tolist()
+
+
+def residency_create(cfg: ResidencyConfig) -> int:
+    out = ctypes.c_void_p()
+    _check("moe_residency_create", lib().moe_residency_create(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def residency_step(res: int, cnt=None, force: bool = False, wait: bool = False):
+    flags = (MOE_RES_FORCE_UPDATE if force else 0) | (MOE_RES_WAIT if wait else 0)
+    _check("moe_residency_step", lib().moe_residency_step(res, _ptr(cnt), flags))
+
+
+def residency_stats(res: int) -> dict:
+    st = ResidencyStats()
+    _check("moe_residency_get_stats", lib().moe_residency_get_stats(res, ctypes.byref(st)))
+    return st.as_dict()

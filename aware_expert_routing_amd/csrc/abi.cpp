@@ -8,9 +8,10 @@
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
+namespace moe {
 namespace {
-
 thread_local char g_last_error[256] = "";
+}
 
 int fail(int status, const char* msg) {
     snprintf(g_last_error, sizeof g_last_error, "%s", msg);
@@ -22,6 +23,15 @@ int hip_status(hipError_t e, const char* where) {
     snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(e));
     return MOE_EHIP;
 }
+
+const char* last_error() { return g_last_error; }
+
+}  // namespace moe
+
+using moe::fail;
+using moe::hip_status;
+
+namespace {
 
 int check_sizes(int B, int N, int k) {
     if (N < 1 || N > moe::kMaxExperts) return fail(MOE_EINVAL, "N must be in [1, 128]");
@@ -41,11 +51,12 @@ MOE_API const char* moe_status_str(int status) {
         case MOE_EINVAL: return "invalid argument";
         case MOE_EUNSUPPORTED: return "unsupported size";
         case MOE_EHIP: return "HIP runtime error";
+        case MOE_EFULL: return "no free block (retry later)";
         default: return "unknown status";
     }
 }
 
-MOE_API const char* moe_last_error(void) { return g_last_error; }
+MOE_API const char* moe_last_error(void) { return moe::last_error(); }
 
 MOE_API int moe_router_logits(const void* x, int x_dtype, const float* w_r, int B, int H, int N,
                               float* logits, void* stream) {

@@ -26,6 +26,14 @@ hipError_t launch_dispatch(const int32_t* idx, int B, int N, int k, int32_t* cnt
                            int32_t* offsets, int32_t* perm, int32_t* active, int32_t* T,
                            hipStream_t s);
 hipError_t launch_hotness_ema(float* S, const int32_t* cnt, int N, float alpha, hipStream_t s);
+hipError_t launch_hotness_accumulate(int32_t* c, const int32_t* cnt, int N, hipStream_t s);
+hipError_t launch_hotness_fold(float* S, int32_t* c, int N, float alpha, hipStream_t s);
+
+// Error reporting shared by the C ABI sources: set the calling thread's
+// message and return the status.
+int fail(int status, const char* msg);
+int hip_status(hipError_t e, const char* where);
+const char* last_error();
 hipError_t launch_handle_publish(moe_expert_handle* table, int e, moe_expert_handle h,
                                  hipStream_t s);
 hipError_t launch_quantize_int4(const uint16_t* w, int rows, int cols, uint8_t* q,

@@ -500,6 +500,21 @@ __global__ void hotness_kernel(float* S, const int32_t* cnt, int N, float alpha)
     if (e < N) S[e] = alpha * S[e] + (1.0f - alpha) * static_cast<float>(cnt[e]);
 }
 
+// Interval counters: c += cnt per forward call; at an update S <- alpha S +
+// (1 - alpha) c and c <- 0 (a kernel, not a memset, so it may be captured).
+__global__ void hotness_accumulate_kernel(int32_t* c, const int32_t* cnt, int N) {
+    int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < N) c[e] += cnt[e];
+}
+
+__global__ void hotness_fold_kernel(float* S, int32_t* c, int N, float alpha) {
+    int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < N) {
+        S[e] = alpha * S[e] + (1.0f - alpha) * static_cast<float>(c[e]);
+        c[e] = 0;
+    }
+}
+
 __global__ void publish_kernel(moe_expert_handle* table, int e, moe_expert_handle h) {
     if (threadIdx.x == 0) table[e] = h;
 }
@@ -556,6 +571,16 @@ hipError_t launch_dispatch(const int32_t* idx, int B, int N, int k, int32_t* cnt
 
 hipError_t launch_hotness_ema(float* S, const int32_t* cnt, int N, float alpha, hipStream_t s) {
     hotness_kernel<<<1, 128, 0, s>>>(S, cnt, N, alpha);
+    return hipGetLastError();
+}
+
+hipError_t launch_hotness_accumulate(int32_t* c, const int32_t* cnt, int N, hipStream_t s) {
+    hotness_accumulate_kernel<<<1, 128, 0, s>>>(c, cnt, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_hotness_fold(float* S, int32_t* c, int N, float alpha, hipStream_t s) {
+    hotness_fold_kernel<<<1, 128, 0, s>>>(S, c, N, alpha);
     return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 """CPU-only checks of the C ABI: the library loads, exports every entry point
-include/moe.h declares, and rejects invalid arguments on the host before
+include/*.h declares, and rejects invalid arguments on the host before
 anything is launched (no call here reaches a kernel)."""
 import ctypes
 import os
@@ -10,13 +10,13 @@ import pytest
 import aware_expert_routing_amd as moe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe.h", "moe_residency.h")]
 
 FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails validation
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
@@ -159,3 +159,123 @@ def test_route_dispatch_rejects_bad_arguments():
     assert lib.moe_route_dispatch(*args(perm=None)) == -1
     assert lib.moe_route_dispatch(*args(B=129)) == -2
     assert lib.moe_route_dispatch(*args(N=0)) == -1
+
+
+# ---------------------------------------------------------------------------
+# residency host objects (include/moe_residency.h): pure host bookkeeping
+# ---------------------------------------------------------------------------
+ARENA = 1 << 32            # a fake device address: the pool never dereferences it
+
+
+def test_pool_hands_out_each_block_once_and_rejects_foreign_or_double_frees():
+    lib = moe.lib()
+    blk = 4096
+    pool = moe.pool_create(ARENA, 5 * blk + 100, blk)
+    try:
+        assert lib.moe_pool_total_blocks(pool) == 5 and lib.moe_pool_block_bytes(pool) == blk
+        got = [moe.pool_alloc(pool) for _ in range(5)]
+        assert sorted(got) == [ARENA + i * blk for i in range(5)]
+        assert moe.pool_alloc(pool) is None                  # exhausted: MOE_EFULL, not an error
+        assert lib.moe_pool_free_blocks(pool) == 0
+        moe.pool_free(pool, got[2])
+        assert moe.pool_alloc(pool) == got[2]                # constant-time reuse of the freed block
+        moe.pool_free(pool, got[0])
+        with pytest.raises(moe.MoeError):
+            moe.pool_free(pool, got[0])                      # double free
+        with pytest.raises(moe.MoeError):
+            moe.pool_free(pool, ARENA + 17)                  # not a block start
+        with pytest.raises(moe.MoeError):
+            moe.pool_free(pool, ARENA + 5 * blk)             # past the last block
+        with pytest.raises(moe.MoeError):
+            moe.pool_free(pool, ARENA - blk)
+    finally:
+        lib.moe_pool_destroy(pool)
+
+
+def test_pool_rejects_bad_geometry():
+    with pytest.raises(moe.MoeError):
+        moe.pool_create(ARENA, 1 << 20, 1000)                # not a multiple of 256
+    with pytest.raises(moe.MoeError):
+        moe.pool_create(ARENA + 128, 1 << 20, 4096)          # misaligned arena
+    with pytest.raises(moe.MoeError):
+        moe.pool_create(ARENA, 100, 256)                     # no whole block
+
+
+def test_budget_tracker_matches_the_budget_model_and_is_thread_safe():
+    import threading
+    from oracle.residency import Budget
+
+    lib = moe.lib()
+    b = moe.budget_create(1000, 300)
+    try:
+        ref = Budget(1000, 300)
+        assert lib.moe_budget_capacity(b) == ref.capacity == 700
+        for nbytes in [100, 250, 400, 350, 1, 0, 50]:
+            assert moe.budget_try_reserve(b, nbytes) == ref.try_reserve(nbytes)
+            assert lib.moe_budget_used(b) == ref.used
+        moe.budget_release(b, 250)
+        ref.release(250)
+        assert lib.moe_budget_used(b) == ref.used
+        with pytest.raises(moe.MoeError):
+            moe.budget_release(b, ref.used + 1)
+        moe.budget_release(b, ref.used)
+        # many threads racing for 7-byte reservations never overshoot
+        wins = []
+
+        def worker():
+            n = 0
+            for _ in range(2000):
+                n += moe.budget_try_reserve(b, 7)
+            wins.append(n)
+
+        ts = [threading.Thread(target=worker) for _ in range(8)]
+        [t.start() for t in ts]
+        [t.join() for t in ts]
+        assert sum(wins) == 700 // 7 and lib.moe_budget_used(b) == 700
+    finally:
+        lib.moe_budget_destroy(b)
+    with pytest.raises(moe.MoeError):
+        moe.budget_create(10, 11)
+
+
+def test_residency_select_matches_the_oracle():
+    import numpy as np
+    import synth
+    from oracle import residency as ref
+
+    r = synth.rng(81)
+    for trial in range(400):
+        N = int(r.integers(1, 129))
+        n_hi = int(r.integers(0, N + 1))
+        kind = trial % 4
+        if kind == 0:
+            S = r.random(N).astype(np.float32)
+        elif kind == 1:
+            S = (r.integers(0, 6, N) / 4.0).astype(np.float32)          # ties and zeros
+        elif kind == 2:
+            S = (r.zipf(1.5, N) % 50).astype(np.float32) * np.float32(0.1)
+        else:
+            S = np.float32(0.3) + (r.integers(-2, 3, N) * np.float32(2.0 ** -24))   # margin rounding cases
+        cur = r.random(N) < r.random()
+        locked = (r.random(N) < 0.15) if trial % 3 == 0 else None
+        margin = float(r.choice([0.0, 0.05, 0.1, 2.0 ** -24, 0.3]))
+        got = moe.residency_select(S, cur, n_hi, margin, locked)
+        want = ref.select(S, cur, n_hi, margin, locked)
+        assert np.array_equal(got[0], want[0]) and got[1] == want[1] and got[2] == want[2], trial
+
+
+def test_residency_create_rejects_bad_configs():
+    lib = moe.lib()
+    cfg = moe.ResidencyConfig()
+    assert lib.moe_residency_create(None, None) == -1
+    out = ctypes.c_void_p()
+    cfg.N, cfg.H, cfg.I = 16, 256, 128
+    assert lib.moe_residency_create(ctypes.byref(cfg), ctypes.byref(out)) == -1   # null pointers
+    assert "null" in moe.lib().moe_last_error().decode()
+    cfg.N = 0
+    assert lib.moe_residency_create(ctypes.byref(cfg), ctypes.byref(out)) == -1
+    cfg.N, cfg.H = 16, 200
+    assert lib.moe_residency_create(ctypes.byref(cfg), ctypes.byref(out)) == -1
+    assert "multiples of 128" in moe.lib().moe_last_error().decode()
+    assert lib.moe_residency_step(None, None, 0) == -1
+    assert lib.moe_residency_state(None, 0) == -1
