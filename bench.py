@@ -242,7 +242,8 @@ def main():
     extended = None
     if not args.no_extended and args.only is None and args.config == "qwen30b":
         extended = {"batch_sweep": batch_sweep(layers, wr_dev, N, k, H, I),
-                    "mixed_int4": mixed_int4(layers, wr_dev, N, k, H, I, gate, up, down)}
+                    "mixed_int4": mixed_int4(layers, wr_dev, N, k, H, I, gate, up, down),
+                    "dynamic_residency": dynamic_residency(wr_dev, N, k, H, I, gate, up, down)}
         del layers[:]
         torch.cuda.empty_cache()
         extended["qwen235b"] = qwen235b_lines()
@@ -487,6 +488,79 @@ def mixed_int4(layers, w_r, N, k, H, I, gate, up, down, B=32, warm=64, hot=32, c
                     "gbps": round(float(np.mean(byts)) / us / 1e3, 1)}
     del mlayers
     return out
+
+
+def dynamic_residency(w_r, N, k, H, I, gate, up, down, B=32, n_hi=32, alpha=0.9, margin=0.5, period=8,
+                      phase_steps=48):
+    """Online residency on the Qwen3-30B shape (page DynaExq, 2.2-2.5 / 3.2-3.5):
+    every expert resident in INT4, bf16 versions in pinned host memory, 32
+    high-precision blocks.  Vanilla top-8 routing with a Zipf(1.1) bias whose
+    expert order changes every `phase_steps` steps; a policy update every
+    `period` steps; copies run on the migration stream while the layer runs.
+    Reports the layer's compute-stream time per step with and without copies
+    in flight, and the promotions' host-to-device rate."""
+    import numpy as np
+    import torch
+
+    import aware_expert_routing_amd as moe
+    import synth
+
+    dev = w_r.device
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    lo, hi_host = [], []
+    for e in range(N):
+        mats = [dev_bf16(gate[e]), dev_bf16(up[e]), dev_bf16(down[e])]
+        q = [moe.quantize_int4_g128(m) for m in mats]
+        lo.append(moe.ExpertTensors.pack(moe.MOE_W_INT4_G128, q[0][0], q[1][0], q[2][0], q[0][1], q[1][1],
+                                         q[2][1]))
+        hi_host.append(moe.pinned_hi_version(moe.ExpertTensors.pack(moe.MOE_W_BF16, *mats)))
+    layer = moe.MoELayer(H, I, N, k, w_r, lo, dev)
+    torch.cuda.synchronize()
+    res = moe.Residency(layer, lo, hi_host, n_hi, alpha=alpha, margin=margin)
+    xs = [dev_bf16(synth.to_bf16_bits(synth.activations(700 + b, B, H))) for b in range(10)]
+    base = [moe.router_logits(x, w_r) for x in xs]
+    biases = [torch.from_numpy(synth.zipf_bias(N, 1.1, seed=40 + ph)).to(dev) for ph in range(3)]
+    quiet, busy = [], []
+    t_update, settle = None, []
+    try:
+        for i in range(3 * phase_steps):
+            logits = base[i % 10] + biases[i // phase_steps][None, :]
+            inflight = any(s in (moe.MOE_RES_PROMOTING, moe.MOE_RES_EVICTING) for s in res.states())
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            buf = layer.forward(xs[i % 10], "topk", logits=logits)
+            e1.record()
+            force = i % period == period - 1
+            res.step(buf.disp["cnt"], force=force)
+            e1.synchronize()
+            (busy if inflight else quiet).append(e0.elapsed_time(e1) * 1e3)
+            now = time.perf_counter()
+            if force:
+                t_update = (now, res.stats()["bytes_h2d"])
+            elif t_update is not None and not any(
+                    s in (moe.MOE_RES_PROMOTING, moe.MOE_RES_EVICTING) for s in res.states()) \
+                    and res.pending() == 0 and res.stats()["decisions"] == res.stats()["updates"]:
+                moved = res.stats()["bytes_h2d"] - t_update[1]
+                if moved:
+                    settle.append((moved, now - t_update[0]))
+                t_update = None
+        st = res.stats()
+    finally:
+        res.close()
+        del layer
+    moved = sum(m for m, _ in settle)
+    span = sum(t for _, t in settle)
+    return {"B": B, "n_hi": n_hi, "alpha": alpha, "margin": margin, "update_every_steps": period,
+            "steps": 3 * phase_steps, "stats": st,
+            "layer_us_quiet": round(float(np.median(quiet)), 2) if quiet else None,
+            "layer_us_copies_in_flight": round(float(np.median(busy)), 2) if busy else None,
+            "steps_with_copies_in_flight": len(busy),
+            "promotion_h2d_gbps": round(moved / span / 1e9, 2) if span else None,
+            "note": "layer time from events on the compute stream (router GEMV + routing + FFN); "
+                    "H2D rate = bytes promoted per update / wall time from the update to settled states"}
 
 
 def qwen235b_lines(copies=2, steps=30):
