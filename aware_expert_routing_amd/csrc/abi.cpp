@@ -104,7 +104,8 @@ MOE_API int moe_dispatch(const int32_t* idx, int B, int N, int k, int32_t* cnt, 
 }
 
 MOE_API int moe_route_dispatch(const float* logits, int B, int N, int k, int mode, int k0, float p, int max_p,
-                               int renorm, const int32_t* n_valid, int32_t* idx, float* w, int32_t* n_base,
+                               int renorm, const int32_t* n_valid, const int32_t* k0_by_batch, int32_t* idx,
+                               float* w, int32_t* n_base,
                                uint32_t* sbase_mask, int32_t* cnt, int32_t* offsets, int32_t* perm,
                                int32_t* active, int32_t* T, void* stream) {
     if (!logits || !idx || !w || !cnt || !offsets || !perm || !active || !T) return fail(MOE_EINVAL, "null pointer");
@@ -119,7 +120,8 @@ MOE_API int moe_route_dispatch(const float* logits, int B, int N, int k, int mod
     }
     const bool oea_like = mode != MOE_ROUTE_TOPK;
     return hip_status(moe::launch_route_dispatch(logits, B, N, k, mode, k0, p, mode == MOE_ROUTE_OEA ? max_p : N,
-                                                 renorm, n_valid, idx, w, oea_like ? n_base : nullptr,
+                                                 renorm, n_valid, oea_like ? k0_by_batch : nullptr, idx, w,
+                                                 oea_like ? n_base : nullptr,
                                                  oea_like ? sbase_mask : nullptr, cnt, offsets, perm, active, T,
                                                  as_stream(stream)),
                       "moe_route_dispatch");

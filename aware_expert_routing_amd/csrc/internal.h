@@ -19,7 +19,8 @@ hipError_t launch_route(const float* logits, int B, int N, int k, int k0, float 
                         int renorm, int32_t* idx, float* w, int32_t* n_base, uint32_t* mask,
                         int32_t* T, hipStream_t s);
 hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int mode, int k0, float p, int max_p,
-                                 int renorm, const int32_t* n_valid, int32_t* idx, float* w, int32_t* n_base,
+                                 int renorm, const int32_t* n_valid, const int32_t* k0_by_batch, int32_t* idx,
+                                 float* w, int32_t* n_base,
                                  uint32_t* mask, int32_t* cnt, int32_t* offsets, int32_t* perm, int32_t* active,
                                  int32_t* T, hipStream_t s);
 hipError_t launch_dispatch(const int32_t* idx, int B, int N, int k, int32_t* cnt,

@@ -286,13 +286,16 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
                                                      uint32_t* __restrict__ mask_out, int32_t* __restrict__ T_out,
                                                      int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm, int32_t* __restrict__ active,
-                                                     int pruned, int max_p, const int32_t* __restrict__ n_valid) {
+                                                     int pruned, int max_p, const int32_t* __restrict__ n_valid,
+                                                     const int32_t* __restrict__ k0_by_batch) {
     __shared__ uint32_t sbase[kMaxExperts / 32];
     __shared__ int sbase_count;
     __shared__ int n_l[kMaxBatch];
     __shared__ int32_t idx_l[kDispatch ? kMaxBatch * kMaxTopK : 1];
     // tokens at or past n_valid are padding: no experts, nothing added to S_base
     const int B_real = n_valid != nullptr ? min(max(*n_valid, 0), B) : B;
+    // batch-size-dependent k0, looked up on the device from the real batch size
+    if (kOea && k0_by_batch != nullptr) k0 = min(max(k0_by_batch[B_real], 1), k);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nwaves = blockDim.x / kWave;
@@ -539,26 +542,28 @@ hipError_t launch_route(const float* logits, int B, int N, int k, int k0, float 
     const int threads = kWave * (B < 16 ? B : 16);
     if (oea)
         route_kernel<true, false><<<1, threads, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, mask, T,
-                                                        nullptr, nullptr, nullptr, nullptr, 0, N, nullptr);
+                                                        nullptr, nullptr, nullptr, nullptr, 0, N, nullptr, nullptr);
     else
         route_kernel<false, false><<<1, threads, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w, nullptr,
                                                          nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
-                                                         N, nullptr);
+                                                         N, nullptr, nullptr);
     return hipGetLastError();
 }
 
 hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int mode, int k0, float p, int max_p,
-                                 int renorm, const int32_t* n_valid, int32_t* idx, float* w, int32_t* n_base,
+                                 int renorm, const int32_t* n_valid, const int32_t* k0_by_batch, int32_t* idx,
+                                 float* w, int32_t* n_base,
                                  uint32_t* mask, int32_t* cnt, int32_t* offsets, int32_t* perm, int32_t* active,
                                  int32_t* T, hipStream_t s) {
     const int threads = kWave * (B < 16 ? B : 16);
     if (mode != MOE_ROUTE_TOPK)
         route_kernel<true, true><<<1, threads, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, mask, T, cnt,
                                                        offsets, perm, active, mode == MOE_ROUTE_PRUNED, max_p,
-                                                       n_valid);
+                                                       n_valid, k0_by_batch);
     else
         route_kernel<false, true><<<1, threads, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w, nullptr,
-                                                        nullptr, T, cnt, offsets, perm, active, 0, N, n_valid);
+                                                        nullptr, T, cnt, offsets, perm, active, 0, N, n_valid,
+                                                        nullptr);
     return hipGetLastError();
 }
 

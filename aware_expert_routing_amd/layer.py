@@ -93,14 +93,17 @@ class MoELayer:
         return b
 
     def route(self, logits: torch.Tensor, mode: str, k0: int = 0, p: float = 1.0,
-              buf: Buffers | None = None, stream=None, max_p: int | None = None, n_valid=None) -> Buffers:
+              buf: Buffers | None = None, stream=None, max_p: int | None = None, n_valid=None,
+              k0_by_batch=None) -> Buffers:
         """Routing ("topk", "oea" or "pruned") and dispatch in one launch; n_valid
-        (device int32 [1]) marks trailing tokens as padding."""
+        (device int32 [1]) marks trailing tokens as padding; k0_by_batch (device
+        int32 [B+1], see k0_schedule) picks k0 from the real batch size."""
         B = logits.shape[0]
         buf = buf or self.buffers(B)
         if mode not in ("topk", "oea", "pruned"):
             raise ValueError(mode)
-        L.route_dispatch(logits, self.k, mode, k0, p, True, buf.route, buf.disp, stream, max_p, n_valid)
+        L.route_dispatch(logits, self.k, mode, k0, p, True, buf.route, buf.disp, stream, max_p, n_valid,
+                         k0_by_batch)
         return buf
 
     def ffn(self, x: torch.Tensor, buf: Buffers, stream=None) -> torch.Tensor:
@@ -109,18 +112,18 @@ class MoELayer:
 
     def forward(self, x: torch.Tensor, mode: str = "oea", k0: int = 3, p: float = 1.0,
                 logits: torch.Tensor | None = None, stream=None, max_p: int | None = None,
-                n_valid=None) -> Buffers:
+                n_valid=None, k0_by_batch=None) -> Buffers:
         """Whole layer.  If `logits` is given the router GEMV is skipped."""
         B = x.shape[0]
         buf = self.buffers(B)
         if logits is None:
             logits = L.router_logits(x, self.w_r, buf.logits, stream)
-        self.route(logits, mode, k0, p, buf, stream, max_p, n_valid)
+        self.route(logits, mode, k0, p, buf, stream, max_p, n_valid, k0_by_batch)
         self.ffn(x, buf, stream)
         return buf
 
     def capture(self, x: torch.Tensor, mode: str = "oea", k0: int = 3, p: float = 1.0,
-                max_p: int | None = None, n_valid=None) -> torch.cuda.CUDAGraph:
+                max_p: int | None = None, n_valid=None, k0_by_batch=None) -> torch.cuda.CUDAGraph:
         """Capture forward(x, ...) into a HIP graph (every kernel of the layer, no
         allocation or memset inside).  Replaying it recomputes the layer for
         whatever `x` and `n_valid` hold at replay time; results land in
@@ -129,11 +132,29 @@ class MoELayer:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):   # warm-up outside capture (allocates the buffers)
-            self.forward(x, mode, k0, p, max_p=max_p, n_valid=n_valid)
+            self.forward(x, mode, k0, p, max_p=max_p, n_valid=n_valid, k0_by_batch=k0_by_batch)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            self.forward(x, mode, k0, p, max_p=max_p, n_valid=n_valid)
+            self.forward(x, mode, k0, p, max_p=max_p, n_valid=n_valid, k0_by_batch=k0_by_batch)
         return graph
 
+
+def k0_schedule(k: int, B_max: int, steps: list[tuple[int, int]], device="cuda") -> torch.Tensor:
+    """Device table for moe_route_dispatch's k0_by_batch: entry b is the k0
+    for a batch of b real tokens.
+
+    Page "Opportunistic Expert Activation (OEA) - L2", section 6 notes:
+    piggybacking cannot help a single token, and the natural tuning axis is a
+    batch-size-dependent k0, larger (safer) at small B.  `steps` lists
+    (first batch size, k0) pairs in increasing batch size; batch sizes below
+    the first pair, and B = 1 always, use k0 = k (plain top-k routing).
+    """
+    table = [k] * (B_max + 1)
+    for b0, k0 in sorted(steps):
+        if not 1 <= k0 <= k:
+            raise ValueError("k0 must be in [1, k]")
+        for b in range(max(b0, 2), B_max + 1):
+            table[b] = k0
+    return torch.tensor(table, dtype=torch.int32, device=device)

@@ -161,6 +161,14 @@ int moe_dispatch(const int32_t *idx, int B, int N, int k, int32_t *cnt, int32_t 
  *             they get no experts (idx -1, w 0) and add nothing to S_base,
  *             so a fixed-size (e.g. graph-captured) batch serves smaller
  *             real batches without inflating T
+ *   k0_by_batch : NULL, or a device int32 [B+1] table for OEA and pruned
+ *             modes [OEA section 6 notes: piggybacking does nothing at B = 1
+ *             and the natural tuning axis is a batch-size-dependent k0,
+ *             larger at small B]: the call uses k0 = k0_by_batch[b] with b
+ *             the number of real tokens (*n_valid, else B), clamped to
+ *             [1, k]; the k0 argument then only bounds max_p's check.  The
+ *             table is read on the device, so a captured graph follows the
+ *             real batch size of each replay.
  *   Outputs as moe_route_oea (n_base, sbase_mask may be NULL; ignored for
  *   top-k) followed by moe_dispatch on idx; T = number of active experts
  *   (for OEA and pruned also |S_base|).  The routed pairs stay on chip
@@ -168,7 +176,8 @@ int moe_dispatch(const int32_t *idx, int B, int N, int k, int32_t *cnt, int32_t 
  */
 enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_OEA = 1, MOE_ROUTE_PRUNED = 2 };
 int moe_route_dispatch(const float *logits, int B, int N, int k, int mode, int k0, float p, int max_p,
-                       int renorm, const int32_t *n_valid, int32_t *idx, float *w, int32_t *n_base,
+                       int renorm, const int32_t *n_valid, const int32_t *k0_by_batch, int32_t *idx,
+                       float *w, int32_t *n_base,
                        uint32_t *sbase_mask, int32_t *cnt, int32_t *offsets, int32_t *perm, int32_t *active,
                        int32_t *T, void *stream);
 

@@ -149,7 +149,7 @@ def test_route_dispatch_rejects_bad_arguments():
     lib = moe.lib()
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("logits", FAKE), ("B", 16), ("N", 128), ("k", 8), ("mode", 1), ("k0", 3), ("p", 1.0), ("max_p", 128),
-        ("renorm", 1), ("n_valid", None), ("idx", FAKE), ("w", FAKE), ("n_base", None), ("mask", None),
+        ("renorm", 1), ("n_valid", None), ("k0_by_batch", None), ("idx", FAKE), ("w", FAKE), ("n_base", None), ("mask", None),
         ("cnt", FAKE), ("offsets", FAKE), ("perm", FAKE), ("active", FAKE), ("T", FAKE), ("stream", None))]
     assert lib.moe_route_dispatch(*args(mode=3)) == -1
     assert lib.moe_route_dispatch(*args(max_p=2)) == -1          # max_p < k0
@@ -279,3 +279,11 @@ def test_residency_create_rejects_bad_configs():
     assert "multiples of 128" in moe.lib().moe_last_error().decode()
     assert lib.moe_residency_step(None, None, 0) == -1
     assert lib.moe_residency_state(None, 0) == -1
+
+
+def test_k0_schedule_table():
+    t = moe.k0_schedule(8, 16, [(6, 3), (2, 5)], device="cpu").tolist()
+    assert len(t) == 17 and t[1] == 8 and t[2:6] == [5] * 4 and t[6:] == [3] * 11
+    assert moe.k0_schedule(8, 4, [(1, 2)], device="cpu").tolist() == [8, 8, 2, 2, 2]   # B = 1 stays top-k
+    with pytest.raises(ValueError):
+        moe.k0_schedule(8, 4, [(2, 9)], device="cpu")

@@ -47,3 +47,26 @@ def test_graph_replays_match_eager(mode, k0):
             torch.cuda.synchronize()
             assert int(alone.disp["T"].item()) == int(got["T"].item())
             assert torch.equal(alone.y, y_graph[:n_real])
+
+
+def test_graph_follows_the_batch_size_k0_table():
+    # one captured graph; each replay's real batch size selects k0 on the device
+    N, k, H, I, B = 32, 8, 512, 256, 16
+    layer, _ = build_layer(N, k, H, I, 12, fmt="bf16")
+    eager_layer, _ = build_layer(N, k, H, I, 12, fmt="bf16")
+    table = moe.k0_schedule(k, B, [(2, 5), (6, 3)], device=DEV)
+    tab = table.cpu().numpy()
+    x_static = _x(20, B, H).clone()
+    nv = torch.tensor([B], dtype=torch.int32, device=DEV)
+    graph = layer.capture(x_static, "oea", 1, 1.0, n_valid=nv, k0_by_batch=table)
+    for rep, (seed, n_real) in enumerate([(21, 16), (22, 1), (23, 4), (24, 9), (25, 16)]):
+        x_static.copy_(_x(seed, B, H))
+        nv.fill_(n_real)
+        graph.replay()
+        torch.cuda.synchronize()
+        y_graph = layer.buffers(B).y.clone()
+        T_graph = int(layer.buffers(B).disp["T"].item())
+        alone = eager_layer.forward(x_static[:n_real].clone(), "oea", int(tab[n_real]), 1.0)
+        torch.cuda.synchronize()
+        assert int(alone.disp["T"].item()) == T_graph, rep
+        assert torch.equal(alone.y, y_graph[:n_real]), rep

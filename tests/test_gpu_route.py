@@ -172,6 +172,30 @@ def test_route_variants_parity(B, N, k, mode, k0, p, max_p, nv, scale, zipf):
         assert int(disp["T"].item()) == dref["T"]
 
 
+@pytest.mark.parametrize("mode", ["oea", "pruned"])
+def test_batch_size_dependent_k0_table(mode):
+    # page OEA section 6 notes: k0 chosen from the real batch size (k at B = 1,
+    # larger at small B); the table is read on the device from n_valid
+    B, N, k = 32, 128, 8
+    table = moe.k0_schedule(k, B, [(2, 6), (8, 4), (24, 2)], device=DEV)
+    tab = table.cpu().numpy()
+    assert tab[1] == k and tab[2] == 6 and tab[7] == 6 and tab[8] == 4 and tab[24] == 2 and tab[32] == 2
+    for seed, nv in enumerate([1, 2, 5, 8, 17, 24, 32, None]):
+        l = _logits("normal", seed, B, N, 1.0, 1.1)
+        n_valid = None if nv is None else torch.tensor([nv], dtype=torch.int32, device=DEV)
+        route, disp = moe.route_dispatch(torch.from_numpy(l).to(DEV), k, mode, 1, 1.0, True, n_valid=n_valid,
+                                         k0_by_batch=table)
+        b = B if nv is None else nv
+        ref = oracle.route(l, k, oea=True, k0=int(tab[b]), p=1.0, pruned=(mode == "pruned"), n_valid=nv)
+        assert np.array_equal(route["idx"].cpu().numpy(), ref["idx"]), nv
+        assert np.abs(route["w"].cpu().numpy().astype(np.float64) - ref["w"]).max() <= 1e-6
+        assert np.array_equal(route["n_base"].cpu().numpy(), ref["n_base"])
+        dref = oracle.dispatch(ref["idx"], N)
+        for key in ("cnt", "offsets", "perm", "active"):
+            assert np.array_equal(disp[key].cpu().numpy(), dref[key]), key
+        assert int(disp["T"].item()) == dref["T"] == ref["T"]
+
+
 def test_dispatch_with_empty_slots_and_rows():
     B, N, k = 6, 16, 4
     idx = np.array([[3, 5, -1, -1], [-1, -1, -1, -1], [15, 0, 3, -1], [7, -1, -1, -1],
