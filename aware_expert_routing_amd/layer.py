@@ -145,7 +145,7 @@ def k0_schedule(k: int, B_max: int, steps: list[tuple[int, int]], device="cuda")
     """Device table for moe_route_dispatch's k0_by_batch: entry b is the k0
     for a batch of b real tokens.
 
-    Page "Opportunistic Expert Activation (OEA) - L2", section 6 notes:
+    Page "Opportunistic Expert Activation (OEA) - L2", section 7 implementation notes:
     piggybacking cannot help a single token, and the natural tuning axis is a
     batch-size-dependent k0, larger (safer) at small B.  `steps` lists
     (first batch size, k0) pairs in increasing batch size; batch sizes below

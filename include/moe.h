@@ -162,7 +162,7 @@ int moe_dispatch(const int32_t *idx, int B, int N, int k, int32_t *cnt, int32_t 
  *             so a fixed-size (e.g. graph-captured) batch serves smaller
  *             real batches without inflating T
  *   k0_by_batch : NULL, or a device int32 [B+1] table for OEA and pruned
- *             modes [OEA section 6 notes: piggybacking does nothing at B = 1
+ *             modes [OEA section 7 notes: piggybacking does nothing at B = 1
  *             and the natural tuning axis is a batch-size-dependent k0,
  *             larger at small B]: the call uses k0 = k0_by_batch[b] with b
  *             the number of real tokens (*n_valid, else B), clamped to

@@ -174,7 +174,7 @@ def test_route_variants_parity(B, N, k, mode, k0, p, max_p, nv, scale, zipf):
 
 @pytest.mark.parametrize("mode", ["oea", "pruned"])
 def test_batch_size_dependent_k0_table(mode):
-    # page OEA section 6 notes: k0 chosen from the real batch size (k at B = 1,
+    # page OEA section 7 notes: k0 chosen from the real batch size (k at B = 1,
     # larger at small B); the table is read on the device from n_valid
     B, N, k = 32, 128, 8
     table = moe.k0_schedule(k, B, [(2, 6), (8, 4), (24, 2)], device=DEV)
