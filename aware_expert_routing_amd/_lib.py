@@ -72,6 +72,7 @@ _SIGNATURES = [
     ("moe_dispatch", [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
     ("moe_route_dispatch", [_P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
      _I),
+    ("moe_router_route_dispatch", [_P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I] + [_P] * 14, _I),
     ("moe_ffn_workspace_bytes", [_I, _I, _I, _I], _S),
     ("moe_expert_ffn", [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _S, _P], _I),
     ("moe_handle_publish", [_P, _I, ctypes.POINTER(ExpertHandle), _P], _I),
@@ -230,6 +231,33 @@ def route_dispatch(logits, k: int, mode: str, k0: int = 0, p: float = 1.0, renor
         _ptr(disp["cnt"]), _ptr(disp["offsets"]), _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]),
         _stream(stream)))
     return route, disp
+
+
+def router_route_dispatch(x, w_r, k: int, mode: str, k0: int = 0, p: float = 1.0, renorm: bool = True,
+                          route=None, disp=None, logits=None, sync=None, stream=None, max_p: int | None = None,
+                          n_valid=None, k0_by_batch=None):
+    """Router logits, routing and dispatch in one launch.  sync: device int32
+    [1] that starts at zero (allocated here if None).  Returns (logits, route,
+    disp)."""
+    B, H = x.shape
+    N = w_r.shape[0]
+    dev = x.device
+    i32 = dict(device=dev, dtype=torch.int32)
+    logits = torch.empty(B, N, device=dev, dtype=torch.float32) if logits is None else logits
+    sync = torch.zeros(1, **i32) if sync is None else sync
+    if route is None:
+        route = dict(idx=torch.empty(B, k, **i32), w=torch.empty(B, k, device=dev, dtype=torch.float32),
+                     n_base=torch.empty(B, **i32), mask=torch.empty((N + 31) // 32, **i32))
+    if disp is None:
+        disp = dict(cnt=torch.empty(N, **i32), offsets=torch.empty(N + 1, **i32), perm=torch.empty(B * k, **i32),
+                    active=torch.empty(N, **i32), T=torch.empty(1, **i32))
+    m = {"topk": MOE_ROUTE_TOPK, "oea": MOE_ROUTE_OEA, "pruned": MOE_ROUTE_PRUNED}[mode]
+    _check("moe_router_route_dispatch", lib().moe_router_route_dispatch(
+        _ptr(x), _x_dtype(x), _ptr(w_r), B, H, N, k, m, int(k0), float(p), N if max_p is None else int(max_p),
+        int(bool(renorm)), _ptr(n_valid), _ptr(k0_by_batch), _ptr(logits), _ptr(route["idx"]), _ptr(route["w"]),
+        _ptr(route.get("n_base")), _ptr(route.get("mask")), _ptr(disp["cnt"]), _ptr(disp["offsets"]),
+        _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]), _ptr(sync), _stream(stream)))
+    return logits, route, disp
 
 
 def ffn_workspace_bytes(B: int, k: int, H: int, I: int) -> int:

@@ -127,6 +127,32 @@ MOE_API int moe_route_dispatch(const float* logits, int B, int N, int k, int mod
                       "moe_route_dispatch");
 }
 
+MOE_API int moe_router_route_dispatch(const void* x, int x_dtype, const float* w_r, int B, int H, int N, int k,
+                                      int mode, int k0, float p, int max_p, int renorm, const int32_t* n_valid,
+                                      const int32_t* k0_by_batch, float* logits, int32_t* idx, float* w,
+                                      int32_t* n_base, uint32_t* sbase_mask, int32_t* cnt, int32_t* offsets,
+                                      int32_t* perm, int32_t* active, int32_t* T, int32_t* sync, void* stream) {
+    if (!x || !w_r || !logits || !idx || !w || !cnt || !offsets || !perm || !active || !T || !sync)
+        return fail(MOE_EINVAL, "null pointer");
+    if (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16) return fail(MOE_EINVAL, "bad x_dtype");
+    if (H < 8 || H % 8) return fail(MOE_EINVAL, "H must be a positive multiple of 8");
+    int st = check_sizes(B, N, k);
+    if (st) return st;
+    if (mode != MOE_ROUTE_TOPK && mode != MOE_ROUTE_OEA && mode != MOE_ROUTE_PRUNED)
+        return fail(MOE_EINVAL, "bad routing mode");
+    if (mode != MOE_ROUTE_TOPK) {
+        if (k0 < 1 || k0 > k) return fail(MOE_EINVAL, "k0 must be in [1, k]");
+        if (!(p > 0.0f)) return fail(MOE_EINVAL, "p must be > 0 (p >= 1 disables top-p)");
+        if (mode == MOE_ROUTE_OEA && (max_p < k0 || max_p > N)) return fail(MOE_EINVAL, "max_p must be in [k0, N]");
+    }
+    const bool oea_like = mode != MOE_ROUTE_TOPK;
+    return hip_status(moe::launch_router_route_dispatch(x, x_dtype, w_r, B, H, N, k, mode, k0, p, max_p, renorm,
+                                                        n_valid, oea_like ? k0_by_batch : nullptr, logits, idx, w,
+                                                        oea_like ? n_base : nullptr, oea_like ? sbase_mask : nullptr,
+                                                        cnt, offsets, perm, active, T, sync, as_stream(stream)),
+                      "moe_router_route_dispatch");
+}
+
 MOE_API size_t moe_ffn_workspace_bytes(int B, int k, int H, int I) {
     if (B < 1 || k < 1 || H < 1 || I < 1) return 0;
     return moe::ffn_workspace_bytes(B, k, H, I);

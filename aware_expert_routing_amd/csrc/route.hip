@@ -106,63 +106,90 @@ __device__ __forceinline__ float wave_tree_sum(float x) {
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // Select up to `count` of the token's experts in rank order from the lane's
-// two candidate keys (0 = unavailable); a selected key is cleared by its
-// owner.  Results are uniform.  Stops early when nothing is left.
-__device__ __forceinline__ int select_ranked(uint32_t& o0, uint32_t& o1, int count, float (&selv)[kMaxTopK],
-                                             int (&selj)[kMaxTopK]) {
+// two candidate keys (0 = unavailable).  Nothing is gathered: the lane that
+// owns the r-th selection records r in slot0 / slot1 for its expert 2l /
+// 2l+1 and clears that key.  Returns the number selected (uniform) and, in
+// top_key, the first selected key.  With p_z > 0 the selection also stops
+// after the first rank at which the running sum of exp(l - l_top) in rank
+// order (fp32, one addition per rank) reaches p_z (the top-p count).
+__device__ __forceinline__ int select_marks(uint32_t& o0, uint32_t& o1, int count, int& slot0, int& slot1,
+                                            uint32_t& top_key, float p_z) {
     const int lane = threadIdx.x & (kWave - 1);
     int got = 0;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-        selv[r] = 0.0f;
-        selj[r] = -1;
-        if (r < count && got == r) {   // wave-uniform
-            const uint32_t m = wave_max_u32(max(o0, o1));
-            if (m != 0) {
-                const uint64_t holders = __ballot(o0 == m || o1 == m);
-                const int L = __ffsll(static_cast<unsigned long long>(holders)) - 1;
-                const uint32_t oL = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(o0), L));
-                const int j = 2 * L + (oL == m ? 0 : 1);
-                selv[r] = key_logit(m);
-                selj[r] = j;
-                if (lane == L) {
-                    if (j & 1) o1 = 0;
-                    else o0 = 0;
-                }
-                got = r + 1;
-            }
+    float c = 0.0f, top = 0.0f;
+    for (int r = 0; r < count; ++r) {   // wave-uniform trip count
+        const uint32_t m = wave_max_u32(max(o0, o1));
+        if (m == 0) break;
+        const uint64_t holders = __ballot(o0 == m || o1 == m);
+        const int L = __ffsll(static_cast<unsigned long long>(holders)) - 1;
+        const uint32_t oL = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(o0), L));
+        const bool first_of_lane = oL == m;   // expert 2L, else 2L+1
+        if (lane == L) {
+            if (first_of_lane) { slot0 = r; o0 = 0; }
+            else { slot1 = r; o1 = 0; }
+        }
+        got = r + 1;
+        if (r == 0) {
+            top_key = m;
+            top = key_logit(m);
+        }
+        if (p_z > 0.0f) {
+            c = c + route_exp(key_logit(m) - top);
+            if (c >= p_z) break;
         }
     }
     return got;
 }
 
-// Wavefront sum of doubles (any fixed order; used for weight denominators).
+// Wavefront sum of a double, returned uniform: DPP steps inside rows of 16
+// (quad pairs, quads, half rows, rows), then the four row sums through lane
+// reads.  Used for weight denominators, which are rounded to fp32 afterwards.
+template <int CTRL>
+__device__ __forceinline__ double dpp_move_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(b), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo));
+}
+__device__ __forceinline__ double lane_f64(double v, int l) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), l));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), l));
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+    v += dpp_move_f64<kQuadXor1>(v);
+    v += dpp_move_f64<kQuadXor2>(v);
+    v += dpp_move_f64<kHalfMirror>(v);
+    v += dpp_move_f64<kMirror>(v);
+    return (lane_f64(v, 0) + lane_f64(v, 16)) + (lane_f64(v, 32) + lane_f64(v, 48));
 }
 
-// Write the kept experts of one token: lane r < kept owns slot r, computes
-// e_r = exp(l_r - m) and w_r = e_r / sum_kept e (renorm) or e_r / Z (raw
-// softmax), the quotient in double rounded once to fp32; slots >= kept get
+// Write one token's selected experts: the lane owning the expert of slot r
+// writes idx[i k + r] and w[i k + r] = e / denom, e = exp(l - l_top); denom is
+// the sum of e over the kept experts (renorm) or Z (raw softmax).  The
+// quotient is taken in double and rounded once to fp32.  Slots got..k-1 get
 // expert -1 and weight 0.
-__device__ __forceinline__ void write_token(int lane, int i, int k, int kept, float m, bool renorm,
-                                            float Z, const float (&selv)[kMaxTopK],
-                                            const int (&selj)[kMaxTopK], int32_t* idx, float* w,
-                                            int32_t* idx_copy) {
-    float my_l = 0.0f;
-    int my_j = -1;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r)
-        if (lane == r) { my_l = selv[r]; my_j = selj[r]; }
-    const bool mine = lane < kept;
-    const double ev = mine ? static_cast<double>(route_exp(my_l - m)) : 0.0;
-    const double denom = renorm ? wave_sum_f64(ev) : static_cast<double>(Z);
-    if (lane < k) {
-        idx[i * k + lane] = mine ? my_j : -1;
-        if (idx_copy != nullptr) idx_copy[i * k + lane] = mine ? my_j : -1;
-        w[i * k + lane] = mine ? static_cast<float>(ev / denom) : 0.0f;
+__device__ __forceinline__ void write_marked(int lane, int i, int k, int got, int slot0, int slot1, float l0,
+                                             float l1, float top, bool renorm, float Z, int32_t* idx, float* w,
+                                             int32_t* idx_copy) {
+    const double ev0 = slot0 >= 0 ? static_cast<double>(route_exp(l0 - top)) : 0.0;
+    const double ev1 = slot1 >= 0 ? static_cast<double>(route_exp(l1 - top)) : 0.0;
+    const double denom = renorm ? wave_sum_f64(ev0 + ev1) : static_cast<double>(Z);
+    if (slot0 >= 0) {
+        idx[i * k + slot0] = 2 * lane;
+        if (idx_copy != nullptr) idx_copy[i * k + slot0] = 2 * lane;
+        w[i * k + slot0] = static_cast<float>(ev0 / denom);
+    }
+    if (slot1 >= 0) {
+        idx[i * k + slot1] = 2 * lane + 1;
+        if (idx_copy != nullptr) idx_copy[i * k + slot1] = 2 * lane + 1;
+        w[i * k + slot1] = static_cast<float>(ev1 / denom);
+    }
+    if (lane >= got && lane < k) {
+        idx[i * k + lane] = -1;
+        if (idx_copy != nullptr) idx_copy[i * k + lane] = -1;
+        w[i * k + lane] = 0.0f;
     }
 }
 
@@ -245,11 +272,7 @@ __device__ __forceinline__ void dispatch_block(const int32_t* idx, int B, int N,
     }
 }
 
-// Routing of a batch by one workgroup of min(B, 16) wavefronts, one token per
-// wavefront at a time.  kOea: OEA Phase 1, the union S_base (LDS bitmask
-// built with integer OR, independent of the order tokens finish), Phase 2;
-// otherwise vanilla top-k.  kDispatch: the same workgroup then dispatches
-// the routed pairs from LDS (one launch instead of two).
+// Slots of a token that routes nowhere (padding).
 __device__ __forceinline__ void write_empty(int lane, int i, int k, int32_t* idx, float* w, int32_t* idx_copy) {
     if (lane < k) {
         idx[i * k + lane] = -1;
@@ -279,15 +302,29 @@ __device__ __forceinline__ void kth_ranked(uint32_t o0, uint32_t o1, int kth, ui
     }
 }
 
-template <bool kOea, bool kDispatch>
-__global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ logits, int B, int N, int k,
-                                                     int k0, float p, int renorm, int32_t* __restrict__ idx,
-                                                     float* __restrict__ w, int32_t* __restrict__ n_base,
-                                                     uint32_t* __restrict__ mask_out, int32_t* __restrict__ T_out,
-                                                     int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ perm, int32_t* __restrict__ active,
-                                                     int pruned, int max_p, const int32_t* __restrict__ n_valid,
-                                                     const int32_t* __restrict__ k0_by_batch) {
+// Tokens per wavefront: B <= 128 tokens over up to 16 wavefronts.
+constexpr int kTokRounds = kMaxBatch / 16;
+
+template <bool kCoherent>
+__device__ __forceinline__ float load_logit(const float* p) {
+    if constexpr (kCoherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+
+// The routing of a whole batch by the calling workgroup (all of its waves).
+// Every wave first loads the logits of all of its tokens (one round trip),
+// keeps them in registers for both phases, then walks its tokens.
+// kCoherent: the logits were written by other workgroups of the same launch
+// and are read with device-scope loads.
+template <bool kOea, bool kDispatch, bool kCoherent>
+__device__ __forceinline__ void route_block(const float* __restrict__ logits, int B, int N, int k, int k0, float p,
+                                            int renorm, int32_t* __restrict__ idx, float* __restrict__ w,
+                                            int32_t* __restrict__ n_base, uint32_t* __restrict__ mask_out,
+                                            int32_t* __restrict__ T_out, int32_t* __restrict__ cnt,
+                                            int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                            int32_t* __restrict__ active, int pruned, int max_p,
+                                            const int32_t* __restrict__ n_valid,
+                                            const int32_t* __restrict__ k0_by_batch) {
     __shared__ uint32_t sbase[kMaxExperts / 32];
     __shared__ int sbase_count;
     __shared__ int n_l[kMaxBatch];
@@ -301,14 +338,27 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
     const int nwaves = blockDim.x / kWave;
     const int e0 = 2 * lane, e1 = 2 * lane + 1;
     if (threadIdx.x < kMaxExperts / 32) sbase[threadIdx.x] = 0u;
+
+    float L0[kTokRounds], L1[kTokRounds];
+#pragma unroll
+    for (int r = 0; r < kTokRounds; ++r) {
+        const int i = wave + r * nwaves;
+        L0[r] = kNegInf;
+        L1[r] = kNegInf;
+        if (i < B_real) {
+            if (e0 < N) L0[r] = load_logit<kCoherent>(logits + i * N + e0);
+            if (e1 < N) L1[r] = load_logit<kCoherent>(logits + i * N + e1);
+        }
+    }
     __syncthreads();
 
-    float selv[kMaxTopK];
-    int selj[kMaxTopK];
     int32_t* idx_copy = kDispatch ? idx_l : nullptr;
 
     // Vanilla top-k, or OEA Phase 1.
-    for (int i = wave; i < B; i += nwaves) {
+#pragma unroll 1
+    for (int r = 0; r < kTokRounds; ++r) {
+        const int i = wave + r * nwaves;
+        if (i >= B) break;
         if (i >= B_real) {
             if (!kOea) write_empty(lane, i, k, idx, w, idx_copy);
             else if (lane == 0) {
@@ -318,44 +368,31 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
             continue;
         }
         const bool v0 = e0 < N, v1 = e1 < N;
-        const float l0 = v0 ? logits[i * N + e0] : kNegInf;
-        const float l1 = v1 ? logits[i * N + e1] : kNegInf;
+        const float l0 = L0[r], l1 = L1[r];
         uint32_t key0 = v0 ? order_key(l0) : 0u;
         uint32_t key1 = v1 ? order_key(l1) : 0u;
         const bool need_z = kOea ? (p < 1.0f) : (renorm == 0);
-        const int first = kOea ? k0 : k;
-        const int kept = select_ranked(key0, key1, first, selv, selj);
-        const float m = selv[0];   // the top logit
         float Z = 0.0f;
-        if (need_z) {
+        if (need_z) {   // normaliser over all experts, relative to the top logit
+            const float m = key_logit(wave_max_u32(max(key0, key1)));
             const float s0 = v0 ? route_exp(l0 - m) : 0.0f;
             const float s1 = v1 ? route_exp(l1 - m) : 0.0f;
             Z = wave_tree_sum(s0 + s1);
         }
+        int slot0 = -1, slot1 = -1;
+        uint32_t top_key = 0u;
+        const float p_z = (kOea && p < 1.0f) ? p * Z : 0.0f;
+        const int got = select_marks(key0, key1, kOea ? k0 : k, slot0, slot1, top_key, p_z);
         if (!kOea) {
-            write_token(lane, i, k, kept, m, renorm != 0, Z, selv, selj, idx, w, idx_copy);
+            write_marked(lane, i, k, got, slot0, slot1, l0, l1, key_logit(top_key), renorm != 0, Z, idx, w,
+                         idx_copy);
         } else {
-            int n = kept;
-            if (p < 1.0f) {
-                const float pz = p * Z;
-                float c = 0.0f;
-                bool reached = false;
-#pragma unroll
-                for (int r = 0; r < kMaxTopK; ++r) {
-                    if (r < kept && !reached) {
-                        c = c + route_exp(selv[r] - m);
-                        if (c >= pz) { n = r + 1; reached = true; }
-                    }
-                }
-            }
             if (lane == 0) {
-                n_l[i] = n;
-                if (n_base != nullptr) n_base[i] = n;
+                n_l[i] = got;
+                if (n_base != nullptr) n_base[i] = got;
             }
-#pragma unroll
-            for (int r = 0; r < kMaxTopK; ++r) {
-                if (r < n && lane == r) atomicOr(&sbase[selj[r] >> 5], 1u << (selj[r] & 31));
-            }
+            if (slot0 >= 0) atomicOr(&sbase[e0 >> 5], 1u << (e0 & 31));
+            if (slot1 >= 0) atomicOr(&sbase[e1 >> 5], 1u << (e1 & 31));
         }
     }
     if constexpr (kOea) {
@@ -376,13 +413,15 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
         // S_base), then lower-ranked experts that other tokens already
         // activated.  With max_p < N only the token's top-max_p ranks may be
         // taken; pruned keeps the baseline alone (its n_i experts).
-        for (int i = wave; i < B; i += nwaves) {
+#pragma unroll 1
+        for (int r = 0; r < kTokRounds; ++r) {
+            const int i = wave + r * nwaves;
+            if (i >= B) break;
             if (i >= B_real) {
                 write_empty(lane, i, k, idx, w, idx_copy);
                 continue;
             }
-            const float l0 = e0 < N ? logits[i * N + e0] : kNegInf;
-            const float l1 = e1 < N ? logits[i * N + e1] : kNegInf;
+            const float l0 = L0[r], l1 = L1[r];
             bool a0 = e0 < N && ((sbase[e0 >> 5] >> (e0 & 31)) & 1u);
             bool a1 = e1 < N && ((sbase[e1 >> 5] >> (e1 & 31)) & 1u);
             if (!pruned && max_p < N) {
@@ -395,14 +434,33 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
             }
             uint32_t key0 = a0 ? order_key(l0) : 0u;
             uint32_t key1 = a1 ? order_key(l1) : 0u;
-            const int kept = select_ranked(key0, key1, pruned ? n_l[i] : keep, selv, selj);
-            write_token(lane, i, k, kept, selv[0], true, 0.0f, selv, selj, idx, w, idx_copy);
+            int slot0 = -1, slot1 = -1;
+            uint32_t top_key = 0u;
+            const int got = select_marks(key0, key1, pruned ? n_l[i] : keep, slot0, slot1, top_key, 0.0f);
+            write_marked(lane, i, k, got, slot0, slot1, l0, l1, key_logit(top_key), true, 0.0f, idx, w, idx_copy);
         }
     }
     if constexpr (kDispatch) {
         __syncthreads();
         dispatch_block(idx_l, B, N, k, cnt, offsets, perm, active, T_out);
     }
+}
+
+// Routing of a batch by one workgroup of min(B, 16) wavefronts.  kOea: OEA
+// Phase 1, the union S_base (LDS bitmask built with integer OR, independent
+// of the order tokens finish), Phase 2; otherwise vanilla top-k.  kDispatch:
+// the same workgroup then dispatches the routed pairs from LDS.
+template <bool kOea, bool kDispatch>
+__global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ logits, int B, int N, int k,
+                                                     int k0, float p, int renorm, int32_t* __restrict__ idx,
+                                                     float* __restrict__ w, int32_t* __restrict__ n_base,
+                                                     uint32_t* __restrict__ mask_out, int32_t* __restrict__ T_out,
+                                                     int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ active,
+                                                     int pruned, int max_p, const int32_t* __restrict__ n_valid,
+                                                     const int32_t* __restrict__ k0_by_batch) {
+    route_block<kOea, kDispatch, false>(logits, B, N, k, k0, p, renorm, idx, w, n_base, mask_out, T_out, cnt,
+                                        offsets, perm, active, pruned, max_p, n_valid, k0_by_batch);
 }
 
 // Dispatch on its own (idx from global memory).
@@ -452,6 +510,68 @@ __device__ __forceinline__ float row16_sum_f(float v) {
     return v;
 }
 
+// Logits of expert e for tokens t0 .. t0 + nt - 1 by one group of
+// kGemvThreads threads (tid = the thread's index in the group): partial sums
+// per row of 16 lanes land in part[row][token]; the caller sums the rows.
+template <typename XT>
+__device__ __forceinline__ void gemv_expert(const XT* __restrict__ x, const float* __restrict__ w_r, int H, int e,
+                                            int t0, int nt, int tid, float (*part)[kGemvTok]) {
+    // activations stay in their storage format until the multiply (bf16: 4
+    // registers per token per 8 columns); fp32 activations go 8 tokens at a time
+    constexpr int kGroup = sizeof(XT) == 2 ? kGemvTok : kGemvTok / 2;
+    constexpr int kRaw = sizeof(XT) == 2 ? 1 : 2;   // 16-byte chunks per 8 columns
+    const int lane = tid & (kWave - 1);
+    const int col0 = 8 * lane + 512 * (tid / kWave);     // this lane's first column
+    const int stride = 8 * kGemvThreads;                  // 2048 columns per sweep
+    const float* wrow = w_r + static_cast<size_t>(e) * H;
+    float acc[kGemvTok];
+#pragma unroll
+    for (int t = 0; t < kGemvTok; ++t) acc[t] = 0.0f;
+    for (int c = col0; c < H; c += stride) {
+        float wv[8];
+        load_x8<float>(wrow + c, wv);
+#pragma unroll
+        for (int g0 = 0; g0 < kGemvTok; g0 += kGroup) {
+            uint4 raw[kGroup][kRaw];
+#pragma unroll
+            for (int t = 0; t < kGroup; ++t)
+                if (g0 + t < nt)
+#pragma unroll
+                    for (int q = 0; q < kRaw; ++q)
+                        raw[t][q] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t0 + g0 + t) * H + c +
+                                                                     4 * q);
+#pragma unroll
+            for (int t = 0; t < kGroup; ++t) {
+                if (g0 + t >= nt) continue;
+                float xv[8];
+                if constexpr (sizeof(XT) == 2) {
+                    const uint32_t u[4] = {raw[t][0].x, raw[t][0].y, raw[t][0].z, raw[t][0].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        xv[2 * q] = __uint_as_float(u[q] << 16);
+                        xv[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        xv[4 * q] = __uint_as_float(raw[t][q].x);
+                        xv[4 * q + 1] = __uint_as_float(raw[t][q].y);
+                        xv[4 * q + 2] = __uint_as_float(raw[t][q].z);
+                        xv[4 * q + 3] = __uint_as_float(raw[t][q].w);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[g0 + t] = __builtin_fmaf(wv[q], xv[q], acc[g0 + t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kGemvTok; ++t) {
+        const float sum = row16_sum_f(acc[t]);
+        if ((tid & 15) == 0) part[tid / 16][t] = sum;
+    }
+}
+
 template <typename XT>
 __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(const XT* __restrict__ x,
                                                                      const float* __restrict__ w_r,
@@ -460,42 +580,70 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(const XT* _
     __shared__ float part[kGemvThreads / 16][kGemvTok];   // [row of 16 lanes][token]
     const int e = blockIdx.x;
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int col0 = 8 * lane + 512 * (tid / kWave);     // this lane's first column
-    const int stride = 8 * kGemvThreads;                  // 2048 columns per sweep
-    const float* wrow = w_r + static_cast<size_t>(e) * H;
     for (int t0 = blockIdx.y * kGemvTok; t0 < B; t0 += gridDim.y * kGemvTok) {
         const int nt = min(kGemvTok, B - t0);
-        float acc[kGemvTok];
-#pragma unroll
-        for (int t = 0; t < kGemvTok; ++t) acc[t] = 0.0f;
-        for (int c = col0; c < H; c += stride) {
-            float wv[8];
-            load_x8<float>(wrow + c, wv);
-            float xv[kGemvTok][8];
-#pragma unroll
-            for (int t = 0; t < kGemvTok; ++t)
-                if (t < nt) load_x8<XT>(x + static_cast<size_t>(t0 + t) * H + c, xv[t]);
-#pragma unroll
-            for (int t = 0; t < kGemvTok; ++t)
-                if (t < nt)
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) acc[t] = __builtin_fmaf(wv[q], xv[t][q], acc[t]);
-        }
-#pragma unroll
-        for (int t = 0; t < kGemvTok; ++t) {
-            const float s = row16_sum_f(acc[t]);
-            if ((tid & 15) == 0) part[tid / 16][t] = s;
-        }
+        gemv_expert<XT>(x, w_r, H, e, t0, nt, tid, part);
         __syncthreads();
         if (tid < nt) {
-            float s = 0.0f;
+            float sum = 0.0f;
 #pragma unroll
-            for (int r = 0; r < kGemvThreads / 16; ++r) s += part[r][tid];
-            logits[static_cast<size_t>(t0 + tid) * N + e] = s;
+            for (int r = 0; r < kGemvThreads / 16; ++r) sum += part[r][tid];
+            logits[static_cast<size_t>(t0 + tid) * N + e] = sum;
         }
         __syncthreads();
     }
+}
+
+// Router logits, routing and dispatch in one launch.  Workgroup (gx, gy)
+// computes the logits of experts kFusedExperts gx .. + kFusedExperts - 1 for
+// tokens 16 gy .. 16 gy + 15 (one group of kGemvThreads threads per expert,
+// as router_logits_kernel), writes them with device-scope stores, waits for
+// those stores and counts itself done.  The workgroup that completes the
+// count routes and dispatches the whole batch (its 16 wavefronts, one token
+// per wavefront at a time), reading the logits with device-scope loads, and
+// clears the count for the next call.  No workgroup waits for another.
+constexpr int kFusedExperts = 4;
+
+__device__ __forceinline__ void wait_vmem() {   // s_waitcnt vmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <typename XT, bool kOea>
+__global__ __launch_bounds__(kGemvThreads * kFusedExperts) void router_route_kernel(
+        const XT* __restrict__ x, const float* __restrict__ w_r, int B, int H, int N, float* __restrict__ logits,
+        int k, int k0, float p, int renorm, int32_t* __restrict__ idx, float* __restrict__ w,
+        int32_t* __restrict__ n_base, uint32_t* __restrict__ mask_out, int32_t* __restrict__ T_out,
+        int32_t* __restrict__ cnt, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+        int32_t* __restrict__ active, int pruned, int max_p, const int32_t* __restrict__ n_valid,
+        const int32_t* __restrict__ k0_by_batch, int32_t* __restrict__ sync) {
+    __shared__ float part[kFusedExperts][kGemvThreads / 16][kGemvTok];
+    __shared__ int last_s;
+    const int g = threadIdx.x / kGemvThreads;
+    const int tid = threadIdx.x - g * kGemvThreads;
+    const int e = blockIdx.x * kFusedExperts + g;
+    const int t0 = blockIdx.y * kGemvTok;
+    const int nt = min(kGemvTok, B - t0);
+    if (e < N) gemv_expert<XT>(x, w_r, H, e, t0, nt, tid, part[g]);
+    __syncthreads();
+    if (e < N && tid < nt) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < kGemvThreads / 16; ++r) sum += part[g][r][tid];
+        __hip_atomic_store(logits + static_cast<size_t>(t0 + tid) * N + e, sum, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last_s = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 static_cast<int>(gridDim.x * gridDim.y) - 1;
+    __syncthreads();
+    if (!last_s) return;
+    route_block<kOea, true, true>(logits, B, N, k, k0, p, kOea ? 1 : renorm, idx, w, n_base, mask_out, T_out, cnt,
+                                  offsets, perm, active, pruned, max_p, n_valid, k0_by_batch);
+    if (threadIdx.x == 0) __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void hotness_kernel(float* S, const int32_t* cnt, int N, float alpha) {
@@ -564,6 +712,40 @@ hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int m
         route_kernel<false, true><<<1, threads, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w, nullptr,
                                                         nullptr, T, cnt, offsets, perm, active, 0, N, n_valid,
                                                         nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_route_dispatch(const void* x, int x_dtype, const float* w_r, int B, int H, int N, int k,
+                                        int mode, int k0, float p, int max_p, int renorm, const int32_t* n_valid,
+                                        const int32_t* k0_by_batch, float* logits, int32_t* idx, float* w,
+                                        int32_t* n_base, uint32_t* mask, int32_t* cnt, int32_t* offsets,
+                                        int32_t* perm, int32_t* active, int32_t* T, int32_t* sync, hipStream_t s) {
+    const dim3 grid((N + kFusedExperts - 1) / kFusedExperts, (B + kGemvTok - 1) / kGemvTok);
+    const int threads = kGemvThreads * kFusedExperts;
+    const bool oea = mode != MOE_ROUTE_TOPK;
+    const int pruned = mode == MOE_ROUTE_PRUNED;
+    const int mp = mode == MOE_ROUTE_OEA ? max_p : N;
+    if (x_dtype == MOE_DT_BF16) {
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        if (oea)
+            router_route_kernel<uint16_t, true><<<grid, threads, 0, s>>>(
+                xb, w_r, B, H, N, logits, k, k0, p, 1, idx, w, n_base, mask, T, cnt, offsets, perm, active, pruned, mp,
+                n_valid, k0_by_batch, sync);
+        else
+            router_route_kernel<uint16_t, false><<<grid, threads, 0, s>>>(
+                xb, w_r, B, H, N, logits, k, k, 1.0f, renorm, idx, w, nullptr, nullptr, T, cnt, offsets, perm, active,
+                0, N, n_valid, nullptr, sync);
+    } else {
+        const float* xf = static_cast<const float*>(x);
+        if (oea)
+            router_route_kernel<float, true><<<grid, threads, 0, s>>>(
+                xf, w_r, B, H, N, logits, k, k0, p, 1, idx, w, n_base, mask, T, cnt, offsets, perm, active, pruned, mp,
+                n_valid, k0_by_batch, sync);
+        else
+            router_route_kernel<float, false><<<grid, threads, 0, s>>>(
+                xf, w_r, B, H, N, logits, k, k, 1.0f, renorm, idx, w, nullptr, nullptr, T, cnt, offsets, perm, active,
+                0, N, n_valid, nullptr, sync);
+    }
     return hipGetLastError();
 }
 

@@ -88,7 +88,8 @@ class MoELayer:
                         perm=torch.empty(B * k, **i32), active=torch.empty(N, **i32), T=torch.empty(1, **i32))
             ws = torch.zeros(L.ffn_workspace_bytes(B, k, self.H, self.I), device=dev, dtype=torch.uint8)
             b = Buffers(B, torch.empty(B, N, device=dev, dtype=torch.float32), route, disp,
-                        torch.empty(B, self.H, device=dev, dtype=torch.float32), ws)
+                        torch.empty(B, self.H, device=dev, dtype=torch.float32), ws,
+                        {"sync": torch.zeros(1, **i32)})
             self._bufs[B] = b
         return b
 
@@ -113,12 +114,17 @@ class MoELayer:
     def forward(self, x: torch.Tensor, mode: str = "oea", k0: int = 3, p: float = 1.0,
                 logits: torch.Tensor | None = None, stream=None, max_p: int | None = None,
                 n_valid=None, k0_by_batch=None) -> Buffers:
-        """Whole layer.  If `logits` is given the router GEMV is skipped."""
+        """Whole layer.  If `logits` is given the router GEMV is skipped;
+        otherwise router, routing and dispatch run as one launch."""
         B = x.shape[0]
         buf = self.buffers(B)
         if logits is None:
-            logits = L.router_logits(x, self.w_r, buf.logits, stream)
-        self.route(logits, mode, k0, p, buf, stream, max_p, n_valid, k0_by_batch)
+            if mode not in ("topk", "oea", "pruned"):
+                raise ValueError(mode)
+            L.router_route_dispatch(x, self.w_r, self.k, mode, k0, p, True, buf.route, buf.disp, buf.logits,
+                                    buf.extra["sync"], stream, max_p, n_valid, k0_by_batch)
+        else:
+            self.route(logits, mode, k0, p, buf, stream, max_p, n_valid, k0_by_batch)
         self.ffn(x, buf, stream)
         return buf
 

@@ -166,8 +166,9 @@ def main():
             lay = layers[i % len(layers)]
             x = xs[i % len(xs)]
             buf = lay.buffers(B)
-            moe.router_logits(x, lay.w_r, buf.logits)
-            lay.route(buf.logits, mode, k0, 1.0, buf)
+            # router GEMV + routing + dispatch: one launch
+            moe.router_route_dispatch(x, lay.w_r, k, mode, k0, 1.0, True, buf.route, buf.disp, buf.logits,
+                                      buf.extra["sync"])
             if timed:
                 ev0[i].record(stream)
             lay.ffn(x, buf)

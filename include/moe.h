@@ -181,6 +181,26 @@ int moe_route_dispatch(const float *logits, int B, int N, int k, int mode, int k
                        uint32_t *sbase_mask, int32_t *cnt, int32_t *offsets, int32_t *perm, int32_t *active,
                        int32_t *T, void *stream);
 
+/*
+ * Router logits, routing and dispatch in one launch [OEA section 2 Q1: the
+ * router scores every expert for every token; then as moe_route_dispatch].
+ *   x, x_dtype, w_r, H : as moe_router_logits; logits [B, N] fp32 receives
+ *                        the router output (the routing decisions use it)
+ *   the remaining arguments are those of moe_route_dispatch, plus
+ *   sync : device int32 [1], zero before the first call; every call leaves
+ *          it at zero.  Calls sharing a sync word must be ordered (e.g. on
+ *          one stream).
+ * The launch's workgroups each compute a slice of the logits; the one that
+ * finishes last routes and dispatches the batch, so no workgroup waits.
+ * Requires H a positive multiple of 8, plus the conditions of
+ * moe_route_dispatch.
+ */
+int moe_router_route_dispatch(const void *x, int x_dtype, const float *w_r, int B, int H, int N, int k, int mode,
+                              int k0, float p, int max_p, int renorm, const int32_t *n_valid,
+                              const int32_t *k0_by_batch, float *logits, int32_t *idx, float *w,
+                              int32_t *n_base, uint32_t *sbase_mask, int32_t *cnt, int32_t *offsets,
+                              int32_t *perm, int32_t *active, int32_t *T, int32_t *sync, void *stream);
+
 /* Workspace bytes moe_expert_ffn needs for these sizes (host call). */
 size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
 

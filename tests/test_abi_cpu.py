@@ -287,3 +287,14 @@ def test_k0_schedule_table():
     assert moe.k0_schedule(8, 4, [(1, 2)], device="cpu").tolist() == [8, 8, 2, 2, 2]   # B = 1 stays top-k
     with pytest.raises(ValueError):
         moe.k0_schedule(8, 4, [(2, 9)], device="cpu")
+
+
+def test_binding_arity_matches_the_headers():
+    # every ctypes signature passes exactly the parameters the header declares
+    text = "".join(open(h).read() for h in HEADERS)
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    from aware_expert_routing_amd import _lib
+    for name, args, _ in _lib._SIGNATURES:
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", text)
+        params = [a for a in m.group(1).split(",") if a.strip() and a.strip() != "void"]
+        assert len(params) == len(args), name

@@ -259,3 +259,36 @@ def test_handle_publish_writes_the_record():
     rec = table.cpu().numpy()[2 * 64:3 * 64].tobytes()
     assert rec == bytes(h)
     assert np.all(table.cpu().numpy()[:128] == 0)
+
+
+@pytest.mark.parametrize("B,N,H,k,mode,k0,p,nv,dtype", [
+    (16, 128, 2048, 8, "oea", 3, 1.0, None, "bf16"),
+    (16, 128, 2048, 8, "topk", 0, 1.0, None, "bf16"),
+    (1, 128, 2048, 8, "oea", 3, 1.0, None, "bf16"),
+    (37, 128, 2048, 8, "oea", 5, 0.7, None, "bf16"),       # three token groups, ragged
+    (128, 128, 2048, 8, "pruned", 3, 1.0, 100, "bf16"),
+    (128, 128, 4096, 8, "oea", 5, 1.0, None, "bf16"),      # two sweeps of the hidden dimension
+    (6, 22, 520, 4, "oea", 2, 0.9, 4, "f32"),              # N not a multiple of 4, fp32 activations
+])
+def test_fused_router_route_dispatch(B, N, H, k, mode, k0, p, nv, dtype):
+    # one launch: router GEMV slices, then the last workgroup routes and
+    # dispatches; same logits as moe_router_logits bit for bit, routing as the
+    # oracle's on those logits; the sync word is left at zero for the next call
+    x = synth.activations(40 + B, B, H)
+    wr = torch.from_numpy(synth.router_weight(40, N, H)).to(DEV)
+    xd = bf16_dev(synth.to_bf16_bits(x)) if dtype == "bf16" else torch.from_numpy(x).to(DEV)
+    sync = torch.zeros(1, dtype=torch.int32, device=DEV)
+    n_valid = None if nv is None else torch.tensor([nv], dtype=torch.int32, device=DEV)
+    for rep in range(3):
+        logits, route, disp = moe.router_route_dispatch(xd, wr, k, mode, k0, p, True, sync=sync, n_valid=n_valid)
+        torch.cuda.synchronize()
+        assert int(sync.item()) == 0
+        assert torch.equal(logits, moe.router_logits(xd, wr))
+        l = logits.cpu().numpy()
+        ref = oracle.route(l, k, oea=(mode != "topk"), k0=k0, p=p, pruned=(mode == "pruned"), n_valid=nv)
+        assert np.array_equal(route["idx"].cpu().numpy(), ref["idx"]), rep
+        assert np.abs(route["w"].cpu().numpy().astype(np.float64) - ref["w"]).max() <= 1e-6
+        dref = oracle.dispatch(ref["idx"], N)
+        for key in ("cnt", "offsets", "perm", "active"):
+            assert np.array_equal(disp[key].cpu().numpy(), dref[key]), key
+        assert int(disp["T"].item()) == dref["T"]
