@@ -9,11 +9,14 @@
 //   section 4      Eq. 2: cnt_i per expert and T = #{i : cnt_i > 0}.
 // Page "DynaExq" section 2.5: hotness score S <- alpha S + (1 - alpha) c.
 //
-// Layout on the GPU: one wavefront per token, lane l owns experts 2l and 2l+1
-// (N <= 128), so the softmax normaliser is an xor butterfly over 64 lanes
-// and every selection step is one wavefront argmax.  S_base is a 128-bit set
-// in LDS built with integer OR, so its value does not depend on the order in
-// which tokens finish.
+// Layout on the GPU: one row of 16 lanes per token (four tokens per
+// wavefront); lane l of a row owns experts 8l .. 8l+7 (N <= 128).  A
+// selection step is a lane-local maximum over 8 keys and a 4-step DPP
+// maximum inside the row, so the four tokens of a wavefront select together;
+// the softmax normaliser is a 3-level lane-local tree followed by 4 DPP
+// levels, the balanced pairwise tree over 128 slots.  S_base is a 128-bit
+// set in LDS built with integer OR, so its value does not depend on the
+// order in which tokens finish.
 //
 // Floating-point contraction is off in this file: the top-p decision must be
 // reproducible bit for bit, so every fused multiply-add is written out.
@@ -75,75 +78,10 @@ __device__ __forceinline__ uint32_t dpp32(uint32_t old, uint32_t v) {
         __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROWS, 0xF, false));
 }
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
-constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
-
-// Wavefront maximum of a 32-bit key; returned uniform (read from lane 63).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, dpp32<kQuadXor1, 0xF>(v, v));
-    v = max(v, dpp32<kQuadXor2, 0xF>(v, v));
-    v = max(v, dpp32<kHalfMirror, 0xF>(v, v));
-    v = max(v, dpp32<kMirror, 0xF>(v, v));
-    v = max(v, dpp32<kRowBcast15, 0xA>(v, v));   // rows 1, 3 take rows 0, 2
-    v = max(v, dpp32<kRowBcast31, 0xC>(v, v));   // rows 2, 3 take row 1
-    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
-}
-
-// Normaliser Z from the lane sums of experts (2l, 2l+1).  The DPP steps pair
-// lanes (l, l^1), then quads, then 8-lane and 16-lane halves, then rows 0+1
-// and 2+3, then the two halves of the wave: exactly the balanced pairwise
-// tree over 128 slots in expert order (fp32 addition is commutative).
-__device__ __forceinline__ float wave_tree_sum(float x) {
-    uint32_t s = __float_as_uint(x);
-    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kQuadXor1, 0xF>(s, s)));
-    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kQuadXor2, 0xF>(s, s)));
-    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kHalfMirror, 0xF>(s, s)));
-    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kMirror, 0xF>(s, s)));
-    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kRowBcast15, 0xA>(s, s)));  // rows 1, 3
-    s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kRowBcast31, 0xC>(s, s)));  // row 3
-    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(s), 63)));
-}
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
-// Select up to `count` of the token's experts in rank order from the lane's
-// two candidate keys (0 = unavailable).  Nothing is gathered: the lane that
-// owns the r-th selection records r in slot0 / slot1 for its expert 2l /
-// 2l+1 and clears that key.  Returns the number selected (uniform) and, in
-// top_key, the first selected key.  With p_z > 0 the selection also stops
-// after the first rank at which the running sum of exp(l - l_top) in rank
-// order (fp32, one addition per rank) reaches p_z (the top-p count).
-__device__ __forceinline__ int select_marks(uint32_t& o0, uint32_t& o1, int count, int& slot0, int& slot1,
-                                            uint32_t& top_key, float p_z) {
-    const int lane = threadIdx.x & (kWave - 1);
-    int got = 0;
-    float c = 0.0f, top = 0.0f;
-    for (int r = 0; r < count; ++r) {   // wave-uniform trip count
-        const uint32_t m = wave_max_u32(max(o0, o1));
-        if (m == 0) break;
-        const uint64_t holders = __ballot(o0 == m || o1 == m);
-        const int L = __ffsll(static_cast<unsigned long long>(holders)) - 1;
-        const uint32_t oL = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(o0), L));
-        const bool first_of_lane = oL == m;   // expert 2L, else 2L+1
-        if (lane == L) {
-            if (first_of_lane) { slot0 = r; o0 = 0; }
-            else { slot1 = r; o1 = 0; }
-        }
-        got = r + 1;
-        if (r == 0) {
-            top_key = m;
-            top = key_logit(m);
-        }
-        if (p_z > 0.0f) {
-            c = c + route_exp(key_logit(m) - top);
-            if (c >= p_z) break;
-        }
-    }
-    return got;
-}
-
-// Wavefront sum of a double, returned uniform: DPP steps inside rows of 16
-// (quad pairs, quads, half rows, rows), then the four row sums through lane
-// reads.  Used for weight denominators, which are rounded to fp32 afterwards.
 template <int CTRL>
 __device__ __forceinline__ double dpp_move_f64(double v) {
     const uint64_t b = __builtin_bit_cast(uint64_t, v);
@@ -157,39 +95,211 @@ __device__ __forceinline__ double lane_f64(double v, int l) {
     const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), l));
     return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
-__device__ __forceinline__ double wave_sum_f64(double v) {
-    v += dpp_move_f64<kQuadXor1>(v);
-    v += dpp_move_f64<kQuadXor2>(v);
-    v += dpp_move_f64<kHalfMirror>(v);
-    v += dpp_move_f64<kMirror>(v);
-    return (lane_f64(v, 0) + lane_f64(v, 16)) + (lane_f64(v, 32) + lane_f64(v, 48));
+
+// A token is handled by a group of G lanes: G = 64 (a whole wavefront, two
+// experts per lane; the lowest latency, for small batches) or G = 16 (a row,
+// eight experts per lane, four tokens per wavefront; for large batches).
+// Lane l of a group owns experts kPer l .. kPer l + kPer - 1.  Reductions
+// give their result in every lane of the group.
+template <int G>
+struct Grp;
+
+template <>
+struct Grp<16> {
+    static constexpr int kPer = kMaxExperts / 16;
+    static constexpr int kPerWave = kWave / 16;
+    static constexpr int kRounds = kMaxBatch / (16 * kPerWave);   // 16 wavefronts cover 128 tokens
+    __device__ static uint32_t max_u32(uint32_t v) {
+        v = max(v, dpp32<kQuadXor1, 0xF>(v, v));
+        v = max(v, dpp32<kQuadXor2, 0xF>(v, v));
+        v = max(v, dpp32<kHalfMirror, 0xF>(v, v));
+        v = max(v, dpp32<kMirror, 0xF>(v, v));
+        return v;
+    }
+    // levels 4..7 of the balanced tree over 128 slots: lane pairs, quads, half rows, rows
+    __device__ static float tree_sum(float x) {
+        uint32_t s = __float_as_uint(x);
+        s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kQuadXor1, 0xF>(s, s)));
+        s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kQuadXor2, 0xF>(s, s)));
+        s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kHalfMirror, 0xF>(s, s)));
+        s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kMirror, 0xF>(s, s)));
+        return __uint_as_float(s);
+    }
+    __device__ static double sum_f64(double v) {
+        v += dpp_move_f64<kQuadXor1>(v);
+        v += dpp_move_f64<kQuadXor2>(v);
+        v += dpp_move_f64<kHalfMirror>(v);
+        v += dpp_move_f64<kMirror>(v);
+        return v;
+    }
+    // lowest lane (group-relative) whose ballot bit is set, -1 if none
+    __device__ static int lowest(uint64_t ballot) {
+        const int row0 = (threadIdx.x & (kWave - 1)) & ~15;
+        return __ffs(static_cast<uint32_t>(ballot >> row0) & 0xFFFFu) - 1;
+    }
+};
+
+template <>
+struct Grp<64> {
+    static constexpr int kPer = kMaxExperts / 64;
+    static constexpr int kPerWave = 1;
+    static constexpr int kRounds = 1;   // B <= 16 tokens, one per wavefront
+    __device__ static uint32_t max_u32(uint32_t v) {
+        v = Grp<16>::max_u32(v);
+        v = max(v, dpp32<kRowBcast15, 0xA>(v, v));   // rows 1, 3 take rows 0, 2
+        v = max(v, dpp32<kRowBcast31, 0xC>(v, v));   // rows 2, 3 take row 1
+        return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+    }
+    // levels 2..7 of the balanced tree: as Grp<16>, then row pairs, then the halves
+    __device__ static float tree_sum(float x) {
+        uint32_t s = __float_as_uint(Grp<16>::tree_sum(x));
+        s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kRowBcast15, 0xA>(s, s)));   // rows 1, 3
+        s = __float_as_uint(__uint_as_float(s) + __uint_as_float(dpp32<kRowBcast31, 0xC>(s, s)));   // row 3
+        return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(s), 63)));
+    }
+    __device__ static double sum_f64(double v) {
+        v = Grp<16>::sum_f64(v);
+        return (lane_f64(v, 0) + lane_f64(v, 16)) + (lane_f64(v, 32) + lane_f64(v, 48));
+    }
+    __device__ static int lowest(uint64_t ballot) {
+        return __ffsll(static_cast<unsigned long long>(ballot)) - 1;
+    }
+};
+
+// Lane-local maximum and the lane's level-1..3 (or level-1) tree sum.
+template <int P>
+__device__ __forceinline__ uint32_t lane_max(const uint32_t (&k)[P]) {
+    if constexpr (P == 8) return max(max(max(k[0], k[1]), max(k[2], k[3])), max(max(k[4], k[5]), max(k[6], k[7])));
+    else return max(k[0], k[1]);
+}
+template <int P>
+__device__ __forceinline__ float lane_tree_sum(const float (&v)[P]) {
+    if constexpr (P == 8) return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    else return v[0] + v[1];
+}
+
+// One token per group.  Each lane keeps its experts' logits, keys and slots.
+template <int P>
+struct Tok {
+    float l[P];
+    uint32_t key[P];   // order keys still selectable (0 = none)
+    int slot[P];       // rank slot of a selected expert, else -1
+};
+
+// Select the group's experts of ranks r0 .. count-1 in rank order (count is
+// per group; a group with active == false selects nothing).  The owner lane
+// of the r-th selection records r in slot[] and clears the key: the lowest
+// lane holding the maximum key wins, and inside a lane the lowest expert, so
+// ties go to the lower expert index.  Returns the number selected; top_key
+// holds the first selected key (set by the caller when r0 > 0).  With p_z > 0
+// a group also stops after the first rank at which the running sum of
+// exp(l - l_top) in rank order (fp32, one addition per rank) reaches p_z
+// (the top-p count).  The loop ends when every group of the wavefront is done.
+template <int G>
+__device__ __forceinline__ int group_select(Tok<Grp<G>::kPer>& t, bool active, int r0, int count, uint32_t& top_key,
+                                            float p_z) {
+    constexpr int P = Grp<G>::kPer;
+    const int l = threadIdx.x & (G - 1);
+    int got = r0;
+    bool live = active;
+    float c = 0.0f, top = 0.0f;
+    for (int r = r0; r < kMaxTopK; ++r) {
+        const uint32_t lmax = lane_max<P>(t.key);
+        const uint32_t m = Grp<G>::max_u32(lmax);
+        const bool act = live && r < count && m != 0u;
+        if (!__any(act)) break;
+        const bool mine = act && l == Grp<G>::lowest(__ballot(act && lmax == m));
+        int jsel = P;
+#pragma unroll
+        for (int j = P - 1; j >= 0; --j)
+            if (t.key[j] == m) jsel = j;
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            if (mine && j == jsel) {
+                t.key[j] = 0u;
+                t.slot[j] = r;
+            }
+        if (act) {
+            got = r + 1;
+            if (r == 0) {
+                top_key = m;
+                top = key_logit(m);
+            }
+            if (p_z > 0.0f) {
+                c = c + route_exp(key_logit(m) - top);
+                if (c >= p_z) live = false;
+            }
+        }
+    }
+    return got;
 }
 
 // Write one token's selected experts: the lane owning the expert of slot r
 // writes idx[i k + r] and w[i k + r] = e / denom, e = exp(l - l_top); denom is
-// the sum of e over the kept experts (renorm) or Z (raw softmax).  The
-// quotient is taken in double and rounded once to fp32.  Slots got..k-1 get
+// the sum of e over the kept experts (renorm) or Z (raw softmax), the
+// quotient taken in double and rounded once to fp32.  Slots got..k-1 get
 // expert -1 and weight 0.
-__device__ __forceinline__ void write_marked(int lane, int i, int k, int got, int slot0, int slot1, float l0,
-                                             float l1, float top, bool renorm, float Z, int32_t* idx, float* w,
-                                             int32_t* idx_copy) {
-    const double ev0 = slot0 >= 0 ? static_cast<double>(route_exp(l0 - top)) : 0.0;
-    const double ev1 = slot1 >= 0 ? static_cast<double>(route_exp(l1 - top)) : 0.0;
-    const double denom = renorm ? wave_sum_f64(ev0 + ev1) : static_cast<double>(Z);
-    if (slot0 >= 0) {
-        idx[i * k + slot0] = 2 * lane;
-        if (idx_copy != nullptr) idx_copy[i * k + slot0] = 2 * lane;
-        w[i * k + slot0] = static_cast<float>(ev0 / denom);
+template <int G>
+__device__ __forceinline__ void group_write(const Tok<Grp<G>::kPer>& t, int i, int k, int got, float top, bool renorm,
+                                            float Z, int32_t* idx, float* w, int32_t* idx_copy) {
+    constexpr int P = Grp<G>::kPer;
+    const int l = threadIdx.x & (G - 1);
+    double ev[P];
+    double loc = 0.0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        ev[j] = t.slot[j] >= 0 ? static_cast<double>(route_exp(t.l[j] - top)) : 0.0;
+        loc += ev[j];
     }
-    if (slot1 >= 0) {
-        idx[i * k + slot1] = 2 * lane + 1;
-        if (idx_copy != nullptr) idx_copy[i * k + slot1] = 2 * lane + 1;
-        w[i * k + slot1] = static_cast<float>(ev1 / denom);
+    const double denom = renorm ? Grp<G>::sum_f64(loc) : static_cast<double>(Z);
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        if (t.slot[j] < 0) continue;
+        const int q = i * k + t.slot[j];
+        idx[q] = P * l + j;
+        if (idx_copy != nullptr) idx_copy[q] = P * l + j;
+        w[q] = static_cast<float>(ev[j] / denom);
     }
-    if (lane >= got && lane < k) {
-        idx[i * k + lane] = -1;
-        if (idx_copy != nullptr) idx_copy[i * k + lane] = -1;
-        w[i * k + lane] = 0.0f;
+    if (l >= got && l < k) {
+        idx[i * k + l] = -1;
+        if (idx_copy != nullptr) idx_copy[i * k + l] = -1;
+        w[i * k + l] = 0.0f;
+    }
+}
+
+// Key and expert of the group's kth-ranked expert (kth >= 1; with fewer
+// candidates, the last one), by kth selections over copies of the keys.
+template <int G>
+__device__ __forceinline__ void group_kth(const uint32_t (&key_in)[Grp<G>::kPer], bool active, int kth, uint32_t& th,
+                                          int& eth) {
+    constexpr int P = Grp<G>::kPer;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int l = lane & (G - 1);
+    const int g0 = lane - l;
+    uint32_t key[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) key[j] = key_in[j];
+    th = 0u;
+    eth = -1;
+    for (int r = 0; r < kMaxExperts; ++r) {
+        const uint32_t lmax = lane_max<P>(key);
+        const uint32_t m = Grp<G>::max_u32(lmax);
+        const bool act = active && r < kth && m != 0u;
+        if (!__any(act)) break;
+        const int L = Grp<G>::lowest(__ballot(act && lmax == m));
+        const bool mine = act && l == L;
+        int jsel = P;
+#pragma unroll
+        for (int j = P - 1; j >= 0; --j)
+            if (key[j] == m) jsel = j;
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            if (mine && j == jsel) key[j] = 0u;
+        const int jgrp = __shfl(jsel, g0 + (L >= 0 ? L : 0), kWave);   // the owner's choice
+        if (act) {
+            th = m;
+            eth = P * L + jgrp;
+        }
     }
 }
 
@@ -272,51 +382,20 @@ __device__ __forceinline__ void dispatch_block(const int32_t* idx, int B, int N,
     }
 }
 
-// Slots of a token that routes nowhere (padding).
-__device__ __forceinline__ void write_empty(int lane, int i, int k, int32_t* idx, float* w, int32_t* idx_copy) {
-    if (lane < k) {
-        idx[i * k + lane] = -1;
-        w[i * k + lane] = 0.0f;
-        if (idx_copy != nullptr) idx_copy[i * k + lane] = -1;
-    }
-}
-
-// Key and index of the token's kth-ranked expert (kth >= 1; fewer candidates:
-// the last one), by kth wavefront selections over copies of the keys.
-__device__ __forceinline__ void kth_ranked(uint32_t o0, uint32_t o1, int kth, uint32_t& th, int& jth) {
-    th = 0;
-    jth = -1;
-    for (int r = 0; r < kth; ++r) {   // uniform trip count
-        const uint32_t m = wave_max_u32(max(o0, o1));
-        if (m == 0) break;
-        const uint64_t holders = __ballot(o0 == m || o1 == m);
-        const int L = __ffsll(static_cast<unsigned long long>(holders)) - 1;
-        const uint32_t oL = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(o0), L));
-        const int j = 2 * L + (oL == m ? 0 : 1);
-        if ((threadIdx.x & (kWave - 1)) == L) {
-            if (j & 1) o1 = 0;
-            else o0 = 0;
-        }
-        th = m;
-        jth = j;
-    }
-}
-
-// Tokens per wavefront: B <= 128 tokens over up to 16 wavefronts.
-constexpr int kTokRounds = kMaxBatch / 16;
-
 template <bool kCoherent>
 __device__ __forceinline__ float load_logit(const float* p) {
     if constexpr (kCoherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else return *p;
 }
 
-// The routing of a whole batch by the calling workgroup (all of its waves).
-// Every wave first loads the logits of all of its tokens (one round trip),
-// keeps them in registers for both phases, then walks its tokens.
+// The routing of a whole batch by the calling workgroup, one token per group
+// of G lanes: token i = kPerWave (wave + r nwaves) + group.  The launch has
+// enough wavefronts for Grp<G>::kRounds rounds.  Every lane first loads the
+// logits of its experts for all of its tokens (one round trip) and keeps
+// them in registers; Phase 2 continues from Phase 1's selections.
 // kCoherent: the logits were written by other workgroups of the same launch
 // and are read with device-scope loads.
-template <bool kOea, bool kDispatch, bool kCoherent>
+template <bool kOea, bool kDispatch, bool kCoherent, int G>
 __device__ __forceinline__ void route_block(const float* __restrict__ logits, int B, int N, int k, int k0, float p,
                                             int renorm, int32_t* __restrict__ idx, float* __restrict__ w,
                                             int32_t* __restrict__ n_base, uint32_t* __restrict__ mask_out,
@@ -325,6 +404,9 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
                                             int32_t* __restrict__ active, int pruned, int max_p,
                                             const int32_t* __restrict__ n_valid,
                                             const int32_t* __restrict__ k0_by_batch) {
+    using Gr = Grp<G>;
+    constexpr int P = Gr::kPer;
+    constexpr int R = Gr::kRounds;
     __shared__ uint32_t sbase[kMaxExperts / 32];
     __shared__ int sbase_count;
     __shared__ int n_l[kMaxBatch];
@@ -334,65 +416,70 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     // batch-size-dependent k0, looked up on the device from the real batch size
     if (kOea && k0_by_batch != nullptr) k0 = min(max(k0_by_batch[B_real], 1), k);
     const int lane = threadIdx.x & (kWave - 1);
+    const int l = lane & (G - 1);
     const int wave = threadIdx.x / kWave;
     const int nwaves = blockDim.x / kWave;
-    const int e0 = 2 * lane, e1 = 2 * lane + 1;
+    const int e_first = P * l;
     if (threadIdx.x < kMaxExperts / 32) sbase[threadIdx.x] = 0u;
 
-    float L0[kTokRounds], L1[kTokRounds];
+    float L[R][P];
 #pragma unroll
-    for (int r = 0; r < kTokRounds; ++r) {
-        const int i = wave + r * nwaves;
-        L0[r] = kNegInf;
-        L1[r] = kNegInf;
-        if (i < B_real) {
-            if (e0 < N) L0[r] = load_logit<kCoherent>(logits + i * N + e0);
-            if (e1 < N) L1[r] = load_logit<kCoherent>(logits + i * N + e1);
+    for (int r = 0; r < R; ++r) {
+        const int i = Gr::kPerWave * (wave + r * nwaves) + lane / G;
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int e = e_first + j;
+            L[r][j] = (i < B_real && e < N) ? load_logit<kCoherent>(logits + i * N + e) : kNegInf;
         }
     }
     __syncthreads();
-
     int32_t* idx_copy = kDispatch ? idx_l : nullptr;
 
-    // Vanilla top-k, or OEA Phase 1.
-#pragma unroll 1
-    for (int r = 0; r < kTokRounds; ++r) {
-        const int i = wave + r * nwaves;
-        if (i >= B) break;
-        if (i >= B_real) {
-            if (!kOea) write_empty(lane, i, k, idx, w, idx_copy);
-            else if (lane == 0) {
-                n_l[i] = 0;
-                if (n_base != nullptr) n_base[i] = 0;
-            }
-            continue;
+    // Vanilla top-k, or OEA Phase 1 (kept in registers for Phase 2).
+    Tok<P> tok[R];
+    int got1[R];
+    uint32_t top1[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        got1[r] = 0;
+        top1[r] = 0u;
+        const int base = Gr::kPerWave * (wave + r * nwaves);
+        if (base >= B) break;   // wave-uniform
+        const int i = base + lane / G;
+        const bool real = i < B_real;
+        Tok<P>& t = tok[r];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            t.l[j] = L[r][j];
+            t.key[j] = (real && e_first + j < N) ? order_key(t.l[j]) : 0u;
+            t.slot[j] = -1;
         }
-        const bool v0 = e0 < N, v1 = e1 < N;
-        const float l0 = L0[r], l1 = L1[r];
-        uint32_t key0 = v0 ? order_key(l0) : 0u;
-        uint32_t key1 = v1 ? order_key(l1) : 0u;
         const bool need_z = kOea ? (p < 1.0f) : (renorm == 0);
         float Z = 0.0f;
         if (need_z) {   // normaliser over all experts, relative to the top logit
-            const float m = key_logit(wave_max_u32(max(key0, key1)));
-            const float s0 = v0 ? route_exp(l0 - m) : 0.0f;
-            const float s1 = v1 ? route_exp(l1 - m) : 0.0f;
-            Z = wave_tree_sum(s0 + s1);
+            const float m = key_logit(Gr::max_u32(lane_max<P>(t.key)));
+            float sj[P];
+#pragma unroll
+            for (int j = 0; j < P; ++j) sj[j] = t.key[j] != 0u ? route_exp(t.l[j] - m) : 0.0f;
+            Z = Gr::tree_sum(lane_tree_sum<P>(sj));
         }
-        int slot0 = -1, slot1 = -1;
         uint32_t top_key = 0u;
         const float p_z = (kOea && p < 1.0f) ? p * Z : 0.0f;
-        const int got = select_marks(key0, key1, kOea ? k0 : k, slot0, slot1, top_key, p_z);
-        if (!kOea) {
-            write_marked(lane, i, k, got, slot0, slot1, l0, l1, key_logit(top_key), renorm != 0, Z, idx, w,
-                         idx_copy);
-        } else {
-            if (lane == 0) {
-                n_l[i] = got;
-                if (n_base != nullptr) n_base[i] = got;
+        const int got = group_select<G>(t, real, 0, kOea ? k0 : k, top_key, p_z);
+        got1[r] = got;
+        top1[r] = top_key;
+        if (i < B) {
+            if (!kOea) {
+                group_write<G>(t, i, k, got, key_logit(top_key), renorm != 0, Z, idx, w, idx_copy);
+            } else {
+                if (l == 0) {
+                    n_l[i] = got;
+                    if (n_base != nullptr) n_base[i] = got;
+                }
+#pragma unroll
+                for (int j = 0; j < P; ++j)
+                    if (t.slot[j] >= 0) atomicOr(&sbase[(e_first + j) >> 5], 1u << ((e_first + j) & 31));
             }
-            if (slot0 >= 0) atomicOr(&sbase[e0 >> 5], 1u << (e0 & 31));
-            if (slot1 >= 0) atomicOr(&sbase[e1 >> 5], 1u << (e1 & 31));
         }
     }
     if constexpr (kOea) {
@@ -409,35 +496,36 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
         const int keep = T < k ? T : k;
 
         // Phase 2: token i keeps the first min(k, T) members of S_base in its
-        // rank order -- its baseline first (the top-ranked experts are in
-        // S_base), then lower-ranked experts that other tokens already
-        // activated.  With max_p < N only the token's top-max_p ranks may be
-        // taken; pruned keeps the baseline alone (its n_i experts).
-#pragma unroll 1
-        for (int r = 0; r < kTokRounds; ++r) {
-            const int i = wave + r * nwaves;
-            if (i >= B) break;
-            if (i >= B_real) {
-                write_empty(lane, i, k, idx, w, idx_copy);
-                continue;
-            }
-            const float l0 = L0[r], l1 = L1[r];
-            bool a0 = e0 < N && ((sbase[e0 >> 5] >> (e0 & 31)) & 1u);
-            bool a1 = e1 < N && ((sbase[e1 >> 5] >> (e1 & 31)) & 1u);
+        // rank order -- its baseline first (already selected: the top-ranked
+        // experts are in S_base), then lower-ranked experts that other tokens
+        // already activated.  With max_p < N only the token's top-max_p ranks
+        // may be taken; pruned keeps the baseline alone (its n_i experts).
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int base = Gr::kPerWave * (wave + r * nwaves);
+            if (base >= B) break;
+            const int i = base + lane / G;
+            const bool real = i < B_real;
+            Tok<P>& t = tok[r];
+            uint32_t th = 0u;
+            int eth = kMaxExperts;
             if (!pruned && max_p < N) {
-                uint32_t th;
-                int jth;
-                kth_ranked(e0 < N ? order_key(l0) : 0u, e1 < N ? order_key(l1) : 0u, max_p, th, jth);
-                const uint32_t q0 = order_key(l0), q1 = order_key(l1);
-                a0 = a0 && (q0 > th || (q0 == th && e0 <= jth));
-                a1 = a1 && (q1 > th || (q1 == th && e1 <= jth));
+                uint32_t full[P];
+#pragma unroll
+                for (int j = 0; j < P; ++j) full[j] = (real && e_first + j < N) ? order_key(t.l[j]) : 0u;
+                group_kth<G>(full, real, max_p, th, eth);
             }
-            uint32_t key0 = a0 ? order_key(l0) : 0u;
-            uint32_t key1 = a1 ? order_key(l1) : 0u;
-            int slot0 = -1, slot1 = -1;
-            uint32_t top_key = 0u;
-            const int got = select_marks(key0, key1, pruned ? n_l[i] : keep, slot0, slot1, top_key, 0.0f);
-            write_marked(lane, i, k, got, slot0, slot1, l0, l1, key_logit(top_key), true, 0.0f, idx, w, idx_copy);
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const int e = e_first + j;
+                bool a = t.key[j] != 0u && ((sbase[e >> 5] >> (e & 31)) & 1u);
+                if (!pruned && max_p < N) a = a && (t.key[j] > th || (t.key[j] == th && e <= eth));
+                if (!a) t.key[j] = 0u;
+            }
+            uint32_t top_key = top1[r];
+            const int count = pruned ? got1[r] : keep;
+            const int got = group_select<G>(t, real, got1[r], count, top_key, 0.0f);
+            if (i < B) group_write<G>(t, i, k, got, key_logit(top_key), true, 0.0f, idx, w, idx_copy);
         }
     }
     if constexpr (kDispatch) {
@@ -446,11 +534,13 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     }
 }
 
-// Routing of a batch by one workgroup of min(B, 16) wavefronts.  kOea: OEA
+// Routing of a batch by one workgroup: one wavefront per token for B <= 16
+// (G = 64), else one row of 16 lanes per token, four per wavefront, on up to
+// 16 wavefronts and two rounds (G = 16).  kOea: OEA
 // Phase 1, the union S_base (LDS bitmask built with integer OR, independent
 // of the order tokens finish), Phase 2; otherwise vanilla top-k.  kDispatch:
 // the same workgroup then dispatches the routed pairs from LDS.
-template <bool kOea, bool kDispatch>
+template <bool kOea, bool kDispatch, int G>
 __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ logits, int B, int N, int k,
                                                      int k0, float p, int renorm, int32_t* __restrict__ idx,
                                                      float* __restrict__ w, int32_t* __restrict__ n_base,
@@ -459,8 +549,8 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ l
                                                      int32_t* __restrict__ perm, int32_t* __restrict__ active,
                                                      int pruned, int max_p, const int32_t* __restrict__ n_valid,
                                                      const int32_t* __restrict__ k0_by_batch) {
-    route_block<kOea, kDispatch, false>(logits, B, N, k, k0, p, renorm, idx, w, n_base, mask_out, T_out, cnt,
-                                        offsets, perm, active, pruned, max_p, n_valid, k0_by_batch);
+    route_block<kOea, kDispatch, false, G>(logits, B, N, k, k0, p, renorm, idx, w, n_base, mask_out, T_out, cnt,
+                                           offsets, perm, active, pruned, max_p, n_valid, k0_by_batch);
 }
 
 // Dispatch on its own (idx from global memory).
@@ -610,7 +700,7 @@ __device__ __forceinline__ void wait_vmem() {   // s_waitcnt vmcnt(0)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename XT, bool kOea>
+template <typename XT, bool kOea, int G>
 __global__ __launch_bounds__(kGemvThreads * kFusedExperts) void router_route_kernel(
         const XT* __restrict__ x, const float* __restrict__ w_r, int B, int H, int N, float* __restrict__ logits,
         int k, int k0, float p, int renorm, int32_t* __restrict__ idx, float* __restrict__ w,
@@ -641,8 +731,8 @@ __global__ __launch_bounds__(kGemvThreads * kFusedExperts) void router_route_ker
                  static_cast<int>(gridDim.x * gridDim.y) - 1;
     __syncthreads();
     if (!last_s) return;
-    route_block<kOea, true, true>(logits, B, N, k, k0, p, kOea ? 1 : renorm, idx, w, n_base, mask_out, T_out, cnt,
-                                  offsets, perm, active, pruned, max_p, n_valid, k0_by_batch);
+    route_block<kOea, true, true, G>(logits, B, N, k, k0, p, kOea ? 1 : renorm, idx, w, n_base, mask_out, T_out,
+                                     cnt, offsets, perm, active, pruned, max_p, n_valid, k0_by_batch);
     if (threadIdx.x == 0) __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -684,17 +774,29 @@ hipError_t launch_router_logits(const void* x, int x_dtype, const float* w_r, in
     return hipGetLastError();
 }
 
+// Batches up to kSmallBatch route one token per wavefront, larger ones one
+// token per 16-lane row (four per wavefront, at most 16 wavefronts).
+constexpr int kSmallBatch = 16;
+int route_threads(int B) {
+    const int waves = B <= kSmallBatch ? B : (B + Grp<16>::kPerWave - 1) / Grp<16>::kPerWave;
+    return kWave * (waves < 16 ? waves : 16);
+}
+
 hipError_t launch_route(const float* logits, int B, int N, int k, int k0, float p, int oea,
                         int renorm, int32_t* idx, float* w, int32_t* n_base, uint32_t* mask,
                         int32_t* T, hipStream_t s) {
-    const int threads = kWave * (B < 16 ? B : 16);
-    if (oea)
-        route_kernel<true, false><<<1, threads, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, mask, T,
-                                                        nullptr, nullptr, nullptr, nullptr, 0, N, nullptr, nullptr);
-    else
-        route_kernel<false, false><<<1, threads, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w, nullptr,
-                                                         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
-                                                         N, nullptr, nullptr);
+#define MOE_ROUTE(G_, OEA_)                                                                                      \
+    route_kernel<OEA_, false, G_><<<1, route_threads(B), 0, s>>>(                                                \
+        logits, B, N, k, OEA_ ? k0 : k, OEA_ ? p : 1.0f, OEA_ ? 1 : renorm, idx, w, OEA_ ? n_base : nullptr,      \
+        OEA_ ? mask : nullptr, OEA_ ? T : nullptr, nullptr, nullptr, nullptr, nullptr, 0, N, nullptr, nullptr)
+    if (B <= kSmallBatch) {
+        if (oea) MOE_ROUTE(64, true);
+        else MOE_ROUTE(64, false);
+    } else {
+        if (oea) MOE_ROUTE(16, true);
+        else MOE_ROUTE(16, false);
+    }
+#undef MOE_ROUTE
     return hipGetLastError();
 }
 
@@ -703,15 +805,20 @@ hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int m
                                  float* w, int32_t* n_base,
                                  uint32_t* mask, int32_t* cnt, int32_t* offsets, int32_t* perm, int32_t* active,
                                  int32_t* T, hipStream_t s) {
-    const int threads = kWave * (B < 16 ? B : 16);
-    if (mode != MOE_ROUTE_TOPK)
-        route_kernel<true, true><<<1, threads, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, mask, T, cnt,
-                                                       offsets, perm, active, mode == MOE_ROUTE_PRUNED, max_p,
-                                                       n_valid, k0_by_batch);
-    else
-        route_kernel<false, true><<<1, threads, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w, nullptr,
-                                                        nullptr, T, cnt, offsets, perm, active, 0, N, n_valid,
-                                                        nullptr);
+    const bool oea = mode != MOE_ROUTE_TOPK;
+#define MOE_ROUTE(G_, OEA_)                                                                                      \
+    route_kernel<OEA_, true, G_><<<1, route_threads(B), 0, s>>>(                                                 \
+        logits, B, N, k, OEA_ ? k0 : k, OEA_ ? p : 1.0f, OEA_ ? 1 : renorm, idx, w, OEA_ ? n_base : nullptr,      \
+        OEA_ ? mask : nullptr, T, cnt, offsets, perm, active, OEA_ ? (mode == MOE_ROUTE_PRUNED) : 0,             \
+        OEA_ ? max_p : N, n_valid, OEA_ ? k0_by_batch : nullptr)
+    if (B <= kSmallBatch) {
+        if (oea) MOE_ROUTE(64, true);
+        else MOE_ROUTE(64, false);
+    } else {
+        if (oea) MOE_ROUTE(16, true);
+        else MOE_ROUTE(16, false);
+    }
+#undef MOE_ROUTE
     return hipGetLastError();
 }
 
@@ -725,27 +832,26 @@ hipError_t launch_router_route_dispatch(const void* x, int x_dtype, const float*
     const bool oea = mode != MOE_ROUTE_TOPK;
     const int pruned = mode == MOE_ROUTE_PRUNED;
     const int mp = mode == MOE_ROUTE_OEA ? max_p : N;
-    if (x_dtype == MOE_DT_BF16) {
-        const uint16_t* xb = static_cast<const uint16_t*>(x);
-        if (oea)
-            router_route_kernel<uint16_t, true><<<grid, threads, 0, s>>>(
-                xb, w_r, B, H, N, logits, k, k0, p, 1, idx, w, n_base, mask, T, cnt, offsets, perm, active, pruned, mp,
-                n_valid, k0_by_batch, sync);
-        else
-            router_route_kernel<uint16_t, false><<<grid, threads, 0, s>>>(
-                xb, w_r, B, H, N, logits, k, k, 1.0f, renorm, idx, w, nullptr, nullptr, T, cnt, offsets, perm, active,
-                0, N, n_valid, nullptr, sync);
-    } else {
-        const float* xf = static_cast<const float*>(x);
-        if (oea)
-            router_route_kernel<float, true><<<grid, threads, 0, s>>>(
-                xf, w_r, B, H, N, logits, k, k0, p, 1, idx, w, n_base, mask, T, cnt, offsets, perm, active, pruned, mp,
-                n_valid, k0_by_batch, sync);
-        else
-            router_route_kernel<float, false><<<grid, threads, 0, s>>>(
-                xf, w_r, B, H, N, logits, k, k, 1.0f, renorm, idx, w, nullptr, nullptr, T, cnt, offsets, perm, active,
-                0, N, n_valid, nullptr, sync);
+#define MOE_FUSED(XT_, G_, OEA_)                                                                                 \
+    router_route_kernel<XT_, OEA_, G_><<<grid, threads, 0, s>>>(                                                 \
+        static_cast<const XT_*>(x), w_r, B, H, N, logits, k, OEA_ ? k0 : k, OEA_ ? p : 1.0f, OEA_ ? 1 : renorm,  \
+        idx, w, OEA_ ? n_base : nullptr, OEA_ ? mask : nullptr, T, cnt, offsets, perm, active, OEA_ ? pruned : 0,  \
+        OEA_ ? mp : N, n_valid, OEA_ ? k0_by_batch : nullptr, sync)
+#define MOE_FUSED_G(XT_)                                  \
+    if (B <= kSmallBatch) {                               \
+        if (oea) MOE_FUSED(XT_, 64, true);                \
+        else MOE_FUSED(XT_, 64, false);                   \
+    } else {                                              \
+        if (oea) MOE_FUSED(XT_, 16, true);                \
+        else MOE_FUSED(XT_, 16, false);                   \
     }
+    if (x_dtype == MOE_DT_BF16) {
+        MOE_FUSED_G(uint16_t)
+    } else {
+        MOE_FUSED_G(float)
+    }
+#undef MOE_FUSED_G
+#undef MOE_FUSED
     return hipGetLastError();
 }
 
