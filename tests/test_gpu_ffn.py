@@ -193,3 +193,22 @@ def test_qwen235b_layer_sampled():
     _run_and_check(layer, host, x, xd, logits, "oea", 5, 1.0, TOL["bf16"], tokens=[0, 31])
     del layer
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode,k0", [("topk", 0), ("oea", 5)])
+def test_qwen30b_mixed_int4_b32_sampled(mode, k0):
+    # the mixed-residency layer: the 32 hottest experts (by the Zipf bias) in
+    # bf16, the other 96 INT4 group-128, B = 32 with Zipf-biased routing;
+    # the oracle computes sampled tokens with the dequantised INT4 weights
+    s = synth.SHAPES["qwen30b"]
+    bias = synth.zipf_bias(s["N"], 1.1)
+    hot = set(np.argsort(-bias, kind="stable")[:32].tolist())
+    cold = [e for e in range(s["N"]) if e not in hot]
+    layer, host = build_layer(s["N"], s["k"], s["H"], s["I"], 34, fmt="bf16", int4_experts=cold,
+                              with_router=False)
+    B = 32
+    x, xd = _x(34, B, layer.H, "bf16")
+    logits = (synth.logits(34, B, layer.N, 0.9) + bias[None, :]).astype(np.float32)
+    _run_and_check(layer, host, x, xd, logits, mode, k0, 1.0, TOL["int4"], tokens=[0, 9, 20, 31])
+    del layer
+    torch.cuda.empty_cache()
