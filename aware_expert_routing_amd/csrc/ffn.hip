@@ -121,26 +121,41 @@ struct Act {
     static constexpr int kRaw = kLaneBytes >= 16 ? kLaneBytes / 16 : 1;
 };
 
+// Ring depths of a wave: weight tiles are loaded D positions ahead of the
+// multiply, activation fragments X positions ahead.  X = D except where the
+// activation fragments are much larger than the weights (INT4 with fp32
+// activations: 128 columns of fp32 per 1 KB tile), where one activation
+// stage frees the registers for a deeper weight ring.  The depths come from
+// a register budget per case (the rest holds addresses and temporaries; the
+// split and INT4 paths need more temporaries).
 template <int PHASE, int FMT, bool XF32, int NT>
-constexpr int stages() {
-    constexpr int nmat = PHASE == 0 ? 2 : 1;
-    constexpr int rb = PHASE == 0 ? kRbA : kRbB;
-    constexpr int per = nmat * rb * (FMT == MOE_W_INT4_G128 ? 6 : 4) + NT * Act<FMT, XF32>::kRaw * 4;
-    constexpr int acc = nmat * rb * NT * 4;
-    // register budget for the ring (the rest holds addresses and temporaries;
-    // the split and INT4 paths need more temporaries)
-    constexpr int budget = PHASE == 1 ? 90 : ((FMT == MOE_W_INT4_G128 || XF32) ? 150 : 200);
-    constexpr int fit = (budget - acc) / per;
-    if constexpr (FMT == MOE_W_INT4_G128 && (XF32 || NT > 1)) return 1;   // avoids spills
-    return fit >= 8 ? 8 : (fit >= 4 ? 4 : (fit >= 2 ? 2 : 1));
-}
+struct Ring {
+    static constexpr int kMatN = PHASE == 0 ? 2 : 1;
+    static constexpr int kRbN = PHASE == 0 ? kRbA : kRbB;
+    static constexpr int kW = kMatN * kRbN * (FMT == MOE_W_INT4_G128 ? 6 : 4);   // registers per weight stage
+    static constexpr int kX = NT * Act<FMT, XF32>::kRaw * 4;                      // per activation stage
+    static constexpr int kAcc = kMatN * kRbN * NT * 4;
+    static constexpr int kBudget = (FMT == MOE_W_INT4_G128 && XF32) ? (PHASE == 1 ? 70 : 110)
+                                                                    : (PHASE == 1 ? 90 : ((FMT == MOE_W_INT4_G128 || XF32) ? 150 : 200));
+    static constexpr bool kSplit = FMT == MOE_W_INT4_G128 && XF32;
+    static constexpr int depth(int x_fixed) {   // x_fixed = 0: X = D
+        for (int d = 8; d >= 1; d /= 2)
+            if (kW * d + kX * (x_fixed ? x_fixed : d) + kAcc <= kBudget) return d;
+        return 1;
+    }
+    static constexpr int D = kSplit ? depth(1) : (FMT == MOE_W_INT4_G128 && NT > 1 ? 1 : depth(0));
+    static constexpr int X = kSplit ? 1 : D;
+};
 
 template <int PHASE, int FMT, bool XF32, int NT>
-struct Stage {
+struct WStage {
     static constexpr int kMat = PHASE == 0 ? 2 : 1;
     static constexpr int kRb = PHASE == 0 ? kRbA : kRbB;
     u32x4 w[kMat][kRb];
     u32x2 sc[kMat][kRb];                       // INT4 only
+};
+template <int FMT, bool XF32, int NT>
+struct XStage {
     u32x4 x[NT][Act<FMT, XF32>::kRaw];
 };
 
@@ -148,14 +163,19 @@ struct Stage {
 // is all ones, or zero for a padding position: the activation bits are
 // ANDed with it, so a padding tile adds exact zeros without a branch.
 template <int PHASE, int FMT, bool XF32, int NT>
-__device__ __forceinline__ void tile_mma(const Stage<PHASE, FMT, XF32, NT>& st_in, uint32_t keep,
+__device__ __forceinline__ void tile_mma(const WStage<PHASE, FMT, XF32, NT>& ws, const XStage<FMT, XF32, NT>& xs_in,
+                                         uint32_t keep,
                                          f32x4 (&acc)[PHASE == 0 ? 2 : 1][PHASE == 0 ? kRbA : kRbB][NT]) {
-    using S = Stage<PHASE, FMT, XF32, NT>;
-    S st = st_in;
+    using S = WStage<PHASE, FMT, XF32, NT>;
+    struct {
+        const u32x4 (&w)[S::kMat][S::kRb];
+        const u32x2 (&sc)[S::kMat][S::kRb];
+        u32x4 x[NT][Act<FMT, XF32>::kRaw];
+    } st{ws.w, ws.sc, {}};
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int c = 0; c < Act<FMT, XF32>::kRaw; ++c) st.x[t][c] &= keep;
+        for (int c = 0; c < Act<FMT, XF32>::kRaw; ++c) st.x[t][c] = xs_in.x[t][c] & keep;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         if constexpr (FMT == MOE_W_BF16) {
@@ -356,10 +376,12 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
     const float* wg = uni_ptr(w_in);
     float* hbuf = const_cast<float*>(uni_ptr(hbuf_in));
     float* dbuf = const_cast<float*>(uni_ptr(dbuf_in));
-    using St = Stage<PHASE, FMT, XF32, NT>;
+    using Wst = WStage<PHASE, FMT, XF32, NT>;
+    using Xst = XStage<FMT, XF32, NT>;
     using Ac = Act<FMT, XF32>;
-    constexpr int kMat = St::kMat, kRb = St::kRb;
-    constexpr int D = stages<PHASE, FMT, XF32, NT>();
+    constexpr int kMat = Wst::kMat, kRb = Wst::kRb;
+    constexpr int D = Ring<PHASE, FMT, XF32, NT>::D;   // weight stages in flight
+    constexpr int X = Ring<PHASE, FMT, XF32, NT>::X;   // activation stages in flight (X divides D)
     const int lane = threadIdx.x & (kWave - 1);
     const int n = lane & 15, q = lane >> 4;
     const int rows = PHASE == 0 ? I : H, cols = PHASE == 0 ? H : I;
@@ -387,8 +409,9 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
         arow[t] += q * Ac::kLaneBytes;
     }
 
-    St ring[D];
-    auto issue = [&](St& st, int item, int s) {
+    Wst ring[D];
+    Xst xring[X];
+    auto issue = [&](Wst& st, int item, int s) {
         const int se = s < S ? s : S - 1;
 #pragma unroll
         for (int m = 0; m < kMat; ++m)
@@ -400,6 +423,10 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
                 st.w[m][r] = load_w(mb[m] + tile * kTileBytes + lane * 16);
                 if constexpr (FMT == MOE_W_INT4_G128) st.sc[m][r] = load_a8(sb[m] + (tile * 16 + 4 * q) * 2);
             }
+    };
+    // activation fragments depend on the tile column only, not on the item
+    auto issue_x = [&](Xst& st, int s) {
+        const int se = s < S ? s : S - 1;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -425,7 +452,10 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
     };
     zero();
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(ring[d], 0, d);
+    for (int d = 0; d < D; ++d) {
+        issue(ring[d], 0, d);
+        if (d < X) issue_x(xring[d], d);
+    }
 
     const int nblk = count * (Sp / D);
     int ci = 0, cs = 0;   // item and first tile of the block being multiplied
@@ -439,12 +469,23 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
         if (!last) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                tile_mma<PHASE, FMT, XF32, NT>(ring[d], cs + d < S ? ~0u : 0u, acc);
+                tile_mma<PHASE, FMT, XF32, NT>(ring[d], xring[d % X], cs + d < S ? ~0u : 0u, acc);
                 issue(ring[d], ii, is + d);
+                if constexpr (X == D) {
+                    issue_x(xring[d], is + d);
+                } else {
+                    const int ta = cs + d + X;   // tile column X positions ahead (wraps into the next item)
+                    issue_x(xring[d % X], ta < Sp ? ta : ta - Sp);
+                }
             }
         } else {
 #pragma unroll
-            for (int d = 0; d < D; ++d) tile_mma<PHASE, FMT, XF32, NT>(ring[d], cs + d < S ? ~0u : 0u, acc);
+            for (int d = 0; d < D; ++d) {
+                tile_mma<PHASE, FMT, XF32, NT>(ring[d], xring[d % X], cs + d < S ? ~0u : 0u, acc);
+                if constexpr (X < D) {
+                    if (d + X < D) issue_x(xring[d % X], cs + d + X);
+                }
+            }
         }
         cs += D;
         if (cs == Sp) {   // item done: write its rows for every real token
