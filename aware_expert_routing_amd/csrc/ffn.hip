@@ -395,19 +395,9 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
     sb[0] = uni_ptr(s0);
     if constexpr (kMat == 2) { mb[1] = uni_ptr(m1); sb[1] = uni_ptr(s1); }
 
-    // activation rows of this lane's tokens (column tile t: token 16 t + n)
-    const char* arow[NT];
+    const char* arow[NT];   // activation rows of this lane's tokens (column tile t: token 16 t + n)
     int pair[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int tok = 16 * t + n;
-        pair[t] = perm[first + (tok < cnt ? tok : 0)];
-        if constexpr (PHASE == 0)
-            arow[t] = xg + static_cast<size_t>(pair[t] / k) * H * (XF32 ? 4 : 2);
-        else
-            arow[t] = reinterpret_cast<const char*>(hbuf + static_cast<size_t>(pair[t]) * I);
-        arow[t] += q * Ac::kLaneBytes;
-    }
+    float wt[NT];           // phase B: the pairs' routing weights
 
     Wst ring[D];
     Xst xring[X];
@@ -451,11 +441,23 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
                 for (int t = 0; t < NT; ++t) acc[m][r][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     };
     zero();
+    // The weight stages go out first; the token lookups (perm, then the
+    // activation rows) follow, so their round trips overlap the weights'.
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        issue(ring[d], 0, d);
-        if (d < X) issue_x(xring[d], d);
+    for (int d = 0; d < D; ++d) issue(ring[d], 0, d);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int tok = 16 * t + n;
+        pair[t] = ((const __attribute__((address_space(1))) int32_t*)perm)[first + (tok < cnt ? tok : 0)];
+        if constexpr (PHASE == 0)
+            arow[t] = xg + static_cast<size_t>(pair[t] / k) * H * (XF32 ? 4 : 2);
+        else
+            arow[t] = reinterpret_cast<const char*>(hbuf + static_cast<size_t>(pair[t]) * I);
+        arow[t] += q * Ac::kLaneBytes;
+        wt[t] = PHASE == 1 ? ((const __attribute__((address_space(1))) float*)wg)[pair[t]] : 0.0f;
     }
+#pragma unroll
+    for (int d = 0; d < X; ++d) issue_x(xring[d], d);
 
     const int nblk = count * (Sp / D);
     int ci = 0, cs = 0;   // item and first tile of the block being multiplied
@@ -504,14 +506,13 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
                         *reinterpret_cast<float4*>(hrow + (rb0 + r) * 16 + 4 * q) = hv;
                     }
                 } else {
-                    const float wt = wg[pair[t]];
                     float* drow = dbuf + static_cast<size_t>(pair[t]) * H;
 #pragma unroll
                     for (int r = 0; r < kRb; ++r) {
                         if (rb0 + r >= nrb) continue;
                         const f32x4 v = acc[0][r][t];
                         *reinterpret_cast<float4*>(drow + (rb0 + r) * 16 + 4 * q) =
-                            make_float4(wt * v.x, wt * v.y, wt * v.z, wt * v.w);
+                            make_float4(wt[t] * v.x, wt[t] * v.y, wt[t] * v.z, wt[t] * v.w);
                     }
                 }
             }
@@ -572,12 +573,21 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     __shared__ int active_l[kMaxExperts];
     __shared__ int offsets_l[kMaxExperts + 1];
     // Stage the handle table, active list and offsets with independent loads
-    // (one round trip) instead of following active -> handle per slot.
+    // (one round trip) instead of following active -> handle per slot.  The
+    // loads take clamped (in-bounds) addresses and are all issued before the
+    // first LDS write, so no load waits behind another.
+    static_assert(kMaxExperts * 4 <= 2 * kThreads && kMaxExperts + 1 <= kThreads, "staging layout");
     const int T = uni(*a.T);
-    for (int c = threadIdx.x; c < a.N * 4; c += kThreads)
-        table_l[c] = load_a(reinterpret_cast<const char*>(a.table) + 16 * c);
-    if (threadIdx.x < a.N) active_l[threadIdx.x] = a.active[threadIdx.x];
-    if (threadIdx.x <= a.N) offsets_l[threadIdx.x] = a.offsets[threadIdx.x];
+    const int tid = threadIdx.x, nc = a.N * 4;
+    const char* tb = reinterpret_cast<const char*>(a.table);
+    const u32x4 t0 = load_a(tb + 16 * min(tid, nc - 1));
+    const u32x4 t1 = load_a(tb + 16 * min(tid + kThreads, nc - 1));
+    const int act = ((const __attribute__((address_space(1))) int32_t*)a.active)[min(tid, a.N - 1)];
+    const int off = ((const __attribute__((address_space(1))) int32_t*)a.offsets)[min(tid, a.N)];
+    if (tid < nc) table_l[tid] = t0;
+    if (tid + kThreads < nc) table_l[tid + kThreads] = t1;
+    if (tid < a.N) active_l[tid] = act;
+    if (tid <= a.N) offsets_l[tid] = off;
     __syncthreads();
     price_slots<PHASE>(a, T, reinterpret_cast<const moe_expert_handle*>(table_l), active_l, offsets_l, recs,
                        pref_cost, pref_item, wave_tot);
@@ -615,17 +625,38 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
 }
 
 // y[i, o] = sum over filled slots s of token i (slot order) of dbuf[i*k+s, o].
-__global__ __launch_bounds__(64) void combine_kernel(FfnArgs a) {
-    const int i = blockIdx.y;
-    const int o = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+// One wavefront per (token, 256 outputs).  All of the token's slot rows
+// are loaded first (unfilled slots' rows are read and ignored); lane j < k
+// then reads slot j's expert index and a ballot makes the filled-slot mask,
+// so every load shares one round trip.  KS >= k slots are loaded.
+template <int KS>
+__device__ __forceinline__ void combine_token(const FfnArgs& a) {
+    const int i = blockIdx.y, k = a.k, lane = threadIdx.x;
+    const int o = (blockIdx.x * kWave + lane) * 4;
+    const float* d0 = a.dbuf + static_cast<size_t>(i) * k * a.H + (o < a.H ? o : a.H - 4);
+    float4 d[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+        d[j] = *reinterpret_cast<const float4*>(d0 + static_cast<size_t>(j < k ? j : k - 1) * a.H);
+    const int32_t* idx = a.idx + static_cast<size_t>(i) * k;
+    const uint64_t filled = __ballot(lane < k && idx[lane < k ? lane : 0] >= 0);
     if (o >= a.H) return;
     float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int q = 0; q < a.k; ++q) {
-        if (a.idx[i * a.k + q] < 0) continue;
-        const float4 d = *reinterpret_cast<const float4*>(a.dbuf + static_cast<size_t>(i * a.k + q) * a.H + o);
-        s.x += d.x; s.y += d.y; s.z += d.z; s.w += d.w;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        const bool f = (filled >> j) & 1;   // bit j is clear for j >= k
+        s.x = f ? s.x + d[j].x : s.x;
+        s.y = f ? s.y + d[j].y : s.y;
+        s.z = f ? s.z + d[j].z : s.z;
+        s.w = f ? s.w + d[j].w : s.w;
     }
     *reinterpret_cast<float4*>(a.y + static_cast<size_t>(i) * a.H + o) = s;
+}
+
+__global__ __launch_bounds__(kWave) void combine_kernel(FfnArgs a) {
+    static_assert(kMaxTopK <= 16, "combine loads at most 16 slots");
+    if (a.k <= 8) combine_token<8>(a);
+    else combine_token<16>(a);
 }
 
 int g_num_cus[64] = {0};
@@ -669,8 +700,8 @@ hipError_t launch_expert_ffn(const FfnArgs& in, void* ws, hipStream_t s) {
     ffn_kernel<1><<<g1 > 0 ? g1 : kXcds, kThreads, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 cg((a.H / 4 + 63) / 64, a.B);
-    combine_kernel<<<cg, 64, 0, s>>>(a);
+    dim3 cg((a.H / 4 + kWave - 1) / kWave, a.B);
+    combine_kernel<<<cg, kWave, 0, s>>>(a);
     return hipGetLastError();
 }
 
