@@ -37,6 +37,10 @@
 // second MFMA with the constant -136 removes the offset (u - 8 = q), and the
 // group's per-row fp16 scale multiplies the result into the accumulator.
 // fp32 activations meeting bf16/INT4 weights enter as bf16 hi + lo pairs.
+// Phase A stores h of a bf16/INT4 expert already in that form (per 8
+// columns: 8 bf16 hi, then 8 bf16 lo; 4 bytes per value as in fp32), so
+// phase B, which reads each h fragment once per row block, does no
+// splitting; an fp32 expert's h stays fp32.
 #include "internal.h"
 
 namespace moe {
@@ -185,8 +189,8 @@ __device__ __forceinline__ void tile_mma(const WStage<PHASE, FMT, XF32, NT>& ws,
 #pragma unroll
                     for (int r = 0; r < S::kRb; ++r) acc[m][r][t] = mma_bf16(st.w[m][r], st.x[t][0], acc[m][r][t]);
             } else {
-                u32x4 hi, lo;
-                split8(st.x[t][0], st.x[t][1], hi, lo);
+                u32x4 hi = st.x[t][0], lo = st.x[t][1];   // phase B: h arrives split
+                if constexpr (PHASE == 0) split8(st.x[t][0], st.x[t][1], hi, lo);
 #pragma unroll
                 for (int m = 0; m < S::kMat; ++m)
 #pragma unroll
@@ -223,8 +227,14 @@ __device__ __forceinline__ void tile_mma(const WStage<PHASE, FMT, XF32, NT>& ws,
             u32x4 xb[4][kParts];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if constexpr (XF32) split8(st.x[t][2 * j], st.x[t][2 * j + 1], xb[j][0], xb[j][kParts - 1]);
-                else xb[j][0] = st.x[t][j];
+                if constexpr (XF32 && PHASE == 0) {
+                    split8(st.x[t][2 * j], st.x[t][2 * j + 1], xb[j][0], xb[j][1]);
+                } else if constexpr (XF32) {   // phase B: h arrives split
+                    xb[j][0] = st.x[t][2 * j];
+                    xb[j][kParts - 1] = st.x[t][2 * j + 1];
+                } else {
+                    xb[j][0] = st.x[t][j];
+                }
             }
             const u32x4 neg = {kBf16Neg136x2, kBf16Neg136x2, kBf16Neg136x2, kBf16Neg136x2};
             f32x4 corr = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -501,9 +511,24 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
                     for (int r = 0; r < kRb; ++r) {
                         if (rb0 + r >= nrb) continue;
                         const f32x4 g = acc[0][r][t], u = acc[kMat - 1][r][t];
-                        const float4 hv = make_float4(silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z,
-                                                      silu(g.w) * u.w);
-                        *reinterpret_cast<float4*>(hrow + (rb0 + r) * 16 + 4 * q) = hv;
+                        const float hv[4] = {silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w};
+                        const int c = (rb0 + r) * 16 + 4 * q;   // first of this lane's 4 columns of h
+                        if constexpr (FMT == MOE_W_F32) {
+                            *reinterpret_cast<float4*>(hrow + c) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+                        } else {
+                            // split layout: per 8 columns, 8 bf16 hi then 8 bf16 lo
+                            uint32_t hi[2], lo[2];
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                const uint32_t a = bf16_rne(hv[2 * j]), b = bf16_rne(hv[2 * j + 1]);
+                                hi[j] = a | (b << 16);
+                                lo[j] = bf16_rne(hv[2 * j] - __uint_as_float(a << 16)) |
+                                        (bf16_rne(hv[2 * j + 1] - __uint_as_float(b << 16)) << 16);
+                            }
+                            char* gp = reinterpret_cast<char*>(hrow) + (c / 8) * 32 + (c % 8) * 2;
+                            *reinterpret_cast<uint2*>(gp) = make_uint2(hi[0], hi[1]);
+                            *reinterpret_cast<uint2*>(gp + 16) = make_uint2(lo[0], lo[1]);
+                        }
                     }
                 } else {
                     float* drow = dbuf + static_cast<size_t>(pair[t]) * H;
@@ -677,8 +702,8 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 }  // namespace
 
-// Workspace: SwiGLU activations [B*k, I] fp32, then weighted down
-// projections [B*k, H] fp32.
+// Workspace: SwiGLU activations [B*k, I] (4 bytes per value: fp32, or the
+// split bf16 hi/lo form), then weighted down projections [B*k, H] fp32.
 size_t ffn_workspace_bytes(int B, int k, int H, int I) {
     const size_t pairs = static_cast<size_t>(B) * k;
     return align256(pairs * I * sizeof(float)) + align256(pairs * H * sizeof(float));
