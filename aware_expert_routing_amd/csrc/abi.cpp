@@ -169,6 +169,7 @@ MOE_API int moe_expert_ffn(const moe_expert_handle* table, int N, int H, int I, 
     if (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16) return fail(MOE_EINVAL, "bad x_dtype");
     if (H < 32 || H % 32 || I < 32 || I % 32) return fail(MOE_EINVAL, "H and I must be positive multiples of 32");
     if (H > 16384 || I > 16384) return fail(MOE_EUNSUPPORTED, "H and I above 16384 are not supported");
+    if (!moe::ffn_cost_fits(B, k, N, H, I)) return fail(MOE_EUNSUPPORTED, "B*k too large for H and I");
     if (ws_bytes < moe::ffn_workspace_bytes(B, k, H, I)) return fail(MOE_EINVAL, "workspace too small");
     if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
     if (reinterpret_cast<uintptr_t>(table) % 16 != 0) return fail(MOE_EINVAL, "handle table must be 16-byte aligned");

@@ -43,6 +43,8 @@
 // splitting; an fp32 expert's h stays fp32.
 #include "internal.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -292,6 +294,20 @@ __host__ __device__ __forceinline__ int pass_tokens(int fmt) { return fmt == MOE
 
 __host__ __device__ __forceinline__ int col_tiles_for(int cnt) { return cnt <= 16 ? 1 : 2; }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront, in registers: DPP
+// row shifts by 1, 2, 4 and 8 scan each row of 16 lanes, then the last lane
+// of row 0 is added to row 1, of row 2 to row 3, and of row 1 (by then the
+// total of rows 0-1) to rows 2 and 3.  Lanes a move does not reach add 0.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
 template <int PHASE>
 __device__ __forceinline__ void price_slots(const FfnArgs& a, int T, const moe_expert_handle* table,
                                             const int* active, const int* offsets, SlotRec* recs, int* pref_cost,
@@ -327,12 +343,8 @@ __device__ __forceinline__ void price_slots(const FfnArgs& a, int T, const moe_e
         }
     }
     if (s < 2 * kWave) {   // waves 0 and 1: inclusive scans of 64 slots each
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int vc = __shfl_up(cost, off);
-            const int vi = __shfl_up(items, off);
-            if (lane >= off) { cost += vc; items += vi; }
-        }
+        cost = wave_incl_scan(cost);
+        items = wave_incl_scan(items);
         if (lane == kWave - 1) { wave_tot[2 * (s / kWave)] = cost; wave_tot[2 * (s / kWave) + 1] = items; }
     }
     __syncthreads();
@@ -344,7 +356,7 @@ __device__ __forceinline__ void price_slots(const FfnArgs& a, int T, const moe_e
 }
 
 // Number of prefix entries <= v (the slot whose range holds v), per wave.
-__device__ __forceinline__ int count_le(const int* pref, long v) {
+__device__ __forceinline__ int count_le(const int* pref, int v) {
     const int lane = threadIdx.x & (kWave - 1);
     int n = 0;
 #pragma unroll
@@ -353,14 +365,14 @@ __device__ __forceinline__ int count_le(const int* pref, long v) {
 }
 
 // The item whose cost range holds position P (the total item count past the end).
-__device__ __forceinline__ int item_at(const int* pref_cost, const int* pref_item, int T, long P) {
+__device__ __forceinline__ int item_at(const int* pref_cost, const int* pref_item, int T, int P) {
     const int slot = count_le(pref_cost, P);
     if (slot >= T) return pref_item[kMaxExperts - 1];
     const int c_lo = slot > 0 ? pref_cost[slot - 1] : 0;
     const int i_lo = slot > 0 ? pref_item[slot - 1] : 0;
     const int n_items = pref_item[slot] - i_lo;
     const int per_item = (pref_cost[slot] - c_lo) / n_items;
-    return i_lo + static_cast<int>((P - c_lo) / per_item);
+    return i_lo + (P - c_lo) / per_item;
 }
 
 // ---------------------------------------------------------------------------
@@ -628,9 +640,12 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     constexpr int wps = waves_per_simd<PHASE>();   // workgroups per CU
     const int slot = per_xcd % wps == 0 ? (lb % (per_xcd / wps)) * wps + lb / (per_xcd / wps) : lb;
     const int gw = (xcd * per_xcd + slot) * kWaves + threadIdx.x / kWave;
-    const long C = pref_cost[kMaxExperts - 1];
-    const int begin = item_at(pref_cost, pref_item, T, C * gw / Wn);
-    const int end = item_at(pref_cost, pref_item, T, C * (gw + 1) / Wn);
+    // Range start of wave w: floor(C w / Wn), in 32-bit arithmetic (C is
+    // below 2^31: the launcher checks its bound; (C mod Wn) w < 2^24).
+    const int C = pref_cost[kMaxExperts - 1];
+    const int cq = C / Wn, cr = C - cq * Wn;
+    const int begin = item_at(pref_cost, pref_item, T, cq * gw + cr * gw / Wn);
+    const int end = item_at(pref_cost, pref_item, T, cq * (gw + 1) + cr * (gw + 1) / Wn);
     int it = begin;
     while (it < end) {   // one run per (expert, pass) touched by the range
         const int slot = count_le(pref_item, it);   // < T because it < total items
@@ -701,6 +716,25 @@ int device_cus() {
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 }  // namespace
+
+// The partition sums item costs in 32-bit integers on the device.  Whatever
+// the formats in the handle table, an expert with c tokens has at most
+// c / pass_tokens + 1 passes and sum(c) <= B k, which bounds the total.
+bool ffn_cost_fits(int B, int k, int N, int H, int I) {
+    long long worst = 0;
+    for (int phase = 0; phase < 2; ++phase) {
+        const int rows = phase == 0 ? I : H, cols = phase == 0 ? H : I;
+        const int rb = phase == 0 ? kRbA : kRbB;
+        const long long ipp = (rows / 16 + rb - 1) / rb;
+        for (int fmt : {MOE_W_F32, MOE_W_BF16, MOE_W_INT4_G128}) {
+            const long long tiles = static_cast<long long>(rb) * (weight_row_bytes(fmt, cols) / 64);
+            const long long per_tile = fmt == MOE_W_INT4_G128 ? 14 : 10;
+            const long long passes = static_cast<long long>(B) * k / pass_tokens(fmt) + N;
+            worst = std::max(worst, passes * ipp * tiles * per_tile);
+        }
+    }
+    return worst < (1LL << 31);
+}
 
 // Workspace: SwiGLU activations [B*k, I] (4 bytes per value: fp32, or the
 // split bf16 hi/lo form), then weighted down projections [B*k, H] fp32.
