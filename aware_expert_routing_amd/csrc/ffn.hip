@@ -25,7 +25,8 @@
 //   * phase A: work items are (active expert, 2 row blocks of 16 rows of I);
 //     the wave streams the gate and up tiles of those rows over all of H and
 //     ends with h = silu(g) * u for every token of the expert.
-//   * phase B: items are (active expert, 2 row blocks of H) over all of I;
+//   * phase B: items are (active expert, 2 row blocks of H; 4 for experts
+//     with more than 16 tokens in a pass) over all of I;
 //     the result is scaled by the pair's routing weight.
 //   * combine: y[i] = sum over token i's filled slots, in slot order.
 // Items belong to single waves (no barriers, no LDS staging): each wave owns
@@ -52,8 +53,14 @@ constexpr int kWave = 64;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTileBytes = 1024;
-constexpr int kRbA = 2;   // row blocks per phase-A item
-constexpr int kRbB = 2;   // row blocks per phase-B item
+// Row blocks per work item.  Every weight position also loads the tokens'
+// activation fragments, once per item, so an item of more row blocks spends
+// fewer activation loads per weight byte.  Two row blocks, except in phase B
+// for experts with more than 16 tokens in a pass (two column tiles, and h
+// fragments as large as the weight tile per token): four.
+template <int PHASE, int NT>
+constexpr int rb_per_item() { return PHASE == 1 && NT == 2 ? 4 : 2; }
+__host__ __device__ __forceinline__ int rb_per_item(int phase, int nt) { return phase == 1 && nt == 2 ? 4 : 2; }
 constexpr int kXcds = 8;  // MI355X: 8 XCDs; the grid is a multiple of 8 workgroups
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -137,12 +144,12 @@ struct Act {
 template <int PHASE, int FMT, bool XF32, int NT>
 struct Ring {
     static constexpr int kMatN = PHASE == 0 ? 2 : 1;
-    static constexpr int kRbN = PHASE == 0 ? kRbA : kRbB;
+    static constexpr int kRbN = rb_per_item<PHASE, NT>();
     static constexpr int kW = kMatN * kRbN * (FMT == MOE_W_INT4_G128 ? 6 : 4);   // registers per weight stage
     static constexpr int kX = NT * Act<FMT, XF32>::kRaw * 4;                      // per activation stage
     static constexpr int kAcc = kMatN * kRbN * NT * 4;
     static constexpr int kBudget = (FMT == MOE_W_INT4_G128 && XF32) ? (PHASE == 1 ? 70 : 110)
-                                                                    : (PHASE == 1 ? 90 : ((FMT == MOE_W_INT4_G128 || XF32) ? 150 : 200));
+                                                                    : (PHASE == 1 ? (NT == 2 ? 110 : 90) : ((FMT == MOE_W_INT4_G128 || XF32) ? 150 : 200));
     static constexpr bool kSplit = FMT == MOE_W_INT4_G128 && XF32;
     static constexpr int depth(int x_fixed) {   // x_fixed = 0: X = D
         for (int d = 8; d >= 1; d /= 2)
@@ -156,7 +163,7 @@ struct Ring {
 template <int PHASE, int FMT, bool XF32, int NT>
 struct WStage {
     static constexpr int kMat = PHASE == 0 ? 2 : 1;
-    static constexpr int kRb = PHASE == 0 ? kRbA : kRbB;
+    static constexpr int kRb = rb_per_item<PHASE, NT>();
     u32x4 w[kMat][kRb];
     u32x2 sc[kMat][kRb];                       // INT4 only
 };
@@ -171,7 +178,7 @@ struct XStage {
 template <int PHASE, int FMT, bool XF32, int NT>
 __device__ __forceinline__ void tile_mma(const WStage<PHASE, FMT, XF32, NT>& ws, const XStage<FMT, XF32, NT>& xs_in,
                                          uint32_t keep,
-                                         f32x4 (&acc)[PHASE == 0 ? 2 : 1][PHASE == 0 ? kRbA : kRbB][NT]) {
+                                         f32x4 (&acc)[PHASE == 0 ? 2 : 1][rb_per_item<PHASE, NT>()][NT]) {
     using S = WStage<PHASE, FMT, XF32, NT>;
     struct {
         const u32x4 (&w)[S::kMat][S::kRb];
@@ -286,6 +293,7 @@ struct SlotRec {
     const char* s0;          // INT4 packed scales (or null)
     const char* s1;
     int32_t fmt, first, cnt, ipp;   // ipp: items per token pass
+    int32_t nt;                     // column tiles of the expert's first pass
 };
 
 // Tokens per pass: two 16-token column tiles (one for INT4, whose
@@ -315,7 +323,6 @@ __device__ __forceinline__ void price_slots(const FfnArgs& a, int T, const moe_e
     const int s = threadIdx.x;
     const int lane = s & (kWave - 1);
     const int rows = PHASE == 0 ? a.I : a.H, cols = PHASE == 0 ? a.H : a.I;
-    const int rb = PHASE == 0 ? kRbA : kRbB;
     int cost = 0, items = 0;
     if (s < T) {
         const int e = active[s];
@@ -328,14 +335,16 @@ __device__ __forceinline__ void price_slots(const FfnArgs& a, int T, const moe_e
         r.s1 = PHASE == 0 ? reinterpret_cast<const char*>(h.s_up) : nullptr;
         r.first = offsets[e];
         r.cnt = offsets[e + 1] - r.first;
+        const int pt = pass_tokens(r.fmt);
+        const int nt = col_tiles_for(min(r.cnt, pt));
+        const int rb = rb_per_item(PHASE, nt);
+        r.nt = nt;
         r.ipp = (rows / 16 + rb - 1) / rb;
         recs[s] = r;
         const bool fits = (r.fmt == MOE_W_F32 || r.fmt == MOE_W_BF16 || r.fmt == MOE_W_INT4_G128) &&
                           cols % tile_cols(r.fmt) == 0 && r.cnt > 0;
         if (fits) {
-            const int pt = pass_tokens(r.fmt);
             const int passes = (r.cnt + pt - 1) / pt;
-            const int nt = col_tiles_for(min(r.cnt, pt));
             items = passes * r.ipp;
             const int tiles = rb * (weight_row_bytes(r.fmt, cols) / 64);
             const int per_tile = r.fmt == MOE_W_INT4_G128 ? 12 + 2 * nt : 8 + nt;
@@ -578,11 +587,15 @@ __device__ __forceinline__ void run_nt(const FfnArgs& a, const SlotRec& rec, int
 #define MOE_RUN(FN, NTV)                                                                                  \
     FN<PHASE, FMT, XF32, NTV>(static_cast<const char*>(a.x), a.perm, a.w, a.hbuf, a.dbuf, a.k, a.H, a.I,  \
                               rec.m0, rec.m1, rec.s0, rec.s1, rec.first, rec.cnt, local0, count)
+    // Phase A picks the column tiles per pass; phase B keeps the expert's
+    // (its items' row blocks depend on them), so a last pass of at most 16
+    // tokens of a larger expert runs with a masked second column tile.
+    const bool one = (PHASE == 0 ? rec.cnt : 16 * rec.nt) <= 16;
     if constexpr (hot) {
-        if (rec.cnt <= 16) MOE_RUN(run_items, 1);
+        if (one) MOE_RUN(run_items, 1);
         else MOE_RUN(run_items, 2);
     } else {
-        if (FMT == MOE_W_INT4_G128 || rec.cnt <= 16) MOE_RUN(run_items_call, 1);
+        if (FMT == MOE_W_INT4_G128 || one) MOE_RUN(run_items_call, 1);
         else MOE_RUN(run_items_call, FMT == MOE_W_INT4_G128 ? 1 : 2);
     }
 #undef MOE_RUN
@@ -724,13 +737,15 @@ bool ffn_cost_fits(int B, int k, int N, int H, int I) {
     long long worst = 0;
     for (int phase = 0; phase < 2; ++phase) {
         const int rows = phase == 0 ? I : H, cols = phase == 0 ? H : I;
-        const int rb = phase == 0 ? kRbA : kRbB;
-        const long long ipp = (rows / 16 + rb - 1) / rb;
-        for (int fmt : {MOE_W_F32, MOE_W_BF16, MOE_W_INT4_G128}) {
-            const long long tiles = static_cast<long long>(rb) * (weight_row_bytes(fmt, cols) / 64);
-            const long long per_tile = fmt == MOE_W_INT4_G128 ? 14 : 10;
-            const long long passes = static_cast<long long>(B) * k / pass_tokens(fmt) + N;
-            worst = std::max(worst, passes * ipp * tiles * per_tile);
+        for (int nt = 1; nt <= 2; ++nt) {
+            const int rb = rb_per_item(phase, nt);
+            const long long ipp = (rows / 16 + rb - 1) / rb;
+            for (int fmt : {MOE_W_F32, MOE_W_BF16, MOE_W_INT4_G128}) {
+                const long long tiles = static_cast<long long>(rb) * (weight_row_bytes(fmt, cols) / 64);
+                const long long per_tile = fmt == MOE_W_INT4_G128 ? 14 : 10;
+                const long long passes = static_cast<long long>(B) * k / pass_tokens(fmt) + N;
+                worst = std::max(worst, passes * ipp * tiles * per_tile);
+            }
         }
     }
     return worst < (1LL << 31);
