@@ -67,6 +67,21 @@ def test_bf16_ffn_shapes(N, k, H, I, B, mode, k0, p):
     _run_and_check(layer, host, x, xd, logits, mode, k0, p, TOL["bf16"])
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "f32"])
+def test_experts_with_two_column_tiles(fmt):
+    # B=40 tokens over 4 experts, top-2: every active expert carries more than
+    # 16 tokens, so both phases use two column tiles and phase B uses items of
+    # 4 row blocks; H = 544 gives 34 row blocks, so the last phase-B item has
+    # two clamped row blocks; B=80 adds a second token pass for some experts.
+    for B, seed in ((40, 11), (80, 12)):
+        N, k, H, I = 4, 2, 544, 224
+        layer, host = build_layer(N, k, H, I, seed, fmt=fmt, with_router=False)
+        x, xd = _x(seed, B, H, "bf16" if fmt == "bf16" else "f32")
+        logits = synth.logits(seed, B, N, 1.0)
+        buf, _ = _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL[fmt])
+        assert buf.disp["cnt"].cpu().numpy().max() > 16
+
+
 def test_fp32_activations_with_bf16_experts():
     N, k, H, I, B = 16, 4, 256, 128, 8
     layer, host = build_layer(N, k, H, I, 3, fmt="bf16", with_router=False)
