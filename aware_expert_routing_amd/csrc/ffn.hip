@@ -302,20 +302,6 @@ __host__ __device__ __forceinline__ int pass_tokens(int fmt) { return fmt == MOE
 
 __host__ __device__ __forceinline__ int col_tiles_for(int cnt) { return cnt <= 16 ? 1 : 2; }
 
-// Inclusive prefix sum over the 64 lanes of a wavefront, in registers: DPP
-// row shifts by 1, 2, 4 and 8 scan each row of 16 lanes, then the last lane
-// of row 0 is added to row 1, of row 2 to row 3, and of row 1 (by then the
-// total of rows 0-1) to rows 2 and 3.  Lanes a move does not reach add 0.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
-    return v;
-}
-
 template <int PHASE>
 __device__ __forceinline__ void price_slots(const FfnArgs& a, int T, const moe_expert_handle* table,
                                             const int* active, const int* offsets, SlotRec* recs, int* pref_cost,

@@ -337,12 +337,8 @@ __device__ __forceinline__ void dispatch_block(const int32_t* idx, int B, int N,
         const int c1 = 2 * lane + 1 < N ? cnt_s[2 * lane + 1] : 0;
         int sum = c0 + c1;
         int act = (c0 > 0) + (c1 > 0);
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {   // inclusive scans over lanes
-            const int os = __shfl_up(sum, off, kWave);
-            const int oa = __shfl_up(act, off, kWave);
-            if (lane >= off) { sum += os; act += oa; }
-        }
+        sum = wave_incl_scan(sum);   // inclusive scans over lanes
+        act = wave_incl_scan(act);
         const int excl = sum - (c0 + c1);
         const int aexcl = act - ((c0 > 0) + (c1 > 0));
         if (2 * lane < N) {
@@ -355,8 +351,8 @@ __device__ __forceinline__ void dispatch_block(const int32_t* idx, int B, int N,
             offsets[2 * lane + 1] = excl + c0;
             cnt[2 * lane + 1] = c1;
         }
-        const int total = __shfl(sum, kWave - 1, kWave);
-        const int tact = __shfl(act, kWave - 1, kWave);
+        const int total = __builtin_amdgcn_readlane(sum, kWave - 1);
+        const int tact = __builtin_amdgcn_readlane(act, kWave - 1);
         if (lane == 0) {
             off_s[N] = total;
             offsets[N] = total;
@@ -386,6 +382,17 @@ template <bool kCoherent>
 __device__ __forceinline__ float load_logit(const float* p) {
     if constexpr (kCoherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else return *p;
+}
+// Two adjacent logits (p 8-byte aligned) in one load.
+template <bool kCoherent>
+__device__ __forceinline__ void load_logit2(const float* p, float& a, float& b) {
+    uint64_t v;
+    if constexpr (kCoherent)
+        v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        v = *reinterpret_cast<const uint64_t*>(p);
+    a = __uint_as_float(static_cast<uint32_t>(v));
+    b = __uint_as_float(static_cast<uint32_t>(v >> 32));
 }
 
 // The routing of a whole batch by the calling workgroup, one token per group
@@ -423,13 +430,30 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     if (threadIdx.x < kMaxExperts / 32) sbase[threadIdx.x] = 0u;
 
     float L[R][P];
+    if ((N & 1) == 0) {   // every lane's experts come in 8-byte aligned pairs (e_first and i N are even)
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int i = Gr::kPerWave * (wave + r * nwaves) + lane / G;
+        for (int r = 0; r < R; ++r) {
+            const int i = Gr::kPerWave * (wave + r * nwaves) + lane / G;
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const int e = e_first + j;
-            L[r][j] = (i < B_real && e < N) ? load_logit<kCoherent>(logits + i * N + e) : kNegInf;
+            for (int j = 0; j < P; j += 2) {
+                const int e = e_first + j;
+                if (i < B_real && e < N) {
+                    load_logit2<kCoherent>(logits + i * N + e, L[r][j], L[r][j + 1]);
+                } else {
+                    L[r][j] = kNegInf;
+                    L[r][j + 1] = kNegInf;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = Gr::kPerWave * (wave + r * nwaves) + lane / G;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                const int e = e_first + j;
+                L[r][j] = (i < B_real && e < N) ? load_logit<kCoherent>(logits + i * N + e) : kNegInf;
+            }
         }
     }
     __syncthreads();
