@@ -708,11 +708,59 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(const XT* _
     }
 }
 
+// Logits of the kFusedExperts experts e0 .. for tokens t0 + 4 g .. + 3 by
+// group g of kGemvThreads threads: each thread multiplies its 8 columns of
+// the 4 experts' router rows with the same columns of the 4 tokens, so one
+// workgroup reads the activations of its 16 tokens once (not once per
+// expert).  Partial sums per row of 16 lanes land in part[row][4 e + t].
+template <typename XT>
+__device__ __forceinline__ void gemv_4x4(const XT* __restrict__ x, const float* __restrict__ w_r, int H, int N,
+                                         int e0, int t0, int nt, int g, int tid, float (*part)[kGemvTok]) {
+    constexpr int kE = 4, kT = 4;
+    const int lane = tid & (kWave - 1);
+    const int col0 = 8 * lane + 512 * (tid / kWave);
+    const int stride = 8 * kGemvThreads;
+    float acc[kE][kT];
+#pragma unroll
+    for (int e = 0; e < kE; ++e)
+#pragma unroll
+        for (int t = 0; t < kT; ++t) acc[e][t] = 0.0f;
+    for (int c = col0; c < H; c += stride) {
+        float wv[kE][8];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            if (e0 + e < N) {
+                load_x8<float>(w_r + static_cast<size_t>(e0 + e) * H + c, wv[e]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) wv[e][q] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            if (kT * g + t >= nt) continue;
+            float xv[8];
+            load_x8<XT>(x + static_cast<size_t>(t0 + kT * g + t) * H + c, xv);
+#pragma unroll
+            for (int e = 0; e < kE; ++e)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[e][t] = __builtin_fmaf(wv[e][q], xv[q], acc[e][t]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < kE; ++e)
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            const float sum = row16_sum_f(acc[e][t]);
+            if ((tid & 15) == 0) part[tid / 16][kT * e + t] = sum;
+        }
+}
+
 // Router logits, routing and dispatch in one launch.  Workgroup (gx, gy)
 // computes the logits of experts kFusedExperts gx .. + kFusedExperts - 1 for
-// tokens 16 gy .. 16 gy + 15 (one group of kGemvThreads threads per expert,
-// as router_logits_kernel), writes them with device-scope stores, waits for
-// those stores and counts itself done.  The workgroup that completes the
+// tokens 16 gy .. 16 gy + 15 (group g of kGemvThreads threads takes tokens
+// 4 g .. 4 g + 3 of all kFusedExperts experts), writes them with
+// device-scope stores, waits for those stores and counts itself done.  The workgroup that completes the
 // count routes and dispatches the whole batch (its 16 wavefronts, one token
 // per wavefront at a time), reading the logits with device-scope loads, and
 // clears the count for the next call.  No workgroup waits for another.
@@ -734,19 +782,23 @@ __global__ __launch_bounds__(kGemvThreads * kFusedExperts) void router_route_ker
         const int32_t* __restrict__ k0_by_batch, int32_t* __restrict__ sync) {
     __shared__ float part[kFusedExperts][kGemvThreads / 16][kGemvTok];
     __shared__ int last_s;
+    static_assert(kFusedExperts == 4 && kGemvTok == 16, "gemv_4x4 layout");
     const int g = threadIdx.x / kGemvThreads;
     const int tid = threadIdx.x - g * kGemvThreads;
-    const int e = blockIdx.x * kFusedExperts + g;
+    const int e0 = blockIdx.x * kFusedExperts;
     const int t0 = blockIdx.y * kGemvTok;
     const int nt = min(kGemvTok, B - t0);
-    if (e < N) gemv_expert<XT>(x, w_r, H, e, t0, nt, tid, part[g]);
+    gemv_4x4<XT>(x, w_r, H, N, e0, t0, nt, g, tid, part[g]);
     __syncthreads();
-    if (e < N && tid < nt) {
-        float sum = 0.0f;
+    if (threadIdx.x < kFusedExperts * kGemvTok) {   // (expert, token) = (threadIdx / 16, threadIdx % 16)
+        const int el = threadIdx.x / kGemvTok, t = threadIdx.x % kGemvTok;
+        if (e0 + el < N && t < nt) {
+            float sum = 0.0f;
 #pragma unroll
-        for (int r = 0; r < kGemvThreads / 16; ++r) sum += part[g][r][tid];
-        __hip_atomic_store(logits + static_cast<size_t>(t0 + tid) * N + e, sum, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+            for (int r = 0; r < kGemvThreads / 16; ++r) sum += part[t / 4][r][4 * el + t % 4];
+            __hip_atomic_store(logits + static_cast<size_t>(t0 + t) * N + e0 + el, sum, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     wait_vmem();
     __syncthreads();
