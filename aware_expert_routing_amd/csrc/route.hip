@@ -236,9 +236,9 @@ __device__ __forceinline__ int group_select(Tok<Grp<G>::kPer>& t, bool active, i
 
 // Write one token's selected experts: the lane owning the expert of slot r
 // writes idx[i k + r] and w[i k + r] = e / denom, e = exp(l - l_top); denom is
-// the sum of e over the kept experts (renorm) or Z (raw softmax), the
-// quotient taken in double and rounded once to fp32.  Slots got..k-1 get
-// expert -1 and weight 0.
+// the sum of e over the kept experts (renorm) or Z (raw softmax), formed in
+// double as e times the double reciprocal of denom (one division per lane)
+// and rounded once to fp32.  Slots got..k-1 get expert -1 and weight 0.
 template <int G>
 __device__ __forceinline__ void group_write(const Tok<Grp<G>::kPer>& t, int i, int k, int got, float top, bool renorm,
                                             float Z, int32_t* idx, float* w, int32_t* idx_copy) {
@@ -252,13 +252,14 @@ __device__ __forceinline__ void group_write(const Tok<Grp<G>::kPer>& t, int i, i
         loc += ev[j];
     }
     const double denom = renorm ? Grp<G>::sum_f64(loc) : static_cast<double>(Z);
+    const double inv = 1.0 / denom;
 #pragma unroll
     for (int j = 0; j < P; ++j) {
         if (t.slot[j] < 0) continue;
         const int q = i * k + t.slot[j];
         idx[q] = P * l + j;
         if (idx_copy != nullptr) idx_copy[q] = P * l + j;
-        w[q] = static_cast<float>(ev[j] / denom);
+        w[q] = static_cast<float>(ev[j] * inv);
     }
     if (l >= got && l < k) {
         idx[i * k + l] = -1;
