@@ -38,10 +38,11 @@
 // second MFMA with the constant -136 removes the offset (u - 8 = q), and the
 // group's per-row fp16 scale multiplies the result into the accumulator.
 // fp32 activations meeting bf16/INT4 weights enter as bf16 hi + lo pairs.
-// Phase A stores h of a bf16/INT4 expert already in that form (per 8
-// columns: 8 bf16 hi, then 8 bf16 lo; 4 bytes per value as in fp32), so
-// phase B, which reads each h fragment once per row block, does no
-// splitting; an fp32 expert's h stays fp32.
+// Phase A stores h of a bf16 expert already in that form (per 8 columns:
+// 8 bf16 hi, then 8 bf16 lo; 4 bytes per value as in fp32), so phase B,
+// which reads each h fragment once per row block, does no splitting; an
+// fp32 expert's h stays fp32; an INT4 expert's h is stored in bf16 (W4A16:
+// its down projection takes bf16 activations, as its gate/up take bf16 x).
 #include "internal.h"
 
 #include <algorithm>
@@ -522,6 +523,11 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
                         const int c = (rb0 + r) * 16 + 4 * q;   // first of this lane's 4 columns of h
                         if constexpr (FMT == MOE_W_F32) {
                             *reinterpret_cast<float4*>(hrow + c) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+                        } else if constexpr (FMT == MOE_W_INT4_G128) {
+                            // INT4 experts take h in bf16 (W4A16), row-major in the row's first 2 I bytes
+                            const uint2 hb = make_uint2(bf16_rne(hv[0]) | (bf16_rne(hv[1]) << 16),
+                                                        bf16_rne(hv[2]) | (bf16_rne(hv[3]) << 16));
+                            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(hrow) + 2 * c) = hb;
                         } else {
                             // split layout: per 8 columns, 8 bf16 hi then 8 bf16 lo
                             uint32_t hi[2], lo[2];
@@ -590,7 +596,7 @@ __device__ __forceinline__ void run_nt(const FfnArgs& a, const SlotRec& rec, int
 template <int PHASE, bool XF32>
 __device__ __forceinline__ void run_fmt(const FfnArgs& a, const SlotRec& rec, int local0, int count) {
     if (rec.fmt == MOE_W_BF16) run_nt<PHASE, MOE_W_BF16, XF32>(a, rec, local0, count);
-    else if (rec.fmt == MOE_W_INT4_G128) run_nt<PHASE, MOE_W_INT4_G128, XF32>(a, rec, local0, count);
+    else if (rec.fmt == MOE_W_INT4_G128) run_nt<PHASE, MOE_W_INT4_G128, PHASE == 0 && XF32>(a, rec, local0, count);
     else run_nt<PHASE, MOE_W_F32, XF32>(a, rec, local0, count);
 }
 

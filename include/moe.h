@@ -214,7 +214,10 @@ size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
  *            format may differ
  *   x      : [B, H] (x_dtype); with bf16/INT4 experts an fp32 activation a
  *            enters the products as hi = bf16(a) plus lo = bf16(a - hi)
- *            (about 16 significant bits); bf16 inputs are used exactly
+ *            (about 16 significant bits); bf16 inputs are used exactly.
+ *            The SwiGLU output a enters the down projection the same split
+ *            way for bf16 experts, exactly for fp32 experts, and rounded to
+ *            bf16 for INT4 experts (4-bit weights, 16-bit activations)
  *   idx, w : routing output [B, k]; offsets, perm, active, T: dispatch output
  *   y      : [B, H] fp32, overwritten
  *   ws     : workspace of at least moe_ffn_workspace_bytes(B, k, H, I) bytes,
