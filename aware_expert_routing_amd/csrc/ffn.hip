@@ -351,6 +351,16 @@ __device__ __forceinline__ void price_slots(const FfnArgs& a, int T, const moe_e
     __syncthreads();
 }
 
+// floor(n / d) for 0 <= n < 2^31 and 0 < d whose quotient is below 2^20:
+// a float reciprocal estimate is within one of the quotient (relative error
+// about 2^-22), and one correction step in each direction makes it exact.
+__device__ __forceinline__ int div_small(int n, int d) {
+    int q = static_cast<int>(static_cast<float>(n) * __builtin_amdgcn_rcpf(static_cast<float>(d)));
+    const int r = n - q * d;
+    q += (r >= d ? 1 : 0) - (r < 0 ? 1 : 0);
+    return q;
+}
+
 // Number of prefix entries <= v (the slot whose range holds v), per wave.
 __device__ __forceinline__ int count_le(const int* pref, int v) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -367,8 +377,8 @@ __device__ __forceinline__ int item_at(const int* pref_cost, const int* pref_ite
     const int c_lo = slot > 0 ? pref_cost[slot - 1] : 0;
     const int i_lo = slot > 0 ? pref_item[slot - 1] : 0;
     const int n_items = pref_item[slot] - i_lo;
-    const int per_item = (pref_cost[slot] - c_lo) / n_items;
-    return i_lo + (P - c_lo) / per_item;
+    const int per_item = div_small(pref_cost[slot] - c_lo, n_items);   // quotients: item cost, item index
+    return i_lo + div_small(P - c_lo, per_item);
 }
 
 // ---------------------------------------------------------------------------
@@ -643,7 +653,8 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     // when items are fewer than waves the idle waves spread evenly over CUs.
     const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds, lb = blockIdx.x / kXcds;
     constexpr int wps = waves_per_simd<PHASE>();   // workgroups per CU
-    const int slot = per_xcd % wps == 0 ? (lb % (per_xcd / wps)) * wps + lb / (per_xcd / wps) : lb;
+    const int cus = per_xcd / wps, lq = div_small(lb, cus > 0 ? cus : 1);
+    const int slot = per_xcd % wps == 0 ? (lb - lq * cus) * wps + lq : lb;
     const int gw = (xcd * per_xcd + slot) * kWaves + threadIdx.x / kWave;
     // Range start of wave w: floor(C w / Wn), in 32-bit arithmetic (C is
     // below 2^31: the launcher checks its bound; (C mod Wn) w < 2^24).
@@ -657,7 +668,7 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
         const int i_lo = slot > 0 ? pref_item[slot - 1] : 0;
         SlotRec rec = recs[slot];
         const int ipp = uni(rec.ipp);
-        const int pass = (it - i_lo) / ipp;
+        const int pass = div_small(it - i_lo, ipp);
         const int local0 = it - i_lo - pass * ipp;
         const int count = uni(min(end, i_lo + (pass + 1) * ipp) - it);
         const int pt = pass_tokens(rec.fmt);
