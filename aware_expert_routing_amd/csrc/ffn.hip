@@ -322,16 +322,19 @@ __device__ __forceinline__ void price_slots(const FfnArgs& a, int T, const moe_e
         r.s1 = PHASE == 0 ? reinterpret_cast<const char*>(h.s_up) : nullptr;
         r.first = offsets[e];
         r.cnt = offsets[e + 1] - r.first;
-        const int pt = pass_tokens(r.fmt);
-        const int nt = col_tiles_for(min(r.cnt, pt));
-        const int rb = rb_per_item(PHASE, nt);
+        // pass tokens (16 or 32), row blocks per item (2 or 4) and tile
+        // columns (16, 32 or 128) are powers of two: shifts and masks
+        const int lpt = r.fmt == MOE_W_INT4_G128 ? 4 : 5;
+        const int nt = col_tiles_for(min(r.cnt, 1 << lpt));
+        const int lrb = rb_per_item(PHASE, nt) == 4 ? 2 : 1;
+        const int rb = 1 << lrb;
         r.nt = nt;
-        r.ipp = (rows / 16 + rb - 1) / rb;
+        r.ipp = (rows / 16 + rb - 1) >> lrb;
         recs[s] = r;
         const bool fits = (r.fmt == MOE_W_F32 || r.fmt == MOE_W_BF16 || r.fmt == MOE_W_INT4_G128) &&
-                          cols % tile_cols(r.fmt) == 0 && r.cnt > 0;
+                          (cols & (tile_cols(r.fmt) - 1)) == 0 && r.cnt > 0;
         if (fits) {
-            const int passes = (r.cnt + pt - 1) / pt;
+            const int passes = (r.cnt + (1 << lpt) - 1) >> lpt;
             items = passes * r.ipp;
             const int tiles = rb * (weight_row_bytes(r.fmt, cols) / 64);
             const int per_tile = r.fmt == MOE_W_INT4_G128 ? 12 + 2 * nt : 8 + nt;
