@@ -738,7 +738,9 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // The partition sums item costs in 32-bit integers on the device.  Whatever
 // the formats in the handle table, an expert with c tokens has at most
-// c / pass_tokens + 1 passes and sum(c) <= B k, which bounds the total.
+// c / pass_tokens + 1 passes and sum(c) <= B k, which bounds the total.  At
+// the largest accepted sizes (B = 128, k = 16, H = I = 16384) the bound is
+// about 2.01e9, so the check is a guard for future limits.
 bool ffn_cost_fits(int B, int k, int N, int H, int I) {
     long long worst = 0;
     for (int phase = 0; phase < 2; ++phase) {

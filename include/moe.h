@@ -229,9 +229,9 @@ size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
  * y; its pairs' outputs are undefined).  Each active expert's weights are
  * streamed from HBM once per pass of up to 32 of its tokens (16 for INT4).
  * Errors: MOE_EINVAL for null pointers, sizes out of range, a short or
- * misaligned workspace or table; MOE_EUNSUPPORTED for H or I above 16384, or
- * when the work partition's total cost could exceed 2^31 (very large
- * B*k with H*I near the limit).
+ * misaligned workspace or table; MOE_EUNSUPPORTED for H or I above 16384 (or,
+ * as a guard that the current size limits never reach, when the work
+ * partition's total cost could exceed 2^31).
  */
 int moe_expert_ffn(const moe_expert_handle *table, int N, int H, int I, const void *x,
                    int x_dtype, const int32_t *idx, const float *w, const int32_t *offsets,
