@@ -104,8 +104,21 @@ def test_int4_and_mixed_experts(int4):
             assert np.array_equal(q["s_" + name].cpu().numpy().view(np.uint16), host[e]["s_" + name])
     x, xd = _x(4, B, H, "bf16")
     logits = (synth.logits(4, B, N, 1.0) + synth.zipf_bias(N, 1.1)[None, :]).astype(np.float32)
-    _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL["int4"])
+    buf, _ = _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL["int4"])
+    if int4 == "all":   # Zipf-hot INT4 experts take more than one pass of 16 tokens
+        assert buf.disp["cnt"].cpu().numpy().max() > 16
     _run_and_check(layer, host, x, xd, logits, "oea", 2, 1.0, TOL["int4"])
+
+
+def test_int4_experts_with_fp32_activations():
+    # fp32 x meets INT4 tiles as bf16 hi + lo pairs (one activation stage,
+    # deeper weight ring); h then enters the down projection in bf16
+    N, k, H, I, B = 8, 2, 512, 256, 24
+    layer, host = build_layer(N, k, H, I, 5, fmt="bf16", int4_experts=range(N), with_router=False)
+    x, xd = _x(5, B, H, "f32")
+    logits = synth.logits(5, B, N, 1.0)
+    _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL["int4"])
+    _run_and_check(layer, host, x, xd, logits, "oea", 1, 1.0, TOL["int4"])
 
 
 def test_publish_switches_version():
