@@ -540,10 +540,12 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
                 for (int j = 0; j < P; ++j) full[j] = (real && e_first + j < N) ? order_key(t.l[j]) : 0u;
                 group_kth<G>(full, real, max_p, th, eth);
             }
+            // a lane's P experts (P divides 32) share one word of the S_base mask
+            const uint32_t sw = sbase[e_first >> 5] >> (e_first & 31);
 #pragma unroll
             for (int j = 0; j < P; ++j) {
                 const int e = e_first + j;
-                bool a = t.key[j] != 0u && ((sbase[e >> 5] >> (e & 31)) & 1u);
+                bool a = t.key[j] != 0u && ((sw >> j) & 1u);
                 if (!pruned && max_p < N) a = a && (t.key[j] > th || (t.key[j] == th && e <= eth));
                 if (!a) t.key[j] = 0u;
             }
