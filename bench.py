@@ -45,8 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["oea", "topk"], default=None,
-                    help="time only this routing (for profiler runs)")
+    ap.add_argument("--only", choices=["oea", "topk", "mixed"], default=None,
+                    help="time only this routing, or only the mixed bf16/INT4 layer at B=32 (for profiler runs)")
     ap.add_argument("--no-extended", action="store_true",
                     help="skip the batch sweep, the 235B-shaped layer and the mixed INT4 layer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -222,6 +222,10 @@ def main():
             graph_us_per_layer=graph_wall / args.steps * 1e6,
             graph_gbps=layer_bytes / graph_wall / 1e9,
         )
+
+    if args.only == "mixed":   # profiler runs of the mixed-residency layer alone (Qwen3-30B shape)
+        print(json.dumps({"mixed_int4": mixed_int4(layers, wr_dev, N, k, H, I, gate, up, down)}), flush=True)
+        return
 
     results = {}
     modes = [("oea", args.k0), ("topk", 0), ("oea", 5)]
