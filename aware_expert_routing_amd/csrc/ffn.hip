@@ -395,11 +395,12 @@ __device__ __forceinline__ int item_at(const int* pref_cost, const int* pref_ite
 // Arguments are plain values (no struct in private memory); every one is
 // wave-uniform and is moved to SGPRs, so the ring's loads and waits are
 // scheduled per stage rather than behind divergent branches.
-template <int PHASE, int FMT, bool XF32, int NT>
+template <int PHASE, int FMT, bool XF32, int NT, int PRE = 0>
 __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_in, const float* w_in,
                                        float* hbuf_in, float* dbuf_in, int k_in, int H_in, int I_in,
                                        const char* m0, const char* m1, const char* s0, const char* s1,
-                                       int first_in, int cnt_in, int local0_in, int count_in) {
+                                       int first_in, int cnt_in, int local0_in, int count_in,
+                                       const WStage<PHASE, FMT, XF32, NT>* pre = nullptr, int pre_pair = 0) {
     const int local0 = uni(local0_in), count = uni(count_in);
     const int k = uni(k_in), H = uni(H_in), I = uni(I_in);
     const char* xg = uni_ptr(x_in);
@@ -430,6 +431,10 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
     int pair[NT];
     float wt[NT];           // phase B: the pairs' routing weights
 
+    // PRE: the caller has already issued the first PRE weight stages of the
+    // first item (the same tiles this function would load) into pre[], and
+    // this lane's perm entry into pre_pair (one column tile).
+    static_assert(PRE == 0 || NT == 1, "pre-issued runs have one column tile");
     Wst ring[D];
     Xst xring[X];
     auto issue = [&](Wst& st, int item, int s) {
@@ -475,11 +480,15 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
     // The weight stages go out first; the token lookups (perm, then the
     // activation rows) follow, so their round trips overlap the weights'.
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(ring[d], 0, d);
+    for (int d = 0; d < D; ++d) {
+        if (d < PRE) ring[d] = pre[d];
+        else issue(ring[d], 0, d);
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int tok = 16 * t + n;
-        pair[t] = ((const __attribute__((address_space(1))) int32_t*)perm)[first + (tok < cnt ? tok : 0)];
+        if constexpr (PRE > 0) pair[t] = pre_pair;
+        else pair[t] = ((const __attribute__((address_space(1))) int32_t*)perm)[first + (tok < cnt ? tok : 0)];
         if constexpr (PHASE == 0)
             arow[t] = xg + static_cast<size_t>(pair[t] / k) * H * (XF32 ? 4 : 2);
         else
@@ -627,6 +636,7 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     __shared__ u32x4 table_l[kMaxExperts * 4];   // the N handles, 4 x 16 bytes each
     __shared__ int active_l[kMaxExperts];
     __shared__ int offsets_l[kMaxExperts + 1];
+    __shared__ int odd_l[kWaves];
     // Stage the handle table, active list and offsets with independent loads
     // (one round trip) instead of following active -> handle per slot.  The
     // loads take clamped (in-bounds) addresses and are all issued before the
@@ -639,13 +649,16 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     const u32x4 t1 = load_a(tb + 16 * min(tid + kThreads, nc - 1));
     const int act = ((const __attribute__((address_space(1))) int32_t*)a.active)[min(tid, a.N - 1)];
     const int off = ((const __attribute__((address_space(1))) int32_t*)a.offsets)[min(tid, a.N)];
+    const int off1 = ((const __attribute__((address_space(1))) int32_t*)a.offsets)[min(tid + 1, a.N)];
+    const int fmt = ((const __attribute__((address_space(1))) int32_t*)tb)[16 * min(tid, a.N - 1)];
     if (tid < nc) table_l[tid] = t0;
     if (tid + kThreads < nc) table_l[tid + kThreads] = t1;
     if (tid < a.N) active_l[tid] = act;
     if (tid <= a.N) offsets_l[tid] = off;
+    // Expert tid outside the uniform case below: active and not bf16 with at most 16 tokens.
+    const uint64_t odd = __ballot(tid < a.N && off1 > off && (fmt != MOE_W_BF16 || off1 - off > 16));
+    if ((tid & (kWave - 1)) == 0) odd_l[tid / kWave] = odd != 0;
     __syncthreads();
-    price_slots<PHASE>(a, T, reinterpret_cast<const moe_expert_handle*>(table_l), active_l, offsets_l, recs,
-                       pref_cost, pref_item, wave_tot);
     const int Wn = gridDim.x * kWaves;
     // XCD- and CU-aware numbering.  Workgroups are dealt to the 8 XCDs
     // round-robin (blockIdx % 8) and, inside an XCD, to its CUs round-robin,
@@ -659,6 +672,50 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     const int cus = per_xcd / wps, lq = div_small(lb, cus > 0 ? cus : 1);
     const int slot = per_xcd % wps == 0 ? (lb - lq * cus) * wps + lq : lb;
     const int gw = (xcd * per_xcd + slot) * kWaves + threadIdx.x / kWave;
+    // Speculative first ring stages.  When every active expert is bf16 with
+    // at most 16 tokens (and phase A's activations are bf16), every item
+    // costs the same and wave gw's first item is floor(T ipp gw / Wn): the
+    // wave issues that item's first weight stages now, while the pricing
+    // below runs, and uses them if the pricing agrees (they are the tiles the
+    // run would load first).  Other batches skip it: there a wrong guess
+    // would cost HBM reads.
+    using WsHot = WStage<PHASE, MOE_W_BF16, PHASE == 1, 1>;
+    constexpr int DH = Ring<PHASE, MOE_W_BF16, PHASE == 1, 1>::D;
+    WsHot spec[DH];
+    int s_g = -1, l0_g = -1, pair_g = 0;
+    bool uniform = PHASE == 1 || a.x_dtype == MOE_DT_BF16;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) uniform = uniform && odd_l[w] == 0;
+    {
+        const int nrb = (PHASE == 0 ? a.I : a.H) / 16, ipp = (nrb + 1) / 2;   // two row blocks per item
+        const int ng = T * ipp, bg = ng * gw / Wn, eg = ng * (gw + 1) / Wn;   // < 2^31
+        if (uniform && bg < eg) {
+            const int sg = div_small(bg, ipp), lg = bg - sg * ipp;
+            const int e = active_l[sg];
+            const moe_expert_handle& h = reinterpret_cast<const moe_expert_handle*>(table_l)[e];
+            s_g = uni(sg);
+            l0_g = uni(lg);
+            // the perm entry first: the run waits for it alone, not for the weights behind it
+            const int f = offsets_l[e], c = offsets_l[e + 1] - f, n = threadIdx.x & 15;
+            pair_g = ((const __attribute__((address_space(1))) int32_t*)a.perm)[f + (n < c ? n : 0)];
+            const char* m[2] = {uni_ptr(static_cast<const char*>(PHASE == 0 ? h.w_gate : h.w_down)),
+                                uni_ptr(static_cast<const char*>(PHASE == 0 ? h.w_up : h.w_down))};
+            const int S = weight_row_bytes(MOE_W_BF16, PHASE == 0 ? a.H : a.I) / 64;
+            const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+            for (int d = 0; d < DH; ++d)
+#pragma unroll
+                for (int mm = 0; mm < WsHot::kMat; ++mm)
+#pragma unroll
+                    for (int r = 0; r < WsHot::kRb; ++r) {
+                        const int rb = min(l0_g * WsHot::kRb + r, nrb - 1);
+                        const long tile = static_cast<long>(rb) * S + min(d, S - 1);
+                        spec[d].w[mm][r] = load_w(m[mm] + tile * kTileBytes + lane * 16);
+                    }
+        }
+    }
+    price_slots<PHASE>(a, T, reinterpret_cast<const moe_expert_handle*>(table_l), active_l, offsets_l, recs,
+                       pref_cost, pref_item, wave_tot);
     // Range start of wave w: floor(C w / Wn), in 32-bit arithmetic (C is
     // below 2^31: the launcher checks its bound; (C mod Wn) w < 2^24).
     const int C = pref_cost[kMaxExperts - 1];
@@ -666,6 +723,24 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     const int begin = item_at(pref_cost, pref_item, T, cq * gw + cr * gw / Wn);
     const int end = item_at(pref_cost, pref_item, T, cq * (gw + 1) + cr * (gw + 1) / Wn);
     int it = begin;
+    // The speculated item: the range starts at item 0 of the first pass of a
+    // bf16 expert with at most 16 tokens.  Peeled out of the loop so that the
+    // speculative stages are not live across the other runs.
+    if (s_g >= 0 && it < end) {
+        const int slot = count_le(pref_item, it);
+        const int i_lo = slot > 0 ? pref_item[slot - 1] : 0;
+        const SlotRec rec = recs[slot];
+        const int ipp = uni(rec.ipp);
+        if (slot == s_g && it - i_lo == l0_g && rec.fmt == MOE_W_BF16 && rec.cnt <= 16) {
+            const int count = uni(min(end, i_lo + ipp) - it);
+            // no use of the perm entry may move above this point (its wait would stall the pricing)
+            asm volatile("" : "+v"(pair_g));
+            run_items<PHASE, MOE_W_BF16, PHASE == 1, 1, DH>(static_cast<const char*>(a.x), a.perm, a.w, a.hbuf,
+                a.dbuf, a.k, a.H, a.I, rec.m0, rec.m1, rec.s0, rec.s1, rec.first, rec.cnt, l0_g, count, spec,
+                pair_g);
+            it += count;
+        }
+    }
     while (it < end) {   // one run per (expert, pass) touched by the range
         const int slot = count_le(pref_item, it);   // < T because it < total items
         const int i_lo = slot > 0 ? pref_item[slot - 1] : 0;
