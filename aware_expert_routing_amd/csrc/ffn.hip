@@ -142,10 +142,10 @@ struct Act {
 // stage frees the registers for a deeper weight ring.  The depths come from
 // a register budget per case (the rest holds addresses and temporaries; the
 // split and INT4 paths need more temporaries).
-template <int PHASE, int FMT, bool XF32, int NT>
+template <int PHASE, int FMT, bool XF32, int NT, int RB = rb_per_item<PHASE, NT>()>
 struct Ring {
     static constexpr int kMatN = PHASE == 0 ? 2 : 1;
-    static constexpr int kRbN = rb_per_item<PHASE, NT>();
+    static constexpr int kRbN = RB;
     static constexpr int kW = kMatN * kRbN * (FMT == MOE_W_INT4_G128 ? 6 : 4);   // registers per weight stage
     static constexpr int kX = NT * Act<FMT, XF32>::kRaw * 4;                      // per activation stage
     static constexpr int kAcc = kMatN * kRbN * NT * 4;
@@ -161,10 +161,10 @@ struct Ring {
     static constexpr int X = kSplit ? 1 : D;
 };
 
-template <int PHASE, int FMT, bool XF32, int NT>
+template <int PHASE, int FMT, bool XF32, int NT, int RB = rb_per_item<PHASE, NT>()>
 struct WStage {
     static constexpr int kMat = PHASE == 0 ? 2 : 1;
-    static constexpr int kRb = rb_per_item<PHASE, NT>();
+    static constexpr int kRb = RB;
     u32x4 w[kMat][kRb];
     u32x2 sc[kMat][kRb];                       // INT4 only
 };
@@ -176,11 +176,11 @@ struct XStage {
 // Accumulate one tile (all row blocks, matrices and column tiles).  `keep`
 // is all ones, or zero for a padding position: the activation bits are
 // ANDed with it, so a padding tile adds exact zeros without a branch.
-template <int PHASE, int FMT, bool XF32, int NT>
-__device__ __forceinline__ void tile_mma(const WStage<PHASE, FMT, XF32, NT>& ws, const XStage<FMT, XF32, NT>& xs_in,
+template <int PHASE, int FMT, bool XF32, int NT, int RB>
+__device__ __forceinline__ void tile_mma(const WStage<PHASE, FMT, XF32, NT, RB>& ws, const XStage<FMT, XF32, NT>& xs_in,
                                          uint32_t keep,
-                                         f32x4 (&acc)[PHASE == 0 ? 2 : 1][rb_per_item<PHASE, NT>()][NT]) {
-    using S = WStage<PHASE, FMT, XF32, NT>;
+                                         f32x4 (&acc)[PHASE == 0 ? 2 : 1][RB][NT]) {
+    using S = WStage<PHASE, FMT, XF32, NT, RB>;
     struct {
         const u32x4 (&w)[S::kMat][S::kRb];
         const u32x2 (&sc)[S::kMat][S::kRb];
@@ -384,6 +384,61 @@ __device__ __forceinline__ int item_at(const int* pref_cost, const int* pref_ite
     return i_lo + div_small(P - c_lo, per_item);
 }
 
+// Write one item's results for every real token of its column tiles:
+// phase A h = silu(g) * u in the expert's h format, phase B the pair's
+// routing weight times the down projection.  acc[m][r][t]: matrix m (gate,
+// up), row block r (first row block rb0), column tile t (tokens 16 t + n).
+template <int PHASE, int FMT, int KMAT, int KRB, int NT>
+__device__ __forceinline__ void store_item(const f32x4 (&acc)[KMAT][KRB][NT], const int (&pair)[NT],
+                                           const float (&wt)[NT], float* hbuf, float* dbuf, int H, int I,
+                                           int rb0, int nrb, int cnt, int n, int q) {
+    constexpr int kMat = KMAT, kRb = KRB;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (16 * t + n >= cnt) continue;
+        if constexpr (PHASE == 0) {
+            float* hrow = hbuf + static_cast<size_t>(pair[t]) * I;
+#pragma unroll
+            for (int r = 0; r < kRb; ++r) {
+                if (rb0 + r >= nrb) continue;
+                const f32x4 g = acc[0][r][t], u = acc[kMat - 1][r][t];
+                const float hv[4] = {silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w};
+                const int c = (rb0 + r) * 16 + 4 * q;   // first of this lane's 4 columns of h
+                if constexpr (FMT == MOE_W_F32) {
+                    *reinterpret_cast<float4*>(hrow + c) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+                } else if constexpr (FMT == MOE_W_INT4_G128) {
+                    // INT4 experts take h in bf16 (W4A16), row-major in the row's first 2 I bytes
+                    const uint2 hb = make_uint2(bf16_rne(hv[0]) | (bf16_rne(hv[1]) << 16),
+                                                bf16_rne(hv[2]) | (bf16_rne(hv[3]) << 16));
+                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(hrow) + 2 * c) = hb;
+                } else {
+                    // split layout: per 8 columns, 8 bf16 hi then 8 bf16 lo
+                    uint32_t hi[2], lo[2];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const uint32_t a = bf16_rne(hv[2 * j]), b = bf16_rne(hv[2 * j + 1]);
+                        hi[j] = a | (b << 16);
+                        lo[j] = bf16_rne(hv[2 * j] - __uint_as_float(a << 16)) |
+                                (bf16_rne(hv[2 * j + 1] - __uint_as_float(b << 16)) << 16);
+                    }
+                    char* gp = reinterpret_cast<char*>(hrow) + (c / 8) * 32 + (c % 8) * 2;
+                    *reinterpret_cast<uint2*>(gp) = make_uint2(hi[0], hi[1]);
+                    *reinterpret_cast<uint2*>(gp + 16) = make_uint2(lo[0], lo[1]);
+                }
+            }
+        } else {
+            float* drow = dbuf + static_cast<size_t>(pair[t]) * H;
+#pragma unroll
+            for (int r = 0; r < kRb; ++r) {
+                if (rb0 + r >= nrb) continue;
+                const f32x4 v = acc[0][r][t];
+                *reinterpret_cast<float4*>(drow + (rb0 + r) * 16 + 4 * q) =
+                    make_float4(wt[t] * v.x, wt[t] * v.y, wt[t] * v.z, wt[t] * v.w);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // One wave streams `count` consecutive items of one expert, starting at item
 // `local0` of that expert.  Positions (item, tile) run through a ring of D
@@ -395,12 +450,13 @@ __device__ __forceinline__ int item_at(const int* pref_cost, const int* pref_ite
 // Arguments are plain values (no struct in private memory); every one is
 // wave-uniform and is moved to SGPRs, so the ring's loads and waits are
 // scheduled per stage rather than behind divergent branches.
-template <int PHASE, int FMT, bool XF32, int NT, int PRE = 0>
+template <int PHASE, int FMT, bool XF32, int NT, int PRE = 0, bool KSPLIT = false, int RB = rb_per_item<PHASE, NT>()>
 __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_in, const float* w_in,
                                        float* hbuf_in, float* dbuf_in, int k_in, int H_in, int I_in,
                                        const char* m0, const char* m1, const char* s0, const char* s1,
                                        int first_in, int cnt_in, int local0_in, int count_in,
-                                       const WStage<PHASE, FMT, XF32, NT>* pre = nullptr, int pre_pair = 0) {
+                                       const WStage<PHASE, FMT, XF32, NT, RB>* pre = nullptr, int pre_pair = 0,
+                                       int t_lo_in = 0, int t_n_in = 0, f32x4* part = nullptr) {
     const int local0 = uni(local0_in), count = uni(count_in);
     const int k = uni(k_in), H = uni(H_in), I = uni(I_in);
     const char* xg = uni_ptr(x_in);
@@ -408,18 +464,26 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
     const float* wg = uni_ptr(w_in);
     float* hbuf = const_cast<float*>(uni_ptr(hbuf_in));
     float* dbuf = const_cast<float*>(uni_ptr(dbuf_in));
-    using Wst = WStage<PHASE, FMT, XF32, NT>;
+    using Wst = WStage<PHASE, FMT, XF32, NT, RB>;
     using Xst = XStage<FMT, XF32, NT>;
     using Ac = Act<FMT, XF32>;
     constexpr int kMat = Wst::kMat, kRb = Wst::kRb;
-    constexpr int D = Ring<PHASE, FMT, XF32, NT>::D;   // weight stages in flight
-    constexpr int X = Ring<PHASE, FMT, XF32, NT>::X;   // activation stages in flight (X divides D)
+    // weight stages in flight, and activation stages (X divides D); a slice
+    // of a column-split item has few tiles and keeps at most 4 stages (2 for
+    // INT4, whose activation stages are four times larger)
+    using Rg = Ring<PHASE, FMT, XF32, NT, RB>;
+    constexpr int D = KSPLIT ? std::min(FMT == MOE_W_INT4_G128 ? 2 : 4, Rg::D) : Rg::D;
+    constexpr int X = std::min(D, Rg::X);
     const int lane = threadIdx.x & (kWave - 1);
     const int n = lane & 15, q = lane >> 4;
     const int rows = PHASE == 0 ? I : H, cols = PHASE == 0 ? H : I;
     const int nrb = rows / 16;
     const int S = uni(weight_row_bytes(FMT, cols) / 64);     // tiles per row block
-    const int Sp = uni((S + D - 1) / D * D);
+    // KSPLIT: the wave streams only tile columns [t_lo, t_lo + Sl) of its
+    // (single) item and leaves the partial sums in part[] (LDS)
+    const int t_lo = KSPLIT ? uni(t_lo_in) : 0;
+    const int Sl = KSPLIT ? uni(t_n_in) : S;
+    const int Sp = uni((Sl + D - 1) / D * D);
     const int first = uni(first_in), cnt = uni(cnt_in);
     const char* mb[kMat];
     const char* sb[kMat];
@@ -438,7 +502,7 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
     Wst ring[D];
     Xst xring[X];
     auto issue = [&](Wst& st, int item, int s) {
-        const int se = s < S ? s : S - 1;
+        const int se = t_lo + (s < Sl ? s : Sl - 1);
 #pragma unroll
         for (int m = 0; m < kMat; ++m)
 #pragma unroll
@@ -452,7 +516,7 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
     };
     // activation fragments depend on the tile column only, not on the item
     auto issue_x = [&](Xst& st, int s) {
-        const int se = s < S ? s : S - 1;
+        const int se = t_lo + (s < Sl ? s : Sl - 1);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -511,7 +575,7 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
         if (!last) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                tile_mma<PHASE, FMT, XF32, NT>(ring[d], xring[d % X], cs + d < S ? ~0u : 0u, acc);
+                tile_mma<PHASE, FMT, XF32, NT, RB>(ring[d], xring[d % X], cs + d < Sl ? ~0u : 0u, acc);
                 issue(ring[d], ii, is + d);
                 if constexpr (X == D) {
                     issue_x(xring[d], is + d);
@@ -523,7 +587,7 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
         } else {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                tile_mma<PHASE, FMT, XF32, NT>(ring[d], xring[d % X], cs + d < S ? ~0u : 0u, acc);
+                tile_mma<PHASE, FMT, XF32, NT, RB>(ring[d], xring[d % X], cs + d < Sl ? ~0u : 0u, acc);
                 if constexpr (X < D) {
                     if (d + X < D) issue_x(xring[d % X], cs + d + X);
                 }
@@ -531,50 +595,16 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
         }
         cs += D;
         if (cs == Sp) {   // item done: write its rows for every real token
-            const int rb0 = (local0 + ci) * kRb;
+            if constexpr (KSPLIT) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                if (16 * t + n >= cnt) continue;
-                if constexpr (PHASE == 0) {
-                    float* hrow = hbuf + static_cast<size_t>(pair[t]) * I;
+                for (int m = 0; m < kMat; ++m)
 #pragma unroll
-                    for (int r = 0; r < kRb; ++r) {
-                        if (rb0 + r >= nrb) continue;
-                        const f32x4 g = acc[0][r][t], u = acc[kMat - 1][r][t];
-                        const float hv[4] = {silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w};
-                        const int c = (rb0 + r) * 16 + 4 * q;   // first of this lane's 4 columns of h
-                        if constexpr (FMT == MOE_W_F32) {
-                            *reinterpret_cast<float4*>(hrow + c) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-                        } else if constexpr (FMT == MOE_W_INT4_G128) {
-                            // INT4 experts take h in bf16 (W4A16), row-major in the row's first 2 I bytes
-                            const uint2 hb = make_uint2(bf16_rne(hv[0]) | (bf16_rne(hv[1]) << 16),
-                                                        bf16_rne(hv[2]) | (bf16_rne(hv[3]) << 16));
-                            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(hrow) + 2 * c) = hb;
-                        } else {
-                            // split layout: per 8 columns, 8 bf16 hi then 8 bf16 lo
-                            uint32_t hi[2], lo[2];
+                    for (int r = 0; r < kRb; ++r)
 #pragma unroll
-                            for (int j = 0; j < 2; ++j) {
-                                const uint32_t a = bf16_rne(hv[2 * j]), b = bf16_rne(hv[2 * j + 1]);
-                                hi[j] = a | (b << 16);
-                                lo[j] = bf16_rne(hv[2 * j] - __uint_as_float(a << 16)) |
-                                        (bf16_rne(hv[2 * j + 1] - __uint_as_float(b << 16)) << 16);
-                            }
-                            char* gp = reinterpret_cast<char*>(hrow) + (c / 8) * 32 + (c % 8) * 2;
-                            *reinterpret_cast<uint2*>(gp) = make_uint2(hi[0], hi[1]);
-                            *reinterpret_cast<uint2*>(gp + 16) = make_uint2(lo[0], lo[1]);
-                        }
-                    }
-                } else {
-                    float* drow = dbuf + static_cast<size_t>(pair[t]) * H;
-#pragma unroll
-                    for (int r = 0; r < kRb; ++r) {
-                        if (rb0 + r >= nrb) continue;
-                        const f32x4 v = acc[0][r][t];
-                        *reinterpret_cast<float4*>(drow + (rb0 + r) * 16 + 4 * q) =
-                            make_float4(wt[t] * v.x, wt[t] * v.y, wt[t] * v.z, wt[t] * v.w);
-                    }
-                }
+                        for (int t = 0; t < NT; ++t) part[((m * kRb + r) * NT + t) * kWave + lane] = acc[m][r][t];
+            } else {
+                store_item<PHASE, FMT, kMat, kRb, NT>(acc, pair, wt, hbuf, dbuf, H, I, (local0 + ci) * kRb, nrb, cnt,
+                                                      n, q);
             }
             zero();
             cs = 0;
@@ -758,6 +788,91 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small batches (at most kSmallPairs routed pairs, so T <= 16 and every
+// expert has at most 16 tokens).  There the per-wave items above leave most
+// of the chip idle (B = 1, T = 3: 72 phase-A items), and each phase lasts as
+// long as one wave needs to stream an item.  Here an item (expert, one or
+// two row blocks) belongs to a workgroup of kSlices waves; wave j streams the j-th
+// contiguous share of the item's tile columns, the partial sums meet in
+// LDS, and wave 0 adds them in slice order (so results are deterministic)
+// and writes the item as the per-wave path does.
+// ---------------------------------------------------------------------------
+constexpr int kSmallPairs = 8;
+constexpr int kSmallThreads = 256;
+constexpr int kSlices = kSmallThreads / kWave;
+// row blocks per item: one in phase A (twice the workgroups), two in phase B
+// (whose items are small: 16 rows of I)
+template <int PHASE>
+constexpr int small_rb() { return PHASE == 0 ? 1 : 2; }
+
+template <int PHASE, int FMT, bool XF32>
+__device__ __forceinline__ void small_item(const FfnArgs& a, const moe_expert_handle& h, int first, int cnt,
+                                           int item, f32x4* part_l) {
+    using Wst = WStage<PHASE, FMT, XF32, 1, small_rb<PHASE>()>;
+    constexpr int kMat = Wst::kMat, kRb = Wst::kRb;
+    constexpr int kPart = kMat * kRb * kWave;   // f32x4 per slice
+    const int cols = PHASE == 0 ? a.H : a.I, nrb = (PHASE == 0 ? a.I : a.H) / 16;
+    const int S = weight_row_bytes(FMT, cols) / 64;
+    const int ns = min(kSlices, S);   // slices with at least one tile column
+    const int j = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const char* m0 = static_cast<const char*>(PHASE == 0 ? h.w_gate : h.w_down);
+    const char* m1 = static_cast<const char*>(PHASE == 0 ? h.w_up : h.w_down);
+    const char* s0 = reinterpret_cast<const char*>(PHASE == 0 ? h.s_gate : h.s_down);
+    const char* s1 = reinterpret_cast<const char*>(PHASE == 0 ? h.s_up : h.s_down);
+    if (j < ns) {
+        const int lo = j * S / ns, hi = (j + 1) * S / ns;   // hi > lo since ns <= S
+        run_items<PHASE, FMT, XF32, 1, 0, true, small_rb<PHASE>()>(static_cast<const char*>(a.x), a.perm, a.w, a.hbuf, a.dbuf, a.k,
+                                                a.H, a.I, m0, m1, s0, s1, first, cnt, item, 1, nullptr, 0, lo,
+                                                hi - lo, part_l + j * kPart);
+    }
+    __syncthreads();
+    if (j == 0) {
+        f32x4 acc[kMat][kRb][1];
+#pragma unroll
+        for (int m = 0; m < kMat; ++m)
+#pragma unroll
+            for (int r = 0; r < kRb; ++r) {
+                f32x4 v = part_l[(m * kRb + r) * kWave + lane];
+                for (int jj = 1; jj < ns; ++jj) v += part_l[jj * kPart + (m * kRb + r) * kWave + lane];
+                acc[m][r][0] = v;
+            }
+        const int n = lane & 15, q = lane >> 4;
+        const int pair[1] = {((const __attribute__((address_space(1))) int32_t*)a.perm)[first + (n < cnt ? n : 0)]};
+        const float wt[1] = {PHASE == 1 ? ((const __attribute__((address_space(1))) float*)a.w)[pair[0]] : 0.0f};
+        store_item<PHASE, FMT, kMat, kRb, 1>(acc, pair, wt, a.hbuf, a.dbuf, a.H, a.I, item * kRb, nrb, cnt, n, q);
+    }
+}
+
+// One workgroup per (active slot, item); workgroups past T exit at once.
+template <int PHASE>
+__global__ __launch_bounds__(kSmallThreads, 2) void ffn_small_kernel(FfnArgs a) {
+    __shared__ f32x4 part_l[kSlices * 2 * kWave];   // slices x (matrices x row blocks = 2) x lanes
+    static_assert((PHASE == 0 ? 2 : 1) * small_rb<PHASE>() == 2, "partial sums layout");
+    const int nrb = (PHASE == 0 ? a.I : a.H) / 16, ipp = (nrb + small_rb<PHASE>() - 1) / small_rb<PHASE>();
+    const int s = blockIdx.x / ipp, item = blockIdx.x - s * ipp;
+    // T and the slot's expert in one round trip (s < N: the grid covers at most N slots)
+    const int T = uni(*a.T);
+    const int e = uni(((const __attribute__((address_space(1))) int32_t*)a.active)[s]);
+    if (s >= T) return;
+    const moe_expert_handle h = a.table[e];
+    const int first = uni(a.offsets[e]), cnt = uni(a.offsets[e + 1]) - first;
+    const int fmt = uni(h.fmt);
+    // as in the per-wave path, an expert whose format does not fit the sizes contributes nothing
+    const bool known = fmt == MOE_W_F32 || fmt == MOE_W_BF16 || fmt == MOE_W_INT4_G128;
+    if (!known || ((PHASE == 0 ? a.H : a.I) & (tile_cols(fmt) - 1)) != 0) return;
+    if (fmt == MOE_W_BF16) {
+        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_BF16, true>(a, h, first, cnt, item, part_l);
+        else small_item<PHASE, MOE_W_BF16, false>(a, h, first, cnt, item, part_l);
+    } else if (fmt == MOE_W_INT4_G128) {
+        if (PHASE == 0 && a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_INT4_G128, true>(a, h, first, cnt, item, part_l);
+        else small_item<PHASE, MOE_W_INT4_G128, false>(a, h, first, cnt, item, part_l);
+    } else {
+        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_F32, true>(a, h, first, cnt, item, part_l);
+        else small_item<PHASE, MOE_W_F32, false>(a, h, first, cnt, item, part_l);
+    }
+}
+
 // y[i, o] = sum over filled slots s of token i (slot order) of dbuf[i*k+s, o].
 // One wavefront per (token, 256 outputs).  All of the token's slot rows
 // are loaded first (unfilled slots' rows are read and ignored); lane j < k
@@ -847,16 +962,27 @@ hipError_t launch_expert_ffn(const FfnArgs& in, void* ws, hipStream_t s) {
     char* p = static_cast<char*>(ws);
     a.hbuf = reinterpret_cast<float*>(p);
     a.dbuf = reinterpret_cast<float*>(p + align256(pairs * a.I * sizeof(float)));
-    const int cus = device_cus();
-    // grids are whole multiples of kXcds workgroups (the virtual numbering needs it)
-    const int g0 = (waves_per_simd<0>() * cus) / kXcds * kXcds;
-    const int g1 = (waves_per_simd<1>() * cus) / kXcds * kXcds;
-    ffn_kernel<0><<<g0 > 0 ? g0 : kXcds, kThreads, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    ffn_kernel<1><<<g1 > 0 ? g1 : kXcds, kThreads, 0, s>>>(a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (pairs <= static_cast<size_t>(kSmallPairs)) {
+        // one workgroup per (slot, item) for every slot that T can reach
+        const int slots = std::min(static_cast<int>(pairs), a.N);
+        ffn_small_kernel<0><<<slots * ((a.I / 16 + small_rb<0>() - 1) / small_rb<0>()), kSmallThreads, 0, s>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ffn_small_kernel<1><<<slots * ((a.H / 16 + small_rb<1>() - 1) / small_rb<1>()), kSmallThreads, 0, s>>>(a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else {
+        const int cus = device_cus();
+        // grids are whole multiples of kXcds workgroups (the virtual numbering needs it)
+        const int g0 = (waves_per_simd<0>() * cus) / kXcds * kXcds;
+        const int g1 = (waves_per_simd<1>() * cus) / kXcds * kXcds;
+        ffn_kernel<0><<<g0 > 0 ? g0 : kXcds, kThreads, 0, s>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ffn_kernel<1><<<g1 > 0 ? g1 : kXcds, kThreads, 0, s>>>(a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     dim3 cg((a.H / 4 + kWave - 1) / kWave, a.B);
     combine_kernel<<<cg, kWave, 0, s>>>(a);
     return hipGetLastError();

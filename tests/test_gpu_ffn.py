@@ -121,6 +121,28 @@ def test_int4_experts_with_fp32_activations():
     _run_and_check(layer, host, x, xd, logits, "oea", 1, 1.0, TOL["int4"])
 
 
+@pytest.mark.parametrize("fmt,x_dtype,H,I", [
+    ("bf16", "bf16", 512, 256), ("bf16", "f32", 512, 256), ("f32", "f32", 256, 128),
+    ("int4", "bf16", 512, 256), ("int4", "f32", 256, 384), ("mixed", "bf16", 640, 384),
+    # fewer tile columns than the four column slices: bf16 3 (phase A) and 2 (phase B), INT4 1
+    ("bf16", "bf16", 96, 64), ("int4", "bf16", 128, 128),
+])
+@pytest.mark.parametrize("B,k", [(1, 8), (2, 4), (8, 1)])
+def test_small_batch_column_split(fmt, x_dtype, H, I, B, k):
+    # calls with B*k <= 8 routed pairs split each item's input columns over
+    # the waves of a workgroup and add the partial sums in LDS
+    N = 16
+    int4 = {"int4": range(N), "mixed": range(0, N, 2)}.get(fmt, [])
+    layer, host = build_layer(N, k, H, I, 40 + B, fmt="f32" if fmt == "f32" else "bf16", int4_experts=int4,
+                              with_router=False)
+    x, xd = _x(41 + B, B, H, x_dtype)
+    logits = synth.logits(42 + B, B, N, 1.0)
+    tol = TOL["int4"] if int4 else TOL[fmt]
+    _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, tol)
+    if k > 1:
+        _run_and_check(layer, host, x, xd, logits, "oea", 1, 1.0, tol)
+
+
 def test_publish_switches_version():
     # page "DynaExq" section 2.2: switching a handle changes the version the next call reads
     N, k, H, I, B = 8, 2, 256, 128, 6

@@ -10,9 +10,19 @@ import torch
 
 import aware_expert_routing_amd as moe
 import synth
-from gpu_util import DEV, build_layer
+from gpu_util import DEV, build_layer, max_err_over_rms
 
 pytestmark = pytest.mark.gpu
+
+
+def _same_rows(alone_y, graph_y, pairs):
+    """A real batch run alone against the same rows of a padded batch: bit for
+    bit, except that a call of at most 8 routed pairs takes the column-split
+    path, whose partial sums are added in another order (fp32 rounding)."""
+    if pairs > 8:
+        return torch.equal(alone_y, graph_y)
+    err, rms = max_err_over_rms(alone_y, graph_y.double().cpu().numpy())
+    return err <= 1e-5 * rms
 
 
 def _x(seed, B, H):
@@ -46,7 +56,7 @@ def test_graph_replays_match_eager(mode, k0):
             alone = eager_layer.forward(x_static[:n_real].clone(), mode, k0, 1.0)
             torch.cuda.synchronize()
             assert int(alone.disp["T"].item()) == int(got["T"].item())
-            assert torch.equal(alone.y, y_graph[:n_real])
+            assert _same_rows(alone.y, y_graph[:n_real], n_real * k)
 
 
 def test_graph_follows_the_batch_size_k0_table():
@@ -69,4 +79,4 @@ def test_graph_follows_the_batch_size_k0_table():
         alone = eager_layer.forward(x_static[:n_real].clone(), "oea", int(tab[n_real]), 1.0)
         torch.cuda.synchronize()
         assert int(alone.disp["T"].item()) == T_graph, rep
-        assert torch.equal(alone.y, y_graph[:n_real]), rep
+        assert _same_rows(alone.y, y_graph[:n_real], n_real * k), rep
