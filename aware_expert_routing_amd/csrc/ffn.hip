@@ -32,7 +32,10 @@
 // Items belong to single waves (no barriers, no LDS staging): each wave owns
 // an equal share of the total streaming cost, keeps several tiles of loads
 // in flight (a register ring of D stages) and reads its tokens' activation
-// fragments straight from global memory (they stay in L1/L2).
+// fragments straight from global memory (they stay in L1/L2).  Calls of at
+// most 8 routed pairs instead give each item to a workgroup whose waves
+// split its input columns and add their partial sums in LDS (see
+// ffn_small_kernel): there the items are too few to occupy the chip.
 // INT4 tiles are one quantisation group: nibbles become the bf16 values
 // 128 + u by bit operations, one MFMA per 32 columns accumulates them, a
 // second MFMA with the constant -136 removes the offset (u - 8 = q), and the

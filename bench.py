@@ -60,11 +60,17 @@ FFN_SOURCES = [os.path.join(ROOT, "aware_expert_routing_amd", "csrc", f) for f i
 
 
 def sources_sha256():
+    """Hash of the expert-FFN sources with comments and whitespace removed,
+    so that the counters stay attached to the code they were taken on."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in FFN_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
