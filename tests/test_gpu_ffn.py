@@ -127,7 +127,7 @@ def test_int4_experts_with_fp32_activations():
     # fewer tile columns than the four column slices: bf16 3 (phase A) and 2 (phase B), INT4 1
     ("bf16", "bf16", 96, 64), ("int4", "bf16", 128, 128),
 ])
-@pytest.mark.parametrize("B,k", [(1, 8), (2, 4), (8, 1)])
+@pytest.mark.parametrize("B,k", [(1, 8), (2, 4), (8, 1), (1, 1), (1, 2)])
 def test_small_batch_column_split(fmt, x_dtype, H, I, B, k):
     # calls with B*k <= 8 routed pairs split each item's input columns over
     # the waves of a workgroup and add the partial sums in LDS
@@ -141,6 +141,19 @@ def test_small_batch_column_split(fmt, x_dtype, H, I, B, k):
     _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, tol)
     if k > 1:
         _run_and_check(layer, host, x, xd, logits, "oea", 1, 1.0, tol)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,k", [(1, 4), (16, 4)])
+def test_smallest_shapes(fmt, B, k):
+    # H = I = 32: one tile column per row block in both phases (bf16), two
+    # (fp32); B*k = 4 takes the column-split path, 64 the per-wave items
+    N, H, I = 8, 32, 32
+    layer, host = build_layer(N, k, H, I, 60 + B, fmt=fmt, with_router=False)
+    x, xd = _x(61 + B, B, H, "bf16" if fmt == "bf16" else "f32")
+    logits = synth.logits(62 + B, B, N, 1.0)
+    _run_and_check(layer, host, x, xd, logits, "topk", 0, 1.0, TOL[fmt])
+    _run_and_check(layer, host, x, xd, logits, "oea", 2, 1.0, TOL[fmt])
 
 
 def test_publish_switches_version():
