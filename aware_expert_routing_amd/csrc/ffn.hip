@@ -655,6 +655,83 @@ __device__ __forceinline__ void run_fmt(const FfnArgs& a, const SlotRec& rec, in
     else run_nt<PHASE, MOE_W_F32, XF32>(a, rec, local0, count);
 }
 
+// ---------------------------------------------------------------------------
+// Small batches (at most kSmallPairs routed pairs, so T <= 16 and every
+// expert has at most 16 tokens).  There the per-wave items above leave most
+// of the chip idle (B = 1, T = 3: 72 phase-A items), and each phase lasts as
+// long as one wave needs to stream an item.  Here an item (expert, one or
+// two row blocks) belongs to a workgroup of kSlices waves; wave j streams the j-th
+// contiguous share of the item's tile columns, the partial sums meet in
+// LDS, and wave 0 adds them in slice order (so results are deterministic)
+// and writes the item as the per-wave path does.
+// ---------------------------------------------------------------------------
+constexpr int kSmallPairs = 8;
+constexpr int kSmallThreads = 256;
+constexpr int kSlices = kSmallThreads / kWave;
+// row blocks per item: one in phase A (twice the workgroups), two in phase B
+// (whose items are small: 16 rows of I)
+template <int PHASE>
+constexpr int small_rb() { return PHASE == 0 ? 1 : 2; }
+
+template <int PHASE, int FMT, bool XF32>
+__device__ __forceinline__ void small_item(const FfnArgs& a, const moe_expert_handle& h, int first, int cnt,
+                                           int item, f32x4* part_l) {
+    using Wst = WStage<PHASE, FMT, XF32, 1, small_rb<PHASE>()>;
+    constexpr int kMat = Wst::kMat, kRb = Wst::kRb;
+    constexpr int kPart = kMat * kRb * kWave;   // f32x4 per slice
+    const int cols = PHASE == 0 ? a.H : a.I, nrb = (PHASE == 0 ? a.I : a.H) / 16;
+    const int S = weight_row_bytes(FMT, cols) / 64;
+    const int ns = min(kSlices, S);   // slices with at least one tile column
+    const int j = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const char* m0 = static_cast<const char*>(PHASE == 0 ? h.w_gate : h.w_down);
+    const char* m1 = static_cast<const char*>(PHASE == 0 ? h.w_up : h.w_down);
+    const char* s0 = reinterpret_cast<const char*>(PHASE == 0 ? h.s_gate : h.s_down);
+    const char* s1 = reinterpret_cast<const char*>(PHASE == 0 ? h.s_up : h.s_down);
+    if (j < ns) {
+        const int lo = j * S / ns, hi = (j + 1) * S / ns;   // hi > lo since ns <= S
+        run_items<PHASE, FMT, XF32, 1, 0, true, small_rb<PHASE>()>(static_cast<const char*>(a.x), a.perm, a.w, a.hbuf, a.dbuf, a.k,
+                                                a.H, a.I, m0, m1, s0, s1, first, cnt, item, 1, nullptr, 0, lo,
+                                                hi - lo, part_l + j * kPart);
+    }
+    __syncthreads();
+    if (j == 0) {
+        f32x4 acc[kMat][kRb][1];
+#pragma unroll
+        for (int m = 0; m < kMat; ++m)
+#pragma unroll
+            for (int r = 0; r < kRb; ++r) {
+                f32x4 v = part_l[(m * kRb + r) * kWave + lane];
+                for (int jj = 1; jj < ns; ++jj) v += part_l[jj * kPart + (m * kRb + r) * kWave + lane];
+                acc[m][r][0] = v;
+            }
+        const int n = lane & 15, q = lane >> 4;
+        const int pair[1] = {((const __attribute__((address_space(1))) int32_t*)a.perm)[first + (n < cnt ? n : 0)]};
+        const float wt[1] = {PHASE == 1 ? ((const __attribute__((address_space(1))) float*)a.w)[pair[0]] : 0.0f};
+        store_item<PHASE, FMT, kMat, kRb, 1>(acc, pair, wt, a.hbuf, a.dbuf, a.H, a.I, item * kRb, nrb, cnt, n, q);
+    }
+}
+
+// One (expert, item) of the column-split path, in the expert's format; the
+// caller's whole workgroup calls it (it holds a barrier).  An expert whose
+// format does not fit the sizes contributes nothing, as in the per-wave path.
+template <int PHASE>
+__device__ __forceinline__ void small_unit(const FfnArgs& a, const moe_expert_handle& h, int first, int cnt,
+                                           int item, f32x4* part_l) {
+    const int fmt = uni(h.fmt);
+    const bool known = fmt == MOE_W_F32 || fmt == MOE_W_BF16 || fmt == MOE_W_INT4_G128;
+    if (!known || ((PHASE == 0 ? a.H : a.I) & (tile_cols(fmt) - 1)) != 0) return;
+    if (fmt == MOE_W_BF16) {
+        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_BF16, true>(a, h, first, cnt, item, part_l);
+        else small_item<PHASE, MOE_W_BF16, false>(a, h, first, cnt, item, part_l);
+    } else if (fmt == MOE_W_INT4_G128) {
+        if (PHASE == 0 && a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_INT4_G128, true>(a, h, first, cnt, item, part_l);
+        else small_item<PHASE, MOE_W_INT4_G128, false>(a, h, first, cnt, item, part_l);
+    } else {
+        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_F32, true>(a, h, first, cnt, item, part_l);
+        else small_item<PHASE, MOE_W_F32, false>(a, h, first, cnt, item, part_l);
+    }
+}
+
 // Resident waves per SIMD: phase A keeps 2 (deep rings of gate+up tiles),
 // phase B 3 (more waves with smaller items).
 template <int PHASE>
@@ -670,6 +747,9 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     __shared__ int active_l[kMaxExperts];
     __shared__ int offsets_l[kMaxExperts + 1];
     __shared__ int odd_l[kWaves];
+    __shared__ int big_l[kWaves];
+    __shared__ f32x4 part_l[kSlices * 2 * kWave];   // column-split path (phase A)
+    static_assert(kSmallThreads == kThreads, "the column-split path runs on this kernel's workgroups");
     // Stage the handle table, active list and offsets with independent loads
     // (one round trip) instead of following active -> handle per slot.  The
     // loads take clamped (in-bounds) addresses and are all issued before the
@@ -691,7 +771,29 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     // Expert tid outside the uniform case below: active and not bf16 with at most 16 tokens.
     const uint64_t odd = __ballot(tid < a.N && off1 > off && (fmt != MOE_W_BF16 || off1 - off > 16));
     if ((tid & (kWave - 1)) == 0) odd_l[tid / kWave] = odd != 0;
+    // expert tid has more than 16 tokens (more than one column tile)
+    const uint64_t big = __ballot(tid < a.N && off1 - off > 16);
+    if ((tid & (kWave - 1)) == 0) big_l[tid / kWave] = big != 0;
     __syncthreads();
+    if constexpr (PHASE == 0) {
+        // Few items: when every (expert, row block) gets a workgroup of its own
+        // and every expert fits one column tile, phase A takes the column-split
+        // path (the per-wave items would leave most CUs idle).  T decides it,
+        // so padding tokens do not change the path.
+        bool one_tile = true;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) one_tile = one_tile && big_l[w] == 0;
+        const int ipp_s = a.I / 16;   // small_rb<0>() == 1
+        if (one_tile && T * ipp_s <= static_cast<int>(gridDim.x)) {
+            const int s = div_small(blockIdx.x, ipp_s), item = blockIdx.x - s * ipp_s;
+            if (s < T) {   // the same for the whole workgroup
+                const int e = active_l[s];
+                small_unit<0>(a, reinterpret_cast<const moe_expert_handle*>(table_l)[e], offsets_l[e],
+                              offsets_l[e + 1] - offsets_l[e], item, part_l);
+            }
+            return;
+        }
+    }
     const int Wn = gridDim.x * kWaves;
     // XCD- and CU-aware numbering.  Workgroups are dealt to the 8 XCDs
     // round-robin (blockIdx % 8) and, inside an XCD, to its CUs round-robin,
@@ -791,62 +893,6 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------
-// Small batches (at most kSmallPairs routed pairs, so T <= 16 and every
-// expert has at most 16 tokens).  There the per-wave items above leave most
-// of the chip idle (B = 1, T = 3: 72 phase-A items), and each phase lasts as
-// long as one wave needs to stream an item.  Here an item (expert, one or
-// two row blocks) belongs to a workgroup of kSlices waves; wave j streams the j-th
-// contiguous share of the item's tile columns, the partial sums meet in
-// LDS, and wave 0 adds them in slice order (so results are deterministic)
-// and writes the item as the per-wave path does.
-// ---------------------------------------------------------------------------
-constexpr int kSmallPairs = 8;
-constexpr int kSmallThreads = 256;
-constexpr int kSlices = kSmallThreads / kWave;
-// row blocks per item: one in phase A (twice the workgroups), two in phase B
-// (whose items are small: 16 rows of I)
-template <int PHASE>
-constexpr int small_rb() { return PHASE == 0 ? 1 : 2; }
-
-template <int PHASE, int FMT, bool XF32>
-__device__ __forceinline__ void small_item(const FfnArgs& a, const moe_expert_handle& h, int first, int cnt,
-                                           int item, f32x4* part_l) {
-    using Wst = WStage<PHASE, FMT, XF32, 1, small_rb<PHASE>()>;
-    constexpr int kMat = Wst::kMat, kRb = Wst::kRb;
-    constexpr int kPart = kMat * kRb * kWave;   // f32x4 per slice
-    const int cols = PHASE == 0 ? a.H : a.I, nrb = (PHASE == 0 ? a.I : a.H) / 16;
-    const int S = weight_row_bytes(FMT, cols) / 64;
-    const int ns = min(kSlices, S);   // slices with at least one tile column
-    const int j = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const char* m0 = static_cast<const char*>(PHASE == 0 ? h.w_gate : h.w_down);
-    const char* m1 = static_cast<const char*>(PHASE == 0 ? h.w_up : h.w_down);
-    const char* s0 = reinterpret_cast<const char*>(PHASE == 0 ? h.s_gate : h.s_down);
-    const char* s1 = reinterpret_cast<const char*>(PHASE == 0 ? h.s_up : h.s_down);
-    if (j < ns) {
-        const int lo = j * S / ns, hi = (j + 1) * S / ns;   // hi > lo since ns <= S
-        run_items<PHASE, FMT, XF32, 1, 0, true, small_rb<PHASE>()>(static_cast<const char*>(a.x), a.perm, a.w, a.hbuf, a.dbuf, a.k,
-                                                a.H, a.I, m0, m1, s0, s1, first, cnt, item, 1, nullptr, 0, lo,
-                                                hi - lo, part_l + j * kPart);
-    }
-    __syncthreads();
-    if (j == 0) {
-        f32x4 acc[kMat][kRb][1];
-#pragma unroll
-        for (int m = 0; m < kMat; ++m)
-#pragma unroll
-            for (int r = 0; r < kRb; ++r) {
-                f32x4 v = part_l[(m * kRb + r) * kWave + lane];
-                for (int jj = 1; jj < ns; ++jj) v += part_l[jj * kPart + (m * kRb + r) * kWave + lane];
-                acc[m][r][0] = v;
-            }
-        const int n = lane & 15, q = lane >> 4;
-        const int pair[1] = {((const __attribute__((address_space(1))) int32_t*)a.perm)[first + (n < cnt ? n : 0)]};
-        const float wt[1] = {PHASE == 1 ? ((const __attribute__((address_space(1))) float*)a.w)[pair[0]] : 0.0f};
-        store_item<PHASE, FMT, kMat, kRb, 1>(acc, pair, wt, a.hbuf, a.dbuf, a.H, a.I, item * kRb, nrb, cnt, n, q);
-    }
-}
-
 // One workgroup per (active slot, item); workgroups past T exit at once.
 template <int PHASE>
 __global__ __launch_bounds__(kSmallThreads, 2) void ffn_small_kernel(FfnArgs a) {
@@ -860,20 +906,7 @@ __global__ __launch_bounds__(kSmallThreads, 2) void ffn_small_kernel(FfnArgs a) 
     if (s >= T) return;
     const moe_expert_handle h = a.table[e];
     const int first = uni(a.offsets[e]), cnt = uni(a.offsets[e + 1]) - first;
-    const int fmt = uni(h.fmt);
-    // as in the per-wave path, an expert whose format does not fit the sizes contributes nothing
-    const bool known = fmt == MOE_W_F32 || fmt == MOE_W_BF16 || fmt == MOE_W_INT4_G128;
-    if (!known || ((PHASE == 0 ? a.H : a.I) & (tile_cols(fmt) - 1)) != 0) return;
-    if (fmt == MOE_W_BF16) {
-        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_BF16, true>(a, h, first, cnt, item, part_l);
-        else small_item<PHASE, MOE_W_BF16, false>(a, h, first, cnt, item, part_l);
-    } else if (fmt == MOE_W_INT4_G128) {
-        if (PHASE == 0 && a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_INT4_G128, true>(a, h, first, cnt, item, part_l);
-        else small_item<PHASE, MOE_W_INT4_G128, false>(a, h, first, cnt, item, part_l);
-    } else {
-        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_F32, true>(a, h, first, cnt, item, part_l);
-        else small_item<PHASE, MOE_W_F32, false>(a, h, first, cnt, item, part_l);
-    }
+    small_unit<PHASE>(a, h, first, cnt, item, part_l);
 }
 
 // y[i, o] = sum over filled slots s of token i (slot order) of dbuf[i*k+s, o].

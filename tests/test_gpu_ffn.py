@@ -127,10 +127,12 @@ def test_int4_experts_with_fp32_activations():
     # fewer tile columns than the four column slices: bf16 3 (phase A) and 2 (phase B), INT4 1
     ("bf16", "bf16", 96, 64), ("int4", "bf16", 128, 128),
 ])
-@pytest.mark.parametrize("B,k", [(1, 8), (2, 4), (8, 1), (1, 1), (1, 2)])
+@pytest.mark.parametrize("B,k", [(1, 8), (2, 4), (8, 1), (1, 1), (1, 2), (6, 2), (20, 1)])
 def test_small_batch_column_split(fmt, x_dtype, H, I, B, k):
     # calls with B*k <= 8 routed pairs split each item's input columns over
-    # the waves of a workgroup and add the partial sums in LDS
+    # the waves of a workgroup and add the partial sums in LDS; larger calls
+    # (6x2, 20x1 here) do so in phase A when T * I/16 items fit the grid and
+    # no expert has more than 16 tokens
     N = 16
     int4 = {"int4": range(N), "mixed": range(0, N, 2)}.get(fmt, [])
     layer, host = build_layer(N, k, H, I, 40 + B, fmt="f32" if fmt == "f32" else "bf16", int4_experts=int4,
