@@ -673,10 +673,10 @@ constexpr int kSlices = kSmallThreads / kWave;
 template <int PHASE>
 constexpr int small_rb() { return PHASE == 0 ? 1 : 2; }
 
-template <int PHASE, int FMT, bool XF32>
+template <int PHASE, int FMT, bool XF32, int RB = small_rb<PHASE>()>
 __device__ __forceinline__ void small_item(const FfnArgs& a, const moe_expert_handle& h, int first, int cnt,
                                            int item, f32x4* part_l) {
-    using Wst = WStage<PHASE, FMT, XF32, 1, small_rb<PHASE>()>;
+    using Wst = WStage<PHASE, FMT, XF32, 1, RB>;
     constexpr int kMat = Wst::kMat, kRb = Wst::kRb;
     constexpr int kPart = kMat * kRb * kWave;   // f32x4 per slice
     const int cols = PHASE == 0 ? a.H : a.I, nrb = (PHASE == 0 ? a.I : a.H) / 16;
@@ -689,7 +689,7 @@ __device__ __forceinline__ void small_item(const FfnArgs& a, const moe_expert_ha
     const char* s1 = reinterpret_cast<const char*>(PHASE == 0 ? h.s_up : h.s_down);
     if (j < ns) {
         const int lo = j * S / ns, hi = (j + 1) * S / ns;   // hi > lo since ns <= S
-        run_items<PHASE, FMT, XF32, 1, 0, true, small_rb<PHASE>()>(static_cast<const char*>(a.x), a.perm, a.w, a.hbuf, a.dbuf, a.k,
+        run_items<PHASE, FMT, XF32, 1, 0, true, RB>(static_cast<const char*>(a.x), a.perm, a.w, a.hbuf, a.dbuf, a.k,
                                                 a.H, a.I, m0, m1, s0, s1, first, cnt, item, 1, nullptr, 0, lo,
                                                 hi - lo, part_l + j * kPart);
     }
@@ -714,21 +714,21 @@ __device__ __forceinline__ void small_item(const FfnArgs& a, const moe_expert_ha
 // One (expert, item) of the column-split path, in the expert's format; the
 // caller's whole workgroup calls it (it holds a barrier).  An expert whose
 // format does not fit the sizes contributes nothing, as in the per-wave path.
-template <int PHASE>
+template <int PHASE, int RB = small_rb<PHASE>()>
 __device__ __forceinline__ void small_unit(const FfnArgs& a, const moe_expert_handle& h, int first, int cnt,
                                            int item, f32x4* part_l) {
     const int fmt = uni(h.fmt);
     const bool known = fmt == MOE_W_F32 || fmt == MOE_W_BF16 || fmt == MOE_W_INT4_G128;
     if (!known || ((PHASE == 0 ? a.H : a.I) & (tile_cols(fmt) - 1)) != 0) return;
     if (fmt == MOE_W_BF16) {
-        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_BF16, true>(a, h, first, cnt, item, part_l);
-        else small_item<PHASE, MOE_W_BF16, false>(a, h, first, cnt, item, part_l);
+        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_BF16, true, RB>(a, h, first, cnt, item, part_l);
+        else small_item<PHASE, MOE_W_BF16, false, RB>(a, h, first, cnt, item, part_l);
     } else if (fmt == MOE_W_INT4_G128) {
-        if (PHASE == 0 && a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_INT4_G128, true>(a, h, first, cnt, item, part_l);
-        else small_item<PHASE, MOE_W_INT4_G128, false>(a, h, first, cnt, item, part_l);
+        if (PHASE == 0 && a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_INT4_G128, true, RB>(a, h, first, cnt, item, part_l);
+        else small_item<PHASE, MOE_W_INT4_G128, false, RB>(a, h, first, cnt, item, part_l);
     } else {
-        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_F32, true>(a, h, first, cnt, item, part_l);
-        else small_item<PHASE, MOE_W_F32, false>(a, h, first, cnt, item, part_l);
+        if (PHASE == 1 || a.x_dtype == MOE_DT_F32) small_item<PHASE, MOE_W_F32, true, RB>(a, h, first, cnt, item, part_l);
+        else small_item<PHASE, MOE_W_F32, false, RB>(a, h, first, cnt, item, part_l);
     }
 }
 
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
     __shared__ int offsets_l[kMaxExperts + 1];
     __shared__ int odd_l[kWaves];
     __shared__ int big_l[kWaves];
-    __shared__ f32x4 part_l[kSlices * 2 * kWave];   // column-split path (phase A)
+    __shared__ f32x4 part_l[kSlices * 2 * kWave];   // column-split path
     static_assert(kSmallThreads == kThreads, "the column-split path runs on this kernel's workgroups");
     // Stage the handle table, active list and offsets with independent loads
     // (one round trip) instead of following active -> handle per slot.  The
@@ -790,6 +790,22 @@ __global__ __launch_bounds__(kThreads, waves_per_simd<PHASE>()) void ffn_kernel(
                 const int e = active_l[s];
                 small_unit<0>(a, reinterpret_cast<const moe_expert_handle*>(table_l)[e], offsets_l[e],
                               offsets_l[e + 1] - offsets_l[e], item, part_l);
+            }
+            return;
+        }
+    } else {
+        // phase B likewise, with items of one row block (the per-wave path's
+        // register budget holds their slices; two row blocks would not fit)
+        bool one_tile = true;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) one_tile = one_tile && big_l[w] == 0;
+        const int ipp_s = a.H / 16;
+        if (one_tile && T * ipp_s <= static_cast<int>(gridDim.x)) {
+            const int s = div_small(blockIdx.x, ipp_s), item = blockIdx.x - s * ipp_s;
+            if (s < T) {
+                const int e = active_l[s];
+                small_unit<1, 1>(a, reinterpret_cast<const moe_expert_handle*>(table_l)[e], offsets_l[e],
+                                 offsets_l[e + 1] - offsets_l[e], item, part_l);
             }
             return;
         }

@@ -228,10 +228,11 @@ size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
  * INT4 experts (an expert whose format does not fit contributes nothing to
  * y; its pairs' outputs are undefined).  Each active expert's weights are
  * streamed from HBM once per pass of up to 32 of its tokens (16 for INT4).
- * Every call is deterministic.  Calls with B*k <= 8, and in phase A calls
- * whose T * I/16 items fit the launch with at most 16 tokens per expert,
- * split each expert's input columns over four waves and add the partial
- * sums in a fixed order; other calls sum each item in one wave.  A token's y
+ * Every call is deterministic.  Calls with B*k <= 8, and in each phase
+ * calls whose items (T * I/16 in phase A, T * H/16 in phase B) fit the
+ * launch with at most 16 tokens per expert, split each expert's input
+ * columns over four waves and add the partial sums in a fixed order; other
+ * calls sum each item in one wave.  A token's y
  * is bit-identical across calls that take the same paths (padding tokens
  * never change them) and agrees to fp32 rounding otherwise.
  * Errors: MOE_EINVAL for null pointers, sizes out of range, a short or

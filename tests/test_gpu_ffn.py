@@ -131,8 +131,8 @@ def test_int4_experts_with_fp32_activations():
 def test_small_batch_column_split(fmt, x_dtype, H, I, B, k):
     # calls with B*k <= 8 routed pairs split each item's input columns over
     # the waves of a workgroup and add the partial sums in LDS; larger calls
-    # (6x2, 20x1 here) do so in phase A when T * I/16 items fit the grid and
-    # no expert has more than 16 tokens
+    # (6x2, 20x1 here) do so in a phase whose items fit the grid when no
+    # expert has more than 16 tokens
     N = 16
     int4 = {"int4": range(N), "mixed": range(0, N, 2)}.get(fmt, [])
     layer, host = build_layer(N, k, H, I, 40 + B, fmt="f32" if fmt == "f32" else "bf16", int4_experts=int4,
