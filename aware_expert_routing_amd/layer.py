@@ -81,11 +81,11 @@ class MoELayer:
         if b is None:
             dev, N, k = self.device, self.N, self.k
             i32 = dict(device=dev, dtype=torch.int32)
+            T = torch.empty(1, **i32)   # written by dispatch; the routing result shares it
             route = dict(idx=torch.empty(B, k, **i32), w=torch.empty(B, k, device=dev, dtype=torch.float32),
-                         n_base=torch.empty(B, **i32), mask=torch.empty((N + 31) // 32, **i32),
-                         T=torch.empty(1, **i32))
+                         n_base=torch.empty(B, **i32), mask=torch.empty((N + 31) // 32, **i32), T=T)
             disp = dict(cnt=torch.empty(N, **i32), offsets=torch.empty(N + 1, **i32),
-                        perm=torch.empty(B * k, **i32), active=torch.empty(N, **i32), T=torch.empty(1, **i32))
+                        perm=torch.empty(B * k, **i32), active=torch.empty(N, **i32), T=T)
             ws = torch.zeros(L.ffn_workspace_bytes(B, k, self.H, self.I), device=dev, dtype=torch.uint8)
             b = Buffers(B, torch.empty(B, N, device=dev, dtype=torch.float32), route, disp,
                         torch.empty(B, self.H, device=dev, dtype=torch.float32), ws,

@@ -74,6 +74,7 @@ def test_random_layer_against_oracle(seed):
     assert np.array_equal(buf.route["idx"].cpu().numpy(), ref["idx"])
     assert np.abs(buf.route["w"].cpu().numpy().astype(np.float64) - ref["w"]).max() <= 1e-6
     assert int(buf.disp["T"].item()) == len(set(ref["idx"][ref["idx"] >= 0].tolist()))
+    assert int(buf.route["T"].item()) == int(buf.disp["T"].item())   # the routing result reports the same T
     yref = oracle.expert_ffn(host, H, I, x, ref["idx"], ref["w"])
     if not np.any(ref["idx"] >= 0):   # every token is padding: the output is exactly zero
         assert not torch.any(buf.y).item()
