@@ -49,7 +49,14 @@ class ExpertTensors:
 
 @dataclass
 class Buffers:
-    """Per-batch-size device buffers for one forward call."""
+    """Per-batch-size device buffers for one forward call.
+
+    route: idx [B, k] and w [B, k] (the routing result), n_base [B] and mask
+    [ceil(N/32)] (OEA and pruned modes only: the baseline counts and S_base;
+    vanilla top-k leaves them as they were), T [1] (the same tensor as
+    disp["T"]).  disp: cnt, offsets, perm, active, T (dispatch output).
+    y: [B, H] layer output.  ws: the expert FFN's workspace.  extra["sync"]:
+    the fused router kernel's completion counter (zero between calls)."""
     B: int
     logits: torch.Tensor
     route: dict
