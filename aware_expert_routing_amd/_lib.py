@@ -271,7 +271,7 @@ def expert_ffn(table, N: int, H: int, I: int, x, idx, w, disp, y=None, ws=None, 
         y = torch.empty(B, H, device=dev, dtype=torch.float32)
     nbytes = ffn_workspace_bytes(B, k, H, I)
     if ws is None:
-        ws = torch.zeros(nbytes, device=dev, dtype=torch.uint8)   # counters start at zero
+        ws = torch.zeros(nbytes, device=dev, dtype=torch.uint8)
     _check("moe_expert_ffn", lib().moe_expert_ffn(
         _ptr(table), N, H, I, _ptr(x), _x_dtype(x), _ptr(idx), _ptr(w), _ptr(disp["offsets"]),
         _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]), B, k, _ptr(y), _ptr(ws),
