@@ -711,15 +711,18 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(const XT* _
     }
 }
 
-// Logits of the kFusedExperts experts e0 .. for tokens t0 + 4 g .. + 3 by
-// group g of kGemvThreads threads: each thread multiplies its 8 columns of
-// the 4 experts' router rows with the same columns of the 4 tokens, so one
+// Logits of the kE experts e0 .. for tokens t0 + 4 g .. + 3 by group g of
+// kGemvThreads threads: each thread multiplies its 8 columns of the kE
+// experts' router rows with the same columns of the 4 tokens, so one
 // workgroup reads the activations of its 16 tokens once (not once per
-// expert).  Partial sums per row of 16 lanes land in part[row][4 e + t].
-template <typename XT>
+// expert).  Each group reads the kE router rows itself, so few experts per
+// workgroup keep the bytes through one CU low (two experts and 16 tokens:
+// 4 x 16 KB of router rows and 64 KB of activations).  Partial sums per row
+// of 16 lanes land in part[row][4 e + t].
+template <typename XT, int kE>
 __device__ __forceinline__ void gemv_4x4(const XT* __restrict__ x, const float* __restrict__ w_r, int H, int N,
                                          int e0, int t0, int nt, int g, int tid, float (*part)[kGemvTok]) {
-    constexpr int kE = 4, kT = 4;
+    constexpr int kT = 4;
     const int lane = tid & (kWave - 1);
     const int col0 = 8 * lane + 512 * (tid / kWave);
     const int stride = 8 * kGemvThreads;
@@ -761,13 +764,14 @@ __device__ __forceinline__ void gemv_4x4(const XT* __restrict__ x, const float* 
 
 // Router logits, routing and dispatch in one launch.  Workgroup (gx, gy)
 // computes the logits of experts kFusedExperts gx .. + kFusedExperts - 1 for
-// tokens 16 gy .. 16 gy + 15 (group g of kGemvThreads threads takes tokens
-// 4 g .. 4 g + 3 of all kFusedExperts experts), writes them with
+// tokens 16 gy .. 16 gy + 15 (group g of kFusedGroups groups of kGemvThreads
+// threads takes tokens 4 g .. 4 g + 3 of those experts), writes them with
 // device-scope stores, waits for those stores and counts itself done.  The workgroup that completes the
 // count routes and dispatches the whole batch (its 16 wavefronts, one token
 // per wavefront at a time), reading the logits with device-scope loads, and
 // clears the count for the next call.  No workgroup waits for another.
-constexpr int kFusedExperts = 4;
+constexpr int kFusedExperts = 2;   // experts per workgroup
+constexpr int kFusedGroups = 4;    // thread groups per workgroup, 4 tokens each
 
 __device__ __forceinline__ void wait_vmem() {   // s_waitcnt vmcnt(0)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -776,22 +780,22 @@ __device__ __forceinline__ void wait_vmem() {   // s_waitcnt vmcnt(0)
 }
 
 template <typename XT, bool kOea, int G>
-__global__ __launch_bounds__(kGemvThreads * kFusedExperts) void router_route_kernel(
+__global__ __launch_bounds__(kGemvThreads * kFusedGroups) void router_route_kernel(
         const XT* __restrict__ x, const float* __restrict__ w_r, int B, int H, int N, float* __restrict__ logits,
         int k, int k0, float p, int renorm, int32_t* __restrict__ idx, float* __restrict__ w,
         int32_t* __restrict__ n_base, uint32_t* __restrict__ mask_out, int32_t* __restrict__ T_out,
         int32_t* __restrict__ cnt, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
         int32_t* __restrict__ active, int pruned, int max_p, const int32_t* __restrict__ n_valid,
         const int32_t* __restrict__ k0_by_batch, int32_t* __restrict__ sync) {
-    __shared__ float part[kFusedExperts][kGemvThreads / 16][kGemvTok];
+    __shared__ float part[kFusedGroups][kGemvThreads / 16][kGemvTok];
     __shared__ int last_s;
-    static_assert(kFusedExperts == 4 && kGemvTok == 16, "gemv_4x4 layout");
+    static_assert(kFusedGroups * 4 == kGemvTok && kFusedExperts * 4 <= kGemvTok, "gemv_4x4 layout");
     const int g = threadIdx.x / kGemvThreads;
     const int tid = threadIdx.x - g * kGemvThreads;
     const int e0 = blockIdx.x * kFusedExperts;
     const int t0 = blockIdx.y * kGemvTok;
     const int nt = min(kGemvTok, B - t0);
-    gemv_4x4<XT>(x, w_r, H, N, e0, t0, nt, g, tid, part[g]);
+    gemv_4x4<XT, kFusedExperts>(x, w_r, H, N, e0, t0, nt, g, tid, part[g]);
     __syncthreads();
     if (threadIdx.x < kFusedExperts * kGemvTok) {   // (expert, token) = (threadIdx / 16, threadIdx % 16)
         const int el = threadIdx.x / kGemvTok, t = threadIdx.x % kGemvTok;
@@ -907,7 +911,7 @@ hipError_t launch_router_route_dispatch(const void* x, int x_dtype, const float*
                                         int32_t* n_base, uint32_t* mask, int32_t* cnt, int32_t* offsets,
                                         int32_t* perm, int32_t* active, int32_t* T, int32_t* sync, hipStream_t s) {
     const dim3 grid((N + kFusedExperts - 1) / kFusedExperts, (B + kGemvTok - 1) / kGemvTok);
-    const int threads = kGemvThreads * kFusedExperts;
+    const int threads = kGemvThreads * kFusedGroups;
     const bool oea = mode != MOE_ROUTE_TOPK;
     const int pruned = mode == MOE_ROUTE_PRUNED;
     const int mp = mode == MOE_ROUTE_OEA ? max_p : N;
