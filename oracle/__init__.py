@@ -38,7 +38,7 @@ def build(force: bool = True) -> str:
     os.makedirs(_BUILD, exist_ok=True)
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"]
+           "-fno-fast-math", "-fopenmp", "-Wall", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -72,8 +72,32 @@ def _load():
     lib.orc_expert_ffn.argtypes = [P, I, I, P, P, P, I, I, P]
     lib.orc_quantize_int4.argtypes = [P, I, I, P, P]
     lib.orc_hotness_ema.argtypes = [P, P, I, ctypes.c_double]
+    lib.orc_set_threads.argtypes = [I]
+    lib.orc_get_threads.restype = I
+    lib.orc_set_threads(_default_threads())
     _lib = lib
     return lib
+
+
+def _default_threads() -> int:
+    """OMP_NUM_THREADS if set, else the usable cores, at most 16."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def set_threads(n: int) -> None:
+    """Threads of the expert FFN's OpenMP loops (results do not depend on it)."""
+    _load().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().orc_get_threads())
 
 
 def _ptr(a: np.ndarray):

@@ -366,39 +366,68 @@ static double weight_at(int fmt, const void *m, const uint16_t *sc, int cols, in
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* Expert FFN and weighted combine, per token and slot, all in double:
- *   g = W_gate x, u = W_up x, a = silu(g) * u, d = W_down a,
- *   y[i] = sum over token i's slots (rank order) of w * d.
- * x is [B, H] (already widened), w is [B, k], idx is [B, k] (-1 = empty). */
+/* Expert FFN and weighted combine, all in double, for every routed pair
+ * (token i, slot s) with expert e = idx[i, s]:
+ *   g = W_gate x_i, u = W_up x_i, a = silu(g) * u, d = W_down a,
+ *   y[i] = sum over token i's filled slots, in slot (rank) order, of w[i, s] * d.
+ * x is [B, H] (already widened), w is [B, k], idx is [B, k] (-1 = empty).
+ * The work runs in three loops: the SwiGLU activations a of every (pair, row
+ * of I), then the down projections d of every (pair, row of H), then the
+ * combine, one output element at a time.  Each a and d element is one plain
+ * dot product in index order, whichever thread computes it, and the combine
+ * is sequential, so the result does not depend on the thread count
+ * (orc_set_threads; OpenMP across pairs and rows). */
+static int g_threads = 1;
+
+void orc_set_threads(int n) { g_threads = n > 0 ? n : 1; }
+
+int orc_get_threads(void) { return g_threads; }
+
 void orc_expert_ffn(const orc_expert *ex, int H, int I, const double *x, const int32_t *idx,
                     const double *w, int B, int k, double *y)
 {
-    double *a = (double *)malloc(sizeof(double) * (size_t)I);
+    long pairs = (long)B * k;
+    double *a = (double *)malloc(sizeof(double) * (size_t)pairs * (size_t)I);
+    double *d = (double *)malloc(sizeof(double) * (size_t)pairs * (size_t)H);
+    long n_a = pairs * I, n_d = pairs * H;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (long t = 0; t < n_a; ++t) {
+        long q = t / I;
+        int j = (int)(t % I);
+        int e = idx[q];
+        if (e < 0) continue;
+        const orc_expert *E = &ex[e];
+        const double *xi = x + (size_t)(q / k) * H;
+        double g = 0.0, u = 0.0;
+        for (int h = 0; h < H; ++h) {
+            g += weight_at(E->fmt, E->gate, E->s_gate, H, j, h) * xi[h];
+            u += weight_at(E->fmt, E->up, E->s_up, H, j, h) * xi[h];
+        }
+        a[(size_t)q * I + j] = silu(g) * u;
+    }
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (long t = 0; t < n_d; ++t) {
+        long q = t / H;
+        int o = (int)(t % H);
+        int e = idx[q];
+        if (e < 0) continue;
+        const orc_expert *E = &ex[e];
+        const double *aq = a + (size_t)q * I;
+        double acc = 0.0;
+        for (int j = 0; j < I; ++j) acc += weight_at(E->fmt, E->down, E->s_down, I, o, j) * aq[j];
+        d[(size_t)q * H + o] = acc;
+    }
     for (int i = 0; i < B; ++i) {
         double *yi = y + (size_t)i * H;
         for (int o = 0; o < H; ++o) yi[o] = 0.0;
-        const double *xi = x + (size_t)i * H;
         for (int s = 0; s < k; ++s) {
-            int e = idx[(size_t)i * k + s];
-            if (e < 0) continue;
-            const orc_expert *E = &ex[e];
-            for (int j = 0; j < I; ++j) {
-                double g = 0.0, u = 0.0;
-                for (int h = 0; h < H; ++h) {
-                    g += weight_at(E->fmt, E->gate, E->s_gate, H, j, h) * xi[h];
-                    u += weight_at(E->fmt, E->up, E->s_up, H, j, h) * xi[h];
-                }
-                a[j] = silu(g) * u;
-            }
-            double ws = w[(size_t)i * k + s];
-            for (int o = 0; o < H; ++o) {
-                double d = 0.0;
-                for (int j = 0; j < I; ++j) d += weight_at(E->fmt, E->down, E->s_down, I, o, j) * a[j];
-                yi[o] += ws * d;
-            }
+            long q = (long)i * k + s;
+            if (idx[q] < 0) continue;
+            for (int o = 0; o < H; ++o) yi[o] += w[q] * d[(size_t)q * H + o];
         }
     }
     free(a);
+    free(d);
 }
 
 /* ------------------------------------------------------------------------- */

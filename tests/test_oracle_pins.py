@@ -415,6 +415,51 @@ def test_int4_quantiser_bounds_and_round_trip():
     assert np.array_equal(repacked, q)
 
 
+def test_int4_quantiser_rounds_exact_ties_to_even():
+    # The INT4 reading takes q = rint(w / s) with ties to even.  With a group
+    # absmax of 7 * 2^-6 the scale is s = fp16(2^-6) = 2^-6 exactly, so each
+    # w = (j + 1/2) * 2^-6 (exact in bf16) has w / s exactly halfway between
+    # two integers.  Ties to even give 0, 2, 2, 4, 4, 6, 6 for |w / s| = 0.5 ..
+    # 6.5 (signs kept); rounding ties away from zero would give 1, 2, 3, 4, 5,
+    # 6, 7, and truncation 0, 1, 2, 3, 4, 5, 6, so either mistake fails here.
+    halves = [0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5]
+    expect_pos = [0, 2, 2, 4, 4, 6, 6]
+    unit = 2.0 ** -6
+    row = [7.0 * unit] + [h * unit for h in halves] + [-h * unit for h in halves]
+    want = [7] + expect_pos + [-q for q in expect_pos]
+    vals = np.zeros(128, np.float32)
+    vals[:len(row)] = row
+    qv = np.zeros(128, np.int32)
+    qv[:len(want)] = want
+    w = synth.to_bf16_bits(vals)[None, :]
+    assert np.array_equal(synth.bf16_bits_to_f32(w)[0], vals)          # exact in bf16
+    q, s = oracle.quantize_int4(w)
+    assert s[0, 0] == 0x2400                                           # fp16 2^-6
+    assert np.array_equal(_unpack(q, 1, 128)[0], qv)
+
+
+def test_ffn_result_does_not_depend_on_thread_count():
+    N, H, I, B, k = 6, 256, 128, 7, 3
+    ex = []
+    for e in range(N):
+        g, u, d = synth.expert_weights_bf16(9, e, H, I)
+        ex.append(dict(fmt=oracle.FMT_BF16, gate=g, up=u, down=d))
+    x = synth.activations(9, B, H)
+    r = oracle.route(synth.logits(9, B, N, 2.0), k, oea=True, k0=1)
+    before = oracle.get_threads()
+    try:
+        oracle.set_threads(1)
+        y1 = oracle.expert_ffn(ex, H, I, x, r["idx"], r["w"])
+        oracle.set_threads(5)
+        y5 = oracle.expert_ffn(ex, H, I, x, r["idx"], r["w"])
+    finally:
+        oracle.set_threads(before)
+    assert np.array_equal(y1, y5)
+    # per token, the combine is the rank-ordered sum of its slots' rows
+    one = [oracle.expert_ffn(ex, H, I, x[i:i + 1], r["idx"][i:i + 1], r["w"][i:i + 1]) for i in range(B)]
+    assert np.array_equal(np.concatenate(one), y1)
+
+
 def test_int4_ffn_equals_f32_ffn_of_dequantised_weights():
     N, H, I, B, k = 3, 128, 128, 4, 2
     exq, exf = [], []
