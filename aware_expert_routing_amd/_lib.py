@@ -99,6 +99,7 @@ _SIGNATURES = [
     ("moe_residency_pending", [_P], _I),
     ("moe_residency_get_stats", [_P, ctypes.POINTER(ResidencyStats)], _I),
     ("moe_residency_destroy", [_P], _I),
+    ("moe_stream_read", [_P, _S, _P, _P], _I),
     ("moe_status_str", [_I], ctypes.c_char_p),
     ("moe_last_error", [], ctypes.c_char_p),
 ]
@@ -133,6 +134,18 @@ def _ptr(t) -> int | None:
     if not t.is_contiguous():
         raise ValueError("tensors passed to libmoe must be contiguous")
     return t.data_ptr()
+
+
+def _check_i32_table(t, need: int, name: str, device) -> None:
+    """A device int32 table the kernels index on the device (n_valid[0],
+    k0_by_batch[b] for b <= B): wrong placement, type or length would be an
+    out-of-bounds device read, so it is refused here."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.device != device:
+        raise ValueError(f"{name} must be an int32 tensor on {device}")
+    if not t.is_contiguous() or t.numel() < need:
+        raise ValueError(f"{name} must be contiguous with at least {need} entries (has {t.numel()})")
 
 
 def _stream(stream=None) -> int:
@@ -225,6 +238,8 @@ def route_dispatch(logits, k: int, mode: str, k0: int = 0, p: float = 1.0, renor
         disp = dict(cnt=torch.empty(N, **i32), offsets=torch.empty(N + 1, **i32), perm=torch.empty(B * k, **i32),
                     active=torch.empty(N, **i32), T=torch.empty(1, **i32))
     m = {"topk": MOE_ROUTE_TOPK, "oea": MOE_ROUTE_OEA, "pruned": MOE_ROUTE_PRUNED}[mode]
+    _check_i32_table(n_valid, 1, "n_valid", dev)
+    _check_i32_table(k0_by_batch, B + 1, "k0_by_batch", dev)
     _check("moe_route_dispatch", lib().moe_route_dispatch(
         _ptr(logits), B, N, k, m, int(k0), float(p), N if max_p is None else int(max_p), int(bool(renorm)),
         _ptr(n_valid), _ptr(k0_by_batch), _ptr(route["idx"]), _ptr(route["w"]), _ptr(route.get("n_base")), _ptr(route.get("mask")),
@@ -252,6 +267,9 @@ def router_route_dispatch(x, w_r, k: int, mode: str, k0: int = 0, p: float = 1.0
         disp = dict(cnt=torch.empty(N, **i32), offsets=torch.empty(N + 1, **i32), perm=torch.empty(B * k, **i32),
                     active=torch.empty(N, **i32), T=torch.empty(1, **i32))
     m = {"topk": MOE_ROUTE_TOPK, "oea": MOE_ROUTE_OEA, "pruned": MOE_ROUTE_PRUNED}[mode]
+    _check_i32_table(n_valid, 1, "n_valid", dev)
+    _check_i32_table(k0_by_batch, B + 1, "k0_by_batch", dev)
+    _check_i32_table(sync, 1, "sync", dev)
     _check("moe_router_route_dispatch", lib().moe_router_route_dispatch(
         _ptr(x), _x_dtype(x), _ptr(w_r), B, H, N, k, m, int(k0), float(p), N if max_p is None else int(max_p),
         int(bool(renorm)), _ptr(n_valid), _ptr(k0_by_batch), _ptr(logits), _ptr(route["idx"]), _ptr(route["w"]),
@@ -310,6 +328,14 @@ def hotness_ema(S, cnt, alpha: float, stream=None):
     _check("moe_hotness_ema", lib().moe_hotness_ema(_ptr(S), _ptr(cnt), S.shape[0], float(alpha),
                                                     _stream(stream)))
     return S
+
+
+def stream_read(buf, out, stream=None):
+    """moe_stream_read: one read pass over buf (the HBM read-ceiling probe);
+    XORs buf's 32-bit words into out[0]."""
+    _check("moe_stream_read", lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                                    _stream(stream)))
+    return out
 
 
 def status_str(status: int) -> str:

@@ -17,7 +17,7 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "residency.cpp", "route.hip", "ffn.hip", "quant.hip", "pack.hip"]
+SOURCES = ["abi.cpp", "residency.cpp", "route.hip", "ffn.hip", "quant.hip", "pack.hip", "probe.hip"]
 NO_CONTRACT = {"route.hip", "quant.hip"}
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "internal.h"
+#include "../../include/moe_probe.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
@@ -158,11 +159,13 @@ MOE_API size_t moe_ffn_workspace_bytes(int B, int k, int H, int I) {
     return moe::ffn_workspace_bytes(B, k, H, I);
 }
 
-MOE_API int moe_expert_ffn(const moe_expert_handle* table, int N, int H, int I, const void* x,
-                           int x_dtype, const int32_t* idx, const float* w, const int32_t* offsets,
-                           const int32_t* perm, const int32_t* active, const int32_t* T, int B,
-                           int k, float* y, void* ws, size_t ws_bytes, void* stream) {
-    if (!table || !x || !idx || !w || !offsets || !perm || !active || !T || !y || !ws)
+namespace {
+
+// Checks shared by both expert-FFN entry points (everything but the workspace).
+int check_ffn(const moe_expert_handle* table, int N, int H, int I, const void* x, int x_dtype, const int32_t* idx,
+              const float* w, const int32_t* offsets, const int32_t* perm, const int32_t* active, const int32_t* T,
+              int B, int k, float* y) {
+    if (!table || !x || !idx || !w || !offsets || !perm || !active || !T || !y)
         return fail(MOE_EINVAL, "null pointer");
     int st = check_sizes(B, N, k);
     if (st) return st;
@@ -170,15 +173,34 @@ MOE_API int moe_expert_ffn(const moe_expert_handle* table, int N, int H, int I, 
     if (H < 32 || H % 32 || I < 32 || I % 32) return fail(MOE_EINVAL, "H and I must be positive multiples of 32");
     if (H > 16384 || I > 16384) return fail(MOE_EUNSUPPORTED, "H and I above 16384 are not supported");
     if (!moe::ffn_cost_fits(B, k, N, H, I)) return fail(MOE_EUNSUPPORTED, "B*k too large for H and I");
-    if (ws_bytes < moe::ffn_workspace_bytes(B, k, H, I)) return fail(MOE_EINVAL, "workspace too small");
-    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
     if (reinterpret_cast<uintptr_t>(table) % 16 != 0) return fail(MOE_EINVAL, "handle table must be 16-byte aligned");
+    return MOE_OK;
+}
+
+moe::FfnArgs ffn_args(const moe_expert_handle* table, int N, int H, int I, const void* x, int x_dtype,
+                      const int32_t* idx, const float* w, const int32_t* offsets, const int32_t* perm,
+                      const int32_t* active, const int32_t* T, int B, int k, float* y) {
     moe::FfnArgs a{};
     a.table = table;
     a.N = N; a.H = H; a.I = I; a.B = B; a.k = k;
     a.x = x; a.x_dtype = x_dtype;
     a.idx = idx; a.w = w; a.offsets = offsets; a.perm = perm; a.active = active; a.T = T;
     a.y = y;
+    return a;
+}
+
+}  // namespace
+
+MOE_API int moe_expert_ffn(const moe_expert_handle* table, int N, int H, int I, const void* x,
+                           int x_dtype, const int32_t* idx, const float* w, const int32_t* offsets,
+                           const int32_t* perm, const int32_t* active, const int32_t* T, int B,
+                           int k, float* y, void* ws, size_t ws_bytes, void* stream) {
+    if (!ws) return fail(MOE_EINVAL, "null pointer");
+    int st = check_ffn(table, N, H, I, x, x_dtype, idx, w, offsets, perm, active, T, B, k, y);
+    if (st) return st;
+    if (ws_bytes < moe::ffn_workspace_bytes(B, k, H, I)) return fail(MOE_EINVAL, "workspace too small");
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+    const moe::FfnArgs a = ffn_args(table, N, H, I, x, x_dtype, idx, w, offsets, perm, active, T, B, k, y);
     return hip_status(moe::launch_expert_ffn(a, ws, as_stream(stream)), "moe_expert_ffn");
 }
 
@@ -231,4 +253,12 @@ MOE_API int moe_hotness_ema(float* S, const int32_t* cnt, int N, float alpha, vo
     if (N < 1 || N > moe::kMaxExperts) return fail(MOE_EINVAL, "N must be in [1, 128]");
     if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(MOE_EINVAL, "alpha must be in [0, 1]");
     return hip_status(moe::launch_hotness_ema(S, cnt, N, alpha, as_stream(stream)), "moe_hotness_ema");
+}
+
+MOE_API int moe_stream_read(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+    if (!buf || !out) return fail(MOE_EINVAL, "null pointer");
+    if (bytes < 16 || bytes % 16) return fail(MOE_EINVAL, "bytes must be a positive multiple of 16");
+    if (reinterpret_cast<uintptr_t>(buf) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
+        return fail(MOE_EINVAL, "buf must be 16-byte aligned");
+    return hip_status(moe::launch_stream_read(buf, bytes, out, moe::device_cus(), as_stream(stream)), "moe_stream_read");
 }

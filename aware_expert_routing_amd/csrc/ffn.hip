@@ -962,6 +962,8 @@ __global__ __launch_bounds__(kWave) void combine_kernel(FfnArgs a) {
 
 int g_num_cus[64] = {0};
 
+}  // namespace
+
 int device_cus() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -973,6 +975,8 @@ int device_cus() {
     }
     return g_num_cus[dev];
 }
+
+namespace {
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 

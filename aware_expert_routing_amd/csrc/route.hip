@@ -807,10 +807,15 @@ __global__ __launch_bounds__(kGemvThreads * kFusedGroups) void router_route_kern
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    // Hand-off: every wave waits for its logit stores to complete, the
+    // workgroup barrier orders them before thread 0's count, and the count is
+    // an agent-scope release (publishing this workgroup's logits) and acquire
+    // (in the workgroup that completes it, of every other workgroup's logits);
+    // the barrier after it passes the acquire on to the routing waves.
     wait_vmem();
     __syncthreads();
     if (threadIdx.x == 0)
-        last_s = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        last_s = __hip_atomic_fetch_add(sync, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
                  static_cast<int>(gridDim.x * gridDim.y) - 1;
     __syncthreads();
     if (!last_s) return;

@@ -129,3 +129,25 @@ class Residency:
             self.close()
         except Exception:
             pass
+
+
+def ema_hot_set(xs, w_r: torch.Tensor, bias: torch.Tensor, k: int, n_hot: int, alpha: float = 0.9,
+                stream=None) -> list[int]:
+    """A static high-precision set from routing history (page "DynaExq",
+    section 2.5: per-expert counts folded into S <- alpha S + (1 - alpha) c;
+    section 2.5 / 3.5: the top-n_hi experts by S).
+
+    For each batch x in `xs` (in order): router logits (moe_router_logits)
+    plus the per-expert `bias`, vanilla top-k routing and dispatch
+    (moe_route_dispatch), and the hotness update (moe_hotness_ema) on the
+    dispatch counts, starting from S = 0.  Returns the n_hot experts with the
+    largest S, ties to the lower index, in ascending expert order.
+    """
+    N = w_r.shape[0]
+    S = torch.zeros(N, device=w_r.device, dtype=torch.float32)
+    for x in xs:
+        logits = L.router_logits(x, w_r, stream=stream) + bias[None, :]
+        _, disp = L.route_dispatch(logits, k, "topk", stream=stream)
+        L.hotness_ema(S, disp["cnt"], alpha, stream=stream)
+    order = torch.argsort(S.cpu(), descending=True, stable=True)
+    return sorted(int(e) for e in order[:n_hot])

@@ -32,6 +32,14 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "MoE-layer decode µs & HBM GB/s (% peak) vs unique experts T, top-8 vs OEA"
 
 
+_T0 = time.time()
+
+
+def progress(msg: str) -> None:
+    """One progress line on stderr (the JSON result goes to stdout)."""
+    print(f"bench [{time.time() - _T0:6.1f} s] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -44,9 +52,11 @@ def parse():
     ap.add_argument("--batches", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["oea", "topk", "mixed"], default=None,
-                    help="time only this routing, or only the mixed bf16/INT4 layer at B=32 (for profiler runs)")
+    ap.add_argument("--only", choices=["oea", "topk", "mixed", "point"], default=None,
+                    help="time only this routing, only the mixed bf16/INT4 layer at B=32, or only one "
+                         "batch-sweep point (--batch, --routing, --k0, --zipf) (for profiler runs)")
+    ap.add_argument("--routing", choices=["oea", "topk"], default="oea", help="routing of --only point")
+    ap.add_argument("--zipf", type=float, default=1.1, help="Zipf bias exponent of --only point (0: uniform)")
     ap.add_argument("--no-extended", action="store_true",
                     help="skip the batch sweep, the 235B-shaped layer and the mixed INT4 layer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -152,6 +162,7 @@ def main():
     xs = [to_dev(x) for x in xs_bits]
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
+    progress(f"setup done ({args.copies} layer copies)")
 
     W_e = 3 * H * I * 2                        # bf16 bytes per expert
     fixed_layer = N * H * 4 + B * H * 2 + B * H * 4
@@ -165,6 +176,7 @@ def main():
             Ts.append(int(buf.disp["T"].item()))
         stream = torch.cuda.current_stream()
         n_ev = args.steps
+        evl = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
         ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
         ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
 
@@ -172,6 +184,8 @@ def main():
             lay = layers[i % len(layers)]
             x = xs[i % len(xs)]
             buf = lay.buffers(B)
+            if timed:
+                evl[i].record(stream)
             # router GEMV + routing + dispatch: one launch
             moe.router_route_dispatch(x, lay.w_r, k, mode, k0, 1.0, True, buf.route, buf.disp, buf.logits,
                                       buf.extra["sync"])
@@ -195,6 +209,7 @@ def main():
             step(i, True)
         torch.cuda.synchronize()
         ffn_ms = [ev0[i].elapsed_time(ev1[i]) for i in range(args.steps)]
+        layer_ms = [evl[i].elapsed_time(ev1[i]) for i in range(args.steps)]
         # the same steps replayed from HIP graphs (one per layer copy and batch)
         graphs = {}
         for i in range(args.steps):
@@ -209,6 +224,12 @@ def main():
             graphs[(i % len(layers), i % len(xs))].replay()
         torch.cuda.synchronize()
         graph_wall = time.perf_counter() - t0
+        for i in range(args.steps):
+            evl[i].record(stream)
+            graphs[(i % len(layers), i % len(xs))].replay()
+            ev1[i].record(stream)
+        torch.cuda.synchronize()
+        graph_ms = [evl[i].elapsed_time(ev1[i]) for i in range(args.steps)]
         del graphs
         Tsteps = [Ts[i % len(Ts)] for i in range(args.steps)]
         layer_bytes = sum(t * W_e + fixed_layer for t in Tsteps)
@@ -222,15 +243,25 @@ def main():
             T_per_batch=Ts,
             ffn_us=ffn_s / args.steps * 1e6,
             ffn_us_p10=float(np.percentile(ffn_ms, 10) * 1e3),
+            ffn_us_p50=float(np.percentile(ffn_ms, 50) * 1e3),
             ffn_us_p90=float(np.percentile(ffn_ms, 90) * 1e3),
             ffn_gbps=ffn_bytes / ffn_s / 1e9,
             ffn_bytes_per_launch=ffn_bytes / args.steps,
+            layer_us_p10=float(np.percentile(layer_ms, 10) * 1e3),
+            layer_us_p50=float(np.percentile(layer_ms, 50) * 1e3),
+            layer_us_p90=float(np.percentile(layer_ms, 90) * 1e3),
             graph_us_per_layer=graph_wall / args.steps * 1e6,
+            graph_us_p10=float(np.percentile(graph_ms, 10) * 1e3),
+            graph_us_p50=float(np.percentile(graph_ms, 50) * 1e3),
+            graph_us_p90=float(np.percentile(graph_ms, 90) * 1e3),
             graph_gbps=layer_bytes / graph_wall / 1e9,
         )
 
     if args.only == "mixed":   # profiler runs of the mixed-residency layer alone (Qwen3-30B shape)
         print(json.dumps({"mixed_int4": mixed_int4(layers, wr_dev, N, k, H, I, gate, up, down)}), flush=True)
+        return
+    if args.only == "point":   # profiler runs of one batch-sweep point
+        print(json.dumps({"point": point_run(layers, wr_dev, N, k, H, I, args)}), flush=True)
         return
 
     results = {}
@@ -243,25 +274,40 @@ def main():
         key = "oea_k0_%d" % k0 if mode == "oea" else "top%d" % k
         if key not in results:
             results[key] = run_mode(mode, k0)
+            progress(f"{key}: FFN {results[key]['ffn_us']:.1f} us, layer p50 {results[key]['layer_us_p50']:.1f} us")
     head = results[list(results)[0]]
 
     # forced-T linearity: B tokens spread over T chosen experts (expert FFN only)
     sweep = None
     if not args.no_sweep and args.only is None:
         sweep = forced_t_sweep(layers, xs[0], B, N, k, W_e, fixed_ffn)
+        progress("forced-T sweep done")
+
+    ceiling = None
+    if args.only is None:
+        ceiling = read_ceiling()
+        progress(f"read ceiling {ceiling['gbps']} GB/s")
 
     extended = None
     if not args.no_extended and args.only is None and args.config == "qwen30b":
-        extended = {"batch_sweep": batch_sweep(layers, wr_dev, N, k, H, I),
-                    "mixed_int4": mixed_int4(layers, wr_dev, N, k, H, I, gate, up, down),
-                    "dynamic_residency": dynamic_residency(wr_dev, N, k, H, I, gate, up, down)}
+        extended = {"small_batch_graphs": small_batch_graphs(layers, N, k, H)}
+        progress("small-batch graphs done")
+        extended["batch_sweep"] = batch_sweep(layers, wr_dev, N, k, H, I)
+        progress("batch sweep done")
+        extended["mixed_int4"] = mixed_int4(layers, wr_dev, N, k, H, I, gate, up, down)
+        progress("mixed INT4 layer done")
+        extended["dynamic_residency"] = dynamic_residency(wr_dev, N, k, H, I, gate, up, down)
+        progress("dynamic residency done")
         del layers[:]
         torch.cuda.empty_cache()
         extended["qwen235b"] = qwen235b_lines()
+        progress("Qwen3-235B-shaped layer done")
 
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
-        cpu = cpu_baseline(args, N, k, H, I, B, gate, up, down, w_r, xs_bits, W_e, fixed_layer)
+        progress("CPU baseline (oracle) starting")
+        cpu = cpu_baseline(args, N, k, H, I, B, gate, up, down, w_r, xs_bits, W_e)
+        progress("CPU baseline done")
 
     out = {
         "metric": METRIC,
@@ -290,7 +336,14 @@ def main():
             "unit": "GB/s",
             "frac": round(head["ffn_gbps"] / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic() if (args.config == "qwen30b" and B == 16 and args.k0 == 3) else None,
+            "read_ceiling_gbps": None if ceiling is None else ceiling["gbps"],
+            "frac_of_read_ceiling": None if ceiling is None else round(head["ffn_gbps"] / ceiling["gbps"], 4),
+            "ffn_us_p10_p50_p90": [round(head["ffn_us_p10"], 2), round(head["ffn_us_p50"], 2),
+                                   round(head["ffn_us_p90"], 2)],
         },
+        "layer_us_p10_p50_p90": [round(head["layer_us_p10"], 2), round(head["layer_us_p50"], 2),
+                                 round(head["layer_us_p90"], 2)],
+        "read_ceiling": ceiling,
         "linearity": sweep,
         "extended": extended,
         "cpu_baseline": cpu,
@@ -439,17 +492,9 @@ def mixed_int4(layers, w_r, N, k, H, I, gate, up, down, B=32, warm=64, hot=32, c
 
     dev = layers[0].device
     beta = torch.from_numpy(synth.zipf_bias(N, 1.1)).to(dev)
-    S = torch.zeros(N, device=dev)
-    lay0 = layers[0]
-    for b in range(warm):
-        x = torch.from_numpy(synth.to_bf16_bits(synth.activations(200 + b, B, H)).view(np.int16)).to(dev) \
-            .view(torch.bfloat16)
-        buf = lay0.buffers(B)
-        logits = moe.router_logits(x, w_r) + beta[None, :]
-        lay0.route(logits, "topk", 0, 1.0, buf)
-        moe.hotness_ema(S, buf.disp["cnt"], 0.9)
-    order = torch.argsort(S.cpu(), descending=True, stable=True).numpy()
-    hot_set = set(int(e) for e in order[:hot])
+    xs_warm = [torch.from_numpy(synth.to_bf16_bits(synth.activations(200 + b, B, H)).view(np.int16)).to(dev)
+               .view(torch.bfloat16) for b in range(warm)]
+    hot_set = set(moe.ema_hot_set(xs_warm, w_r, beta, k, hot, 0.9))
 
     def dev_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -585,19 +630,21 @@ def qwen235b_lines(copies=2, steps=30):
     import aware_expert_routing_amd as moe
     import synth
 
+    from concurrent.futures import ThreadPoolExecutor
+
     dev = torch.device("cuda:0")
     s = synth.SHAPES["qwen235b"]
     N, k, H, I = s["N"], s["k"], s["H"], s["I"]
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(235)
+    w_r = torch.from_numpy(synth.router_weight(235, N, H)).to(dev)
+    packed = [torch.empty(N, rows, cols, device=dev, dtype=torch.bfloat16) for rows, cols in ((I, H), (I, H), (H, I))]
+    with ThreadPoolExecutor(8) as ex:   # the seeded host generator of the parity tests (layer seed 235)
+        for e, mats in enumerate(ex.map(lambda e: synth.expert_weights_bf16(235, e, H, I), range(N))):
+            for m, dst in zip(mats, packed):
+                src = torch.from_numpy(m.view(np.int16)).to(dev).view(torch.bfloat16)
+                moe.pack_weights(moe.MOE_W_BF16, src, dst=dst[e])
     layers = []
-    w_r = torch.randn(N, H, device=dev, generator=gen) * 0.02
     for c in range(copies):
-        mats = []
-        for rows, cols in ((I, H), (I, H), (H, I)):
-            m = (torch.randn(N * rows, cols, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
-            mats.append(moe.pack_weights(moe.MOE_W_BF16, m)[0].view(N, rows, cols))
-            del m
+        mats = packed if c == 0 else [t.clone() for t in packed]
         layers.append(moe.MoELayer(H, I, N, k, w_r, [moe.ExpertTensors(moe.MOE_W_BF16, mats[0][e], mats[1][e],
                                                                        mats[2][e]) for e in range(N)], dev))
     W_e = 3 * H * I * 2
@@ -621,10 +668,23 @@ def qwen235b_lines(copies=2, steps=30):
     return out
 
 
-def cpu_baseline(args, N, k, H, I, B, gate, up, down, w_r, xs_bits, W_e, fixed_layer):
-    """The oracle (plain C, one thread, fp64) on a bounded sample of the same
-    workload: whole layers (router logits, OEA routing, expert FFN) on as many
-    of the benchmark's batches as fit in about --cpu-seconds."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(args, N, k, H, I, B, gate, up, down, w_r, xs_bits, W_e, reps=5):
+    """The oracle (plain C, fp64; OpenMP across routed pairs and rows, the
+    combine sequential, so the result does not depend on the thread count)
+    on whole layers (router logits, routing, expert FFN): the median of
+    `reps` calls at B = 16 (the benchmark's first batch), 1 and 128, for OEA
+    k0 = args.k0 and vanilla top-k, with every host thread the oracle is
+    given, and at the headline point (B = 16, OEA) on one thread."""
     import numpy as np
 
     import oracle
@@ -632,21 +692,166 @@ def cpu_baseline(args, N, k, H, I, B, gate, up, down, w_r, xs_bits, W_e, fixed_l
 
     experts = [dict(fmt=oracle.FMT_BF16, gate=gate[e], up=up[e], down=down[e]) for e in range(N)]
     wr64 = w_r.astype(np.float64)
-    done, bytes_done, t0 = 0, 0, time.perf_counter()
-    while True:
-        x = synth.bf16_bits_to_f32(xs_bits[done % len(xs_bits)]).astype(np.float64)
-        logits = oracle.router_logits(x, wr64).astype(np.float32)
-        r = oracle.route(logits, k, oea=True, k0=args.k0, p=1.0)
-        oracle.expert_ffn(experts, H, I, x, r["idx"], r["w"])
-        bytes_done += r["T"] * W_e + fixed_layer
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or done >= 50:
-            break
-    return {"value": round(bytes_done / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} whole-layer calls (B={B}, OEA k0={args.k0}) of the benchmark's batches, "
-                      f"{el:.1f} s, single-threaded C oracle (fp64)",
-            "us_per_layer": round(el / done * 1e6, 1)}
+
+    def layer_call(x64, mode, k0):
+        logits = oracle.router_logits(x64, wr64).astype(np.float32)
+        r = oracle.route(logits, k, oea=(mode == "oea"), k0=k0, p=1.0)
+        oracle.expert_ffn(experts, H, I, x64, r["idx"], r["w"])
+        return r["T"]
+
+    def timed(x64, mode, k0, n):
+        ts, T = [], 0
+        for _ in range(n):
+            t0 = time.perf_counter()
+            T = layer_call(x64, mode, k0)
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)), T
+
+    threads = oracle.get_threads()
+    t_all = time.perf_counter()
+    points = []
+    for Bp in (B, 1, 128):
+        bits = xs_bits[0] if Bp == B else synth.to_bf16_bits(synth.activations(500, Bp, H))
+        x64 = synth.bf16_bits_to_f32(bits).astype(np.float64)
+        for mode, k0 in (("oea", args.k0), ("topk", 0)):
+            med, T = timed(x64, mode, k0, reps)
+            nbytes = T * W_e + N * H * 4 + Bp * H * 2 + Bp * H * 4
+            points.append({"B": Bp, "routing": f"oea_k0_{k0}" if mode == "oea" else f"top{k}", "T": T,
+                           "threads": threads, "median_s": round(med, 4), "gbps": round(nbytes / med / 1e9, 4)})
+    head = points[0]
+    x64 = synth.bf16_bits_to_f32(xs_bits[0]).astype(np.float64)
+    try:
+        oracle.set_threads(1)
+        med1, T1 = timed(x64, "oea", args.k0, reps)
+    finally:
+        oracle.set_threads(threads)
+    nbytes = T1 * W_e + N * H * 4 + B * H * 2 + B * H * 4
+    single = {"B": B, "routing": head["routing"], "T": T1, "threads": 1, "median_s": round(med1, 4),
+              "gbps": round(nbytes / med1 / 1e9, 4)}
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"value": head["gbps"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"median of {reps} whole-layer oracle calls (router logits, routing, expert FFN) per point: "
+                      f"B={B} (the benchmark's first batch), 1 and 128, OEA k0={args.k0} and top-{k}, "
+                      f"{threads} threads (OpenMP, fp64); value = B={B} OEA k0={args.k0}; plus that point on one "
+                      f"thread; {time.perf_counter() - t_all:.1f} s in all",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": affinity,
+            "us_per_layer": round(head["median_s"] * 1e6, 1), "points": points, "single_thread": single}
+
+
+def read_ceiling(gib=4, reps=10):
+    """HBM read-stream ceiling: moe_stream_read (16-byte non-temporal loads,
+    one pass) over a 4 GiB buffer; median over `reps` timed passes."""
+    import numpy as np
+    import torch
+
+    import aware_expert_routing_amd as moe
+
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(0x5A)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        moe.stream_read(buf, out)
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        e0[i].record(stream)
+        moe.stream_read(buf, out)
+        e1[i].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(reps)]))
+    del buf
+    torch.cuda.empty_cache()
+    return {"kernel": "moe_stream_read", "bytes": nbytes, "us": round(ms * 1e3, 2),
+            "gbps": round(nbytes / ms / 1e6, 1), "frac_of_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+
+
+def small_batch_graphs(layers, N, k, H, steps=60):
+    """Whole-layer latency (router GEMV + routing + dispatch + expert FFN) at
+    B = 1, 2, 4, 8, eager launches against one captured HIP graph per layer
+    copy (page OEA section 7: graph replay of small decode batches), OEA
+    k0 = 3 and vanilla top-8; medians of per-step HIP events."""
+    import numpy as np
+    import torch
+
+    import aware_expert_routing_amd as moe
+    import synth
+
+    dev = layers[0].device
+    stream = torch.cuda.current_stream()
+    out = []
+    for B in (1, 2, 4, 8):
+        xs = [torch.from_numpy(synth.to_bf16_bits(synth.activations(600 + c, B, H)).view(np.int16)).to(dev)
+              .view(torch.bfloat16) for c in range(len(layers))]
+        for mode, k0 in (("oea", 3), ("topk", 0)):
+            e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+            e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+
+            def eager(i, timed=True):
+                c = i % len(layers)
+                if timed:
+                    e0[i].record(stream)
+                layers[c].forward(xs[c], mode, k0, 1.0)
+                if timed:
+                    e1[i].record(stream)
+            for i in range(8):
+                eager(i, False)
+            for i in range(steps):
+                eager(i)
+            torch.cuda.synchronize()
+            eager_us = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(steps)])) * 1e3
+            graphs = [layers[c].capture(xs[c], mode, k0, 1.0) for c in range(len(layers))]
+            for i in range(8):
+                graphs[i % len(graphs)].replay()
+            for i in range(steps):
+                e0[i].record(stream)
+                graphs[i % len(graphs)].replay()
+                e1[i].record(stream)
+            torch.cuda.synchronize()
+            graph_us = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(steps)])) * 1e3
+            del graphs
+            T = int(layers[0].forward(xs[0], mode, k0, 1.0).disp["T"].item())
+            out.append({"B": B, "routing": f"oea_k0_{k0}" if mode == "oea" else f"top{k}", "T_first_copy": T,
+                        "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2)})
+    return out
+
+
+def point_run(layers, w_r, N, k, H, I, args):
+    """One batch-sweep point alone (routing + dispatch + expert FFN per step,
+    router logits plus a Zipf bias given), for counter runs."""
+    import numpy as np
+    import torch
+
+    import aware_expert_routing_amd as moe
+    import synth
+
+    dev = layers[0].device
+    B, mode, k0 = args.batch, args.routing, (args.k0 if args.routing == "oea" else 0)
+    beta = torch.from_numpy(synth.zipf_bias(N, args.zipf)).to(dev)
+    xs = [torch.from_numpy(synth.to_bf16_bits(synth.activations(100 + b, B, H)).view(np.int16)).to(dev)
+          .view(torch.bfloat16) for b in range(5)]
+    logits = [moe.router_logits(x, w_r) + beta[None, :] for x in xs]
+    Ts, sc = [], []
+    for b in range(5):
+        buf = layers[0].buffers(B)
+        layers[0].route(logits[b], mode, k0, 1.0, buf)
+        Ts.append(int(buf.disp["T"].item()))
+        sc.append(int(buf.disp["offsets"][N].item()))
+
+    def step(i):
+        lay = layers[i % len(layers)]
+        buf = lay.buffers(B)
+        lay.route(logits[i % 5], mode, k0, 1.0, buf)
+        lay.ffn(xs[i % 5], buf)
+    us = _time_steps(step, args.steps, warm=args.warmup)
+    W_e = 3 * H * I * 2
+    T = float(np.mean(Ts))
+    return {"B": B, "routing": mode, "k0": k0, "zipf": args.zipf, "T": T, "sum_cnt": float(np.mean(sc)),
+            "steps": args.steps, "us": round(us, 2), "gbps": round(T * W_e / us / 1e3, 1)}
 
 
 if __name__ == "__main__":

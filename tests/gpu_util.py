@@ -72,3 +72,38 @@ def max_err_over_rms(y_gpu: torch.Tensor, y_ref: np.ndarray):
 def gamma(n: int, u: float = 2.0 ** -24) -> float:
     """Standard bound on the relative error of an n-term floating-point sum."""
     return n * u / (1.0 - n * u)
+
+
+def routing_order_is_robust(logits32: np.ndarray, ref_idx: np.ndarray, eps: float) -> bool:
+    """True when no routing decision can differ between two logit matrices
+    that differ by at most eps elementwise: for every token, the logits at
+    consecutive rank positions 0 .. d+1 (d = the deepest rank the routing
+    took, so every comparison the selection made lies inside) are more than
+    2 eps apart.  Lets a test route with the oracle on its own logits and
+    still demand bit-exact indices from the GPU's router output."""
+    B, N = logits32.shape
+    for i in range(B):
+        order = np.lexsort((np.arange(N), -logits32[i].astype(np.float64)))
+        pos = np.empty(N, np.int64)
+        pos[order] = np.arange(N)
+        sel = [int(e) for e in ref_idx[i] if e >= 0]
+        depth = int(max(pos[e] for e in sel)) if sel else 0
+        l = logits32[i][order[:min(N, depth + 2)]].astype(np.float64)
+        if l.size > 1 and np.min(l[:-1] - l[1:]) <= 2.0 * eps:
+            return False
+    return True
+
+
+def sample_tokens(cnt_idx: np.ndarray, N: int, n: int = 8, hot_take: int = 4) -> list[int]:
+    """Up to hot_take tokens of the most-routed expert, then evenly spaced
+    tokens, n in all (fewer if the batch is smaller)."""
+    B = cnt_idx.shape[0]
+    cnt = np.bincount(cnt_idx[cnt_idx >= 0].ravel(), minlength=N)
+    hot = int(np.argmax(cnt))
+    toks = [int(i) for i in np.nonzero((cnt_idx == hot).any(1))[0][:hot_take]]
+    for i in np.linspace(0, B - 1, n).round().astype(int):
+        if len(toks) >= n:
+            break
+        if int(i) not in toks:
+            toks.append(int(i))
+    return sorted(toks)

@@ -10,7 +10,7 @@ import pytest
 import aware_expert_routing_amd as moe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe.h", "moe_residency.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe.h", "moe_residency.h", "moe_probe.h")]
 
 FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails validation
 
@@ -298,3 +298,26 @@ def test_binding_arity_matches_the_headers():
         m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", text)
         params = [a for a in m.group(1).split(",") if a.strip() and a.strip() != "void"]
         assert len(params) == len(args), name
+
+
+def test_binding_refuses_short_or_mistyped_device_tables():
+    # k0_by_batch is read on the device at index B (the real batch size) and
+    # n_valid at index 0: the binding refuses tables that would be read out
+    # of bounds, or whose type or placement is wrong, before any library call
+    import torch
+    logits = torch.zeros(4, 16)
+    x = torch.zeros(4, 32)
+    w_r = torch.zeros(16, 32)
+    bad = [dict(k0_by_batch=torch.zeros(4, dtype=torch.int32)),            # needs B + 1 = 5 entries
+           dict(k0_by_batch=torch.zeros(5, dtype=torch.int64)),
+           dict(k0_by_batch=torch.zeros(10, dtype=torch.int32)[::2]),      # not contiguous
+           dict(n_valid=torch.zeros(0, dtype=torch.int32)),
+           dict(n_valid=torch.zeros(1, dtype=torch.float32)),
+           dict(n_valid=[4])]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            moe.route_dispatch(logits, 4, "oea", 2, **kw)
+        with pytest.raises(ValueError):
+            moe.router_route_dispatch(x, w_r, 4, "oea", 2, **kw)
+    with pytest.raises(ValueError):
+        moe.router_route_dispatch(x, w_r, 4, "oea", 2, sync=torch.zeros(1, dtype=torch.int64))

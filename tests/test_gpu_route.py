@@ -232,10 +232,24 @@ def test_quantizer_bit_exact():
     w[0, :128] = 0                                            # all-zero group
     w[1, :128] = synth.to_bf16_bits(np.full(128, -0.5, np.float32))   # constant negative group
     w[2, 128:256] = synth.to_bf16_bits(synth.normal(32, 128, 30.0))   # large values
+    # exact ties: absmax 7 * 2^-6 makes s = 2^-6, so (j + 1/2) 2^-6 sits halfway
+    # between two codes; ties go to the even code (0, 2, 2, 4, 4, 6, 6)
+    halves = np.array([0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5], np.float32)
+    tie = np.zeros(128, np.float32)
+    tie[0] = 7.0
+    tie[1:8], tie[8:15] = halves, -halves
+    for r, sign in ((3, 1.0), (4, -1.0)):
+        w[r, 256:384] = synth.to_bf16_bits(sign * tie * np.float32(2.0 ** -6))
     q, s = moe.quantize_int4_g128(bf16_dev(w))
     qr, sr = oracle.quantize_int4(w)
     assert np.array_equal(q.cpu().numpy(), qr)
     assert np.array_equal(s.cpu().numpy().view(np.uint16), sr)
+    codes = np.array([7, 0, 2, 2, 4, 4, 6, 6, 0, -2, -2, -4, -4, -6, -6])
+    for r, sign in ((3, 1), (4, -1)):
+        row = q.cpu().numpy()[r, 128:192]                      # columns 256..383, two per byte
+        got = np.empty(128, np.int32)
+        got[0::2], got[1::2] = (row & 0x0F).astype(np.int32) - 8, (row >> 4).astype(np.int32) - 8
+        assert np.array_equal(got[:15], sign * codes) and not got[15:].any()
 
 
 def test_hotness_ema_matches_oracle():
@@ -268,7 +282,11 @@ def test_handle_publish_writes_the_record():
     (37, 128, 2048, 8, "oea", 5, 0.7, None, "bf16"),       # three token groups, ragged
     (128, 128, 2048, 8, "pruned", 3, 1.0, 100, "bf16"),
     (128, 128, 4096, 8, "oea", 5, 1.0, None, "bf16"),      # two sweeps of the hidden dimension
-    (6, 22, 520, 4, "oea", 2, 0.9, 4, "f32"),              # N not a multiple of 4, fp32 activations
+    (6, 22, 520, 4, "oea", 2, 0.9, 4, "f32"),              # N = 22 experts, fp32 activations, padding
+    # odd N: the last workgroup holds one real expert and one past N
+    (7, 23, 520, 4, "oea", 2, 0.9, 5, "f32"),
+    (19, 33, 1024, 8, "topk", 0, 1.0, None, "bf16"),       # two token groups, the second ragged
+    (40, 33, 1024, 8, "oea", 3, 1.0, 37, "bf16"),
 ])
 def test_fused_router_route_dispatch(B, N, H, k, mode, k0, p, nv, dtype):
     # one launch: router GEMV slices, then the last workgroup routes and
@@ -292,3 +310,15 @@ def test_fused_router_route_dispatch(B, N, H, k, mode, k0, p, nv, dtype):
         for key in ("cnt", "offsets", "perm", "active"):
             assert np.array_equal(disp[key].cpu().numpy(), dref[key]), key
         assert int(disp["T"].item()) == dref["T"]
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (3 << 20) + 16 * 17, 64 << 20])
+def test_stream_read_probe_checksum(nbytes):
+    # the read-ceiling probe touches every 16-byte chunk exactly once: the XOR
+    # of all 32-bit words equals numpy's (the unrolled loop and the remainder)
+    words = synth.rng(50, nbytes).integers(0, 2 ** 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to(DEV)
+    out = torch.zeros(1, dtype=torch.int32, device=DEV)
+    moe.stream_read(buf, out)
+    torch.cuda.synchronize()
+    assert int(out.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(words))
