@@ -75,6 +75,7 @@ _SIGNATURES = [
     ("moe_router_route_dispatch", [_P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I] + [_P] * 14, _I),
     ("moe_ffn_workspace_bytes", [_I, _I, _I, _I], _S),
     ("moe_expert_ffn", [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _S, _P], _I),
+    ("moe_expert_ffn_noalloc", [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P], _I),
     ("moe_handle_publish", [_P, _I, ctypes.POINTER(ExpertHandle), _P], _I),
     ("moe_quantize_int4_g128", [_P, _I, _I, _P, _P, _P], _I),
     ("moe_pack_weights", [_I, _P, _P, _I, _I, _P, _P, _P], _I),
@@ -294,6 +295,19 @@ def expert_ffn(table, N: int, H: int, I: int, x, idx, w, disp, y=None, ws=None, 
         _ptr(table), N, H, I, _ptr(x), _x_dtype(x), _ptr(idx), _ptr(w), _ptr(disp["offsets"]),
         _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]), B, k, _ptr(y), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+    return y
+
+
+NOALLOC_WORKSPACE_BYTES = 32 << 20   # MOE_FFN_NOALLOC_WORKSPACE_BYTES
+
+
+def expert_ffn_noalloc(table, N: int, H: int, I: int, x, idx, w, disp, y, stream=None):
+    """moe_expert_ffn_noalloc: the expert FFN with the library's static
+    workspace (the caller passes inputs and the output y only)."""
+    B, k = idx.shape
+    _check("moe_expert_ffn_noalloc", lib().moe_expert_ffn_noalloc(
+        _ptr(table), N, H, I, _ptr(x), _x_dtype(x), _ptr(idx), _ptr(w), _ptr(disp["offsets"]),
+        _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]), B, k, _ptr(y), _stream(stream)))
     return y
 
 

@@ -204,6 +204,21 @@ MOE_API int moe_expert_ffn(const moe_expert_handle* table, int N, int H, int I, 
     return hip_status(moe::launch_expert_ffn(a, ws, as_stream(stream)), "moe_expert_ffn");
 }
 
+MOE_API int moe_expert_ffn_noalloc(const moe_expert_handle* table, int N, int H, int I, const void* x,
+                                   int x_dtype, const int32_t* idx, const float* w, const int32_t* offsets,
+                                   const int32_t* perm, const int32_t* active, const int32_t* T, int B, int k,
+                                   float* y, void* stream) {
+    int st = check_ffn(table, N, H, I, x, x_dtype, idx, w, offsets, perm, active, T, B, k, y);
+    if (st) return st;
+    if (moe::ffn_workspace_bytes(B, k, H, I) > MOE_FFN_NOALLOC_WORKSPACE_BYTES)
+        return fail(MOE_EUNSUPPORTED, "B*k*(H+I)*4 bytes exceed the 32 MiB static workspace of moe_expert_ffn_noalloc");
+    void* ws = nullptr;
+    st = hip_status(moe::ffn_noalloc_workspace(&ws), "moe_expert_ffn_noalloc: static workspace lookup");
+    if (st) return st;
+    const moe::FfnArgs a = ffn_args(table, N, H, I, x, x_dtype, idx, w, offsets, perm, active, T, B, k, y);
+    return hip_status(moe::launch_expert_ffn(a, ws, as_stream(stream)), "moe_expert_ffn_noalloc");
+}
+
 MOE_API int moe_handle_publish(moe_expert_handle* table, int e, const moe_expert_handle* h,
                                void* stream) {
     if (!table || !h) return fail(MOE_EINVAL, "null pointer");

@@ -49,6 +49,7 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace moe {
 namespace {
@@ -980,7 +981,36 @@ namespace {
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// The allocation-free entry point's workspace: one copy per device, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address comes from hipGetSymbolAddress, per
+// device, and only that address is ever passed to a kernel.
+static __device__ __align__(256) char scratch[MOE_FFN_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
 }  // namespace
+
+// Device address of the current device's `scratch`, looked up on the first
+// call on that device (with that device current) and kept.
+hipError_t ffn_noalloc_workspace(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr || reinterpret_cast<uintptr_t>(p) % 256 != 0) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 // The partition sums item costs in 32-bit integers on the device.  Whatever
 // the formats in the handle table, an expert with c tokens has at most

@@ -246,6 +246,27 @@ int moe_expert_ffn(const moe_expert_handle *table, int N, int H, int I, const vo
                    float *y, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_expert_ffn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation.  Arguments, results, limits and errors
+ * are those of moe_expert_ffn; the workspace is instead a fixed device array
+ * of MOE_FFN_NOALLOC_WORKSPACE_BYTES inside the library (one per GPU, held
+ * until the process ends; its address is looked up once per GPU, on the first
+ * call made with that GPU current).  Nothing is allocated or freed.
+ *   Limit: moe_ffn_workspace_bytes(B, k, H, I) <= MOE_FFN_NOALLOC_WORKSPACE_BYTES
+ *   (e.g. B*k <= 2978 pairs at H = 2048, I = 768; B*k <= 1489 at H = 4096,
+ *   I = 1536); larger calls return MOE_EUNSUPPORTED and enqueue nothing.
+ *   Every call on a GPU uses that GPU's one array, which keeps the last call's
+ *   contents (no contents need be preset): calls that may overlap on one GPU
+ *   (several streams or threads) race and must be ordered by the caller.
+ */
+#define MOE_FFN_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+int moe_expert_ffn_noalloc(const moe_expert_handle *table, int N, int H, int I, const void *x,
+                           int x_dtype, const int32_t *idx, const float *w, const int32_t *offsets,
+                           const int32_t *perm, const int32_t *active, const int32_t *T, int B, int k,
+                           float *y, void *stream);
+
+/*
  * Publish a new version of expert e's handle [DYN section 2.2 / 3.2
  * "publish-then-switch": a version becomes visible only after its data is
  * complete; the forward path keeps using the previous version until then].

@@ -88,6 +88,26 @@ def test_expert_ffn_rejects_bad_shapes_and_small_workspace():
     assert lib.moe_expert_ffn(*bad_dtype) == -1
 
 
+def test_expert_ffn_noalloc_rejects_calls_beyond_its_static_workspace():
+    # validation runs before the static workspace is looked up, so no GPU is needed
+    lib = moe.lib()
+    args = lambda B, k, H, I: (FAKE, 128, H, I, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, k, FAKE, None)
+    assert moe.ffn_workspace_bytes(128, 16, 4096, 1536) > moe.NOALLOC_WORKSPACE_BYTES
+    assert lib.moe_expert_ffn_noalloc(*args(128, 16, 4096, 1536)) == -2
+    assert "32 MiB" in lib.moe_last_error().decode()
+    assert lib.moe_expert_ffn_noalloc(*args(16, 8, 2046, 768)) == -1          # H % 32
+    assert lib.moe_expert_ffn_noalloc(*args(200, 8, 2048, 768)) == -2         # B > 128
+    no_y = list(args(16, 8, 2048, 768))
+    no_y[14] = None
+    assert lib.moe_expert_ffn_noalloc(*no_y) == -1
+    # the header's limit and the binding's copy agree; the largest benchmarked calls fit
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    assert re.search(r"MOE_FFN_NOALLOC_WORKSPACE_BYTES \(\(size_t\)32 << 20\)", text)
+    assert moe.NOALLOC_WORKSPACE_BYTES == 32 << 20
+    assert moe.ffn_workspace_bytes(128, 8, 2048, 768) <= moe.NOALLOC_WORKSPACE_BYTES
+    assert moe.ffn_workspace_bytes(64, 8, 4096, 1536) <= moe.NOALLOC_WORKSPACE_BYTES
+
+
 def test_router_logits_rejects_bad_hidden():
     lib = moe.lib()
     assert lib.moe_router_logits(FAKE, 1, FAKE, 4, 250, 16, FAKE, None) == -1
