@@ -100,7 +100,7 @@ _SIGNATURES = [
     ("moe_residency_pending", [_P], _I),
     ("moe_residency_get_stats", [_P, ctypes.POINTER(ResidencyStats)], _I),
     ("moe_residency_destroy", [_P], _I),
-    ("moe_stream_read", [_P, _S, _P, _P], _I),
+    ("moe_stream_read", [_P, _S, _I, _P, _P], _I),
     ("moe_status_str", [_I], ctypes.c_char_p),
     ("moe_last_error", [], ctypes.c_char_p),
 ]
@@ -344,11 +344,11 @@ def hotness_ema(S, cnt, alpha: float, stream=None):
     return S
 
 
-def stream_read(buf, out, stream=None):
+def stream_read(buf, out, waves_per_cu: int = 8, stream=None):
     """moe_stream_read: one read pass over buf (the HBM read-ceiling probe);
     XORs buf's 32-bit words into out[0]."""
-    _check("moe_stream_read", lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
-                                                    _stream(stream)))
+    _check("moe_stream_read", lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(waves_per_cu),
+                                                    _ptr(out), _stream(stream)))
     return out
 
 

@@ -211,7 +211,8 @@ MOE_API int moe_expert_ffn_noalloc(const moe_expert_handle* table, int N, int H,
     int st = check_ffn(table, N, H, I, x, x_dtype, idx, w, offsets, perm, active, T, B, k, y);
     if (st) return st;
     if (moe::ffn_workspace_bytes(B, k, H, I) > MOE_FFN_NOALLOC_WORKSPACE_BYTES)
-        return fail(MOE_EUNSUPPORTED, "B*k*(H+I)*4 bytes exceed the 32 MiB static workspace of moe_expert_ffn_noalloc");
+        return fail(MOE_EUNSUPPORTED, "moe_ffn_workspace_bytes(B, k, H, I) exceeds the 32 MiB static workspace of "
+                                      "moe_expert_ffn_noalloc");
     void* ws = nullptr;
     st = hip_status(moe::ffn_noalloc_workspace(&ws), "moe_expert_ffn_noalloc: static workspace lookup");
     if (st) return st;
@@ -270,10 +271,13 @@ MOE_API int moe_hotness_ema(float* S, const int32_t* cnt, int N, float alpha, vo
     return hip_status(moe::launch_hotness_ema(S, cnt, N, alpha, as_stream(stream)), "moe_hotness_ema");
 }
 
-MOE_API int moe_stream_read(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+MOE_API int moe_stream_read(const void* buf, size_t bytes, int waves_per_cu, uint32_t* out, void* stream) {
     if (!buf || !out) return fail(MOE_EINVAL, "null pointer");
     if (bytes < 16 || bytes % 16) return fail(MOE_EINVAL, "bytes must be a positive multiple of 16");
+    if (waves_per_cu < 4 || waves_per_cu > 32 || waves_per_cu % 4)
+        return fail(MOE_EINVAL, "waves_per_cu must be 4, 8, ..., 32");
     if (reinterpret_cast<uintptr_t>(buf) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
         return fail(MOE_EINVAL, "buf must be 16-byte aligned");
-    return hip_status(moe::launch_stream_read(buf, bytes, out, moe::device_cus(), as_stream(stream)), "moe_stream_read");
+    return hip_status(moe::launch_stream_read(buf, bytes, waves_per_cu, out, moe::device_cus(), as_stream(stream)),
+                      "moe_stream_read");
 }

@@ -741,9 +741,11 @@ def cpu_baseline(args, N, k, H, I, B, gate, up, down, w_r, xs_bits, W_e, reps=5)
             "us_per_layer": round(head["median_s"] * 1e6, 1), "points": points, "single_thread": single}
 
 
-def read_ceiling(gib=4, reps=10):
-    """HBM read-stream ceiling: moe_stream_read (16-byte non-temporal loads,
-    one pass) over a 4 GiB buffer; median over `reps` timed passes."""
+def read_ceiling(gib=4, reps=10, shapes=(4, 8, 16, 32)):
+    """HBM read-stream ceiling: moe_stream_read (each wave a contiguous run of
+    kilobytes, 16-byte non-temporal loads, one pass) over a 4 GiB buffer, for
+    several waves per compute unit; the median over `reps` timed passes of
+    the best shape."""
     import numpy as np
     import torch
 
@@ -754,20 +756,25 @@ def read_ceiling(gib=4, reps=10):
     buf.fill_(0x5A)
     out = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     stream = torch.cuda.current_stream()
-    for _ in range(3):
-        moe.stream_read(buf, out)
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        e0[i].record(stream)
-        moe.stream_read(buf, out)
-        e1[i].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(reps)]))
+    by_shape = {}
+    for wpc in shapes:
+        for _ in range(2):
+            moe.stream_read(buf, out, wpc)
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        for i in range(reps):
+            e0[i].record(stream)
+            moe.stream_read(buf, out, wpc)
+            e1[i].record(stream)
+        torch.cuda.synchronize()
+        by_shape[wpc] = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(reps)]))
     del buf
     torch.cuda.empty_cache()
-    return {"kernel": "moe_stream_read", "bytes": nbytes, "us": round(ms * 1e3, 2),
-            "gbps": round(nbytes / ms / 1e6, 1), "frac_of_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+    best = min(by_shape, key=by_shape.get)
+    ms = by_shape[best]
+    return {"kernel": "moe_stream_read", "bytes": nbytes, "waves_per_cu": best, "us": round(ms * 1e3, 2),
+            "gbps": round(nbytes / ms / 1e6, 1), "frac_of_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+            "gbps_by_waves_per_cu": {str(w): round(nbytes / t / 1e6, 1) for w, t in by_shape.items()}}
 
 
 def small_batch_graphs(layers, N, k, H, steps=60):

@@ -201,7 +201,9 @@ int moe_router_route_dispatch(const void *x, int x_dtype, const float *w_r, int 
                               int32_t *n_base, uint32_t *sbase_mask, int32_t *cnt, int32_t *offsets,
                               int32_t *perm, int32_t *active, int32_t *T, int32_t *sync, void *stream);
 
-/* Workspace bytes moe_expert_ffn needs for these sizes (host call). */
+/* Workspace bytes moe_expert_ffn needs for these sizes (host call):
+ * B*k*(I + H)*4 (per routed pair, its SwiGLU activations and weighted down
+ * projection), each part rounded up to 256 bytes. */
 size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
 
 /*

@@ -15,17 +15,20 @@ extern "C" {
 #endif
 
 /*
- * HBM read-stream ceiling: one pass over `bytes` bytes of `buf` with 16-byte
- * non-temporal loads per lane (the expert FFN's weight loads), 8 in flight
- * per lane, 8 workgroups of 256 threads per compute unit.  The achieved rate
- * is the measured ceiling that the weight-streaming kernels' rates are
- * compared with [OEA section 4, Eq. 2: the b*T term is a weight fetch].
- *   buf   : device memory, 16-byte aligned; bytes a positive multiple of 16
- *   out   : device uint32 [1]; the XOR of every 32-bit word of buf is XORed
- *           into it (so clear it first to read the checksum)
- * Errors: MOE_EINVAL for null or misaligned pointers or a bad size.
+ * HBM read-stream ceiling: one pass over `bytes` bytes of `buf`, each wave
+ * reading its own contiguous run of kilobytes with one 16-byte non-temporal
+ * load per lane per kilobyte (the expert FFN's weight loads), 8 kilobytes in
+ * flight per wave, waves_per_cu waves on each compute unit (workgroups of 4
+ * waves).  The best rate over launch shapes is the measured ceiling the
+ * weight-streaming kernels are compared with [OEA section 4, Eq. 2: the b*T
+ * term is a weight fetch].
+ *   buf          : device memory, 16-byte aligned; bytes a positive multiple of 16
+ *   waves_per_cu : 4, 8, 12, ..., 32
+ *   out          : device uint32 [1]; the XOR of every 32-bit word of buf is
+ *                  XORed into it (so clear it first to read the checksum)
+ * Errors: MOE_EINVAL for null or misaligned pointers or a bad size or shape.
  */
-int moe_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream);
+int moe_stream_read(const void *buf, size_t bytes, int waves_per_cu, uint32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

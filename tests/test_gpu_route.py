@@ -312,13 +312,14 @@ def test_fused_router_route_dispatch(B, N, H, k, mode, k0, p, nv, dtype):
         assert int(disp["T"].item()) == dref["T"]
 
 
+@pytest.mark.parametrize("waves_per_cu", [4, 12, 32])
 @pytest.mark.parametrize("nbytes", [16, 4096 + 48, (3 << 20) + 16 * 17, 64 << 20])
-def test_stream_read_probe_checksum(nbytes):
+def test_stream_read_probe_checksum(nbytes, waves_per_cu):
     # the read-ceiling probe touches every 16-byte chunk exactly once: the XOR
     # of all 32-bit words equals numpy's (the unrolled loop and the remainder)
     words = synth.rng(50, nbytes).integers(0, 2 ** 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
     buf = torch.from_numpy(words.view(np.int32)).to(DEV)
     out = torch.zeros(1, dtype=torch.int32, device=DEV)
-    moe.stream_read(buf, out)
+    moe.stream_read(buf, out, waves_per_cu)
     torch.cuda.synchronize()
     assert int(out.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(words))
