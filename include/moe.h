@@ -228,8 +228,11 @@ size_t moe_ffn_workspace_bytes(int B, int k, int H, int I);
  *            that share a workspace must be ordered, e.g. on one stream).
  * Accumulation is fp32.  H and I must be multiples of 32, and of 128 for
  * INT4 experts (an expert whose format does not fit contributes nothing to
- * y; its pairs' outputs are undefined).  Each active expert's weights are
- * streamed from HBM once per pass of up to 32 of its tokens (16 for INT4).
+ * y; its pairs' outputs are undefined).  An active expert's weights are
+ * streamed from HBM once when it has at most 32 tokens (16 for INT4 experts);
+ * a larger expert is handled in passes of that many tokens, which run side by
+ * side and read its weight tiles through the caches, so the later passes
+ * mostly hit the L2.
  * Every call is deterministic.  Calls with B*k <= 8, and in each phase
  * calls whose items (T * I/16 in phase A, T * H/16 in phase B) fit the
  * launch with at most 16 tokens per expert, split each expert's input
