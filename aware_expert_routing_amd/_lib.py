@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIB selects another build of the same library (e.g. the host-sanitized
+# one from build.py --sanitize); by default the in-tree libmoe.so.
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_EFULL = 0, -1, -2, -3, -4
 MOE_RES_LO, MOE_RES_PROMOTING, MOE_RES_HI, MOE_RES_EVICTING = 0, 1, 2, 3

@@ -32,9 +32,18 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OUT_DIR, src + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj,
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build (CPU checks of
+# the ABI validation, pools, budget tracker and policy; the device code is
+# built as usual).  Each -fsanitize= applies to the host pass only.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+ASAN_DIR = os.path.join(OUT_DIR, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libmoe.so")
+
+
+def _compile(src: str, out_dir: str = OUT_DIR, extra=()) -> str:
+    obj = os.path.join(out_dir, src + ".o")
+    cmd = [_hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj,
            "-I", os.path.join(HERE, "..", "include")]
     if src.endswith(".hip"):
         cmd += ["-x", "hip", *DEVICE]
@@ -45,22 +54,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libmoe.so next to this file."""
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every source and link libmoe.so next to this file; with
+    sanitize=True, a host-sanitized copy in _build/asan/ instead (load it with
+    MOE_LIB=<path> and the sanitizer runtime preloaded)."""
+    out_dir, lib, extra = (ASAN_DIR, ASAN_LIB, SANITIZE_HOST) if sanitize else (OUT_DIR, LIB, [])
+    os.makedirs(out_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+        objs = list(ex.map(lambda src: _compile(src, out_dir, extra), SOURCES))
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *extra, *objs, "-o", tmp]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{proc.stdout}\n{proc.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, sanitize="--sanitize" in sys.argv[1:])
     sys.exit(0)

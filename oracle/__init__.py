@@ -26,29 +26,41 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _BUILD = os.path.join(_HERE, "_build")
-_LIB_PATH = os.path.join(_BUILD, "libmoe_oracle.so")
+# MOE_ORACLE_LIB selects the sanitized build (build(sanitize=True))
+_LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_BUILD, "libmoe_oracle.so")
+ASAN_LIB_PATH = os.path.join(_BUILD, "asan", "libmoe_oracle.so")
 
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (plain -O2, IEEE arithmetic, no contraction)."""
-    if not force and os.path.exists(_LIB_PATH):
-        return _LIB_PATH
-    os.makedirs(_BUILD, exist_ok=True)
-    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-fopenmp", "-Wall", "-o", tmp, _SRC, "-lm"]
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, IEEE arithmetic, no contraction).
+    sanitize=True: the same flags with AddressSanitizer and
+    UndefinedBehaviorSanitizer, built with ROCm's clang (whose sanitizer
+    runtime the sanitized libmoe uses too), into _build/asan/."""
+    path = ASAN_LIB_PATH if sanitize else _LIB_PATH
+    if not force and os.path.exists(path):
+        return path
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    tmp = path + ".tmp%d" % os.getpid()
+    if sanitize:
+        cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-fopenmp", "-Wall", "-fsanitize=address,undefined",
+               "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-o", tmp, _SRC, "-lm"]
+    else:
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-fopenmp", "-Wall", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, path)
+    return path
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    if not os.environ.get("MOE_ORACLE_LIB") and (not os.path.exists(_LIB_PATH) or
+                                                 os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
         build(force=True)
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
