@@ -104,16 +104,24 @@ __device__ __forceinline__ double lane_f64(double v, int l) {
 template <int G>
 struct Grp;
 
+// max(v, v moved by a DPP control): 0 is the identity of the unsigned max,
+// so lanes a move does not reach (and rows the mask leaves out) keep v, and
+// the move folds into the max instruction itself (one v_max_u32 with DPP).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v) {
+    return max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, true)));
+}
+
 template <>
 struct Grp<16> {
     static constexpr int kPer = kMaxExperts / 16;
     static constexpr int kPerWave = kWave / 16;
     static constexpr int kRounds = kMaxBatch / (16 * kPerWave);   // 16 wavefronts cover 128 tokens
     __device__ static uint32_t max_u32(uint32_t v) {
-        v = max(v, dpp32<kQuadXor1, 0xF>(v, v));
-        v = max(v, dpp32<kQuadXor2, 0xF>(v, v));
-        v = max(v, dpp32<kHalfMirror, 0xF>(v, v));
-        v = max(v, dpp32<kMirror, 0xF>(v, v));
+        v = max_dpp<kQuadXor1, 0xF>(v);
+        v = max_dpp<kQuadXor2, 0xF>(v);
+        v = max_dpp<kHalfMirror, 0xF>(v);
+        v = max_dpp<kMirror, 0xF>(v);
         return v;
     }
     // levels 4..7 of the balanced tree over 128 slots: lane pairs, quads, half rows, rows
@@ -146,8 +154,8 @@ struct Grp<64> {
     static constexpr int kRounds = 1;   // B <= 16 tokens, one per wavefront
     __device__ static uint32_t max_u32(uint32_t v) {
         v = Grp<16>::max_u32(v);
-        v = max(v, dpp32<kRowBcast15, 0xA>(v, v));   // rows 1, 3 take rows 0, 2
-        v = max(v, dpp32<kRowBcast31, 0xC>(v, v));   // rows 2, 3 take row 1
+        v = max_dpp<kRowBcast15, 0xA>(v);   // rows 1, 3 take rows 0, 2
+        v = max_dpp<kRowBcast31, 0xC>(v);   // rows 2, 3 take row 1
         return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
     }
     // levels 2..7 of the balanced tree: as Grp<16>, then row pairs, then the halves
@@ -195,7 +203,7 @@ struct Tok {
 // a group also stops after the first rank at which the running sum of
 // exp(l - l_top) in rank order (fp32, one addition per rank) reaches p_z
 // (the top-p count).  The loop ends when every group of the wavefront is done.
-template <int G>
+template <int G, bool kTopP>
 __device__ __forceinline__ int group_select(Tok<Grp<G>::kPer>& t, bool active, int r0, int count, uint32_t& top_key,
                                             float p_z) {
     constexpr int P = Grp<G>::kPer;
@@ -209,26 +217,24 @@ __device__ __forceinline__ int group_select(Tok<Grp<G>::kPer>& t, bool active, i
         const bool act = live && r < count && m != 0u;
         if (!__any(act)) break;
         const bool mine = act && l == Grp<G>::lowest(__ballot(act && lmax == m));
-        int jsel = P;
+        // the owner's lowest expert holding m: clear it and record its rank
+        bool hit = false;
 #pragma unroll
-        for (int j = P - 1; j >= 0; --j)
-            if (t.key[j] == m) jsel = j;
-#pragma unroll
-        for (int j = 0; j < P; ++j)
-            if (mine && j == jsel) {
-                t.key[j] = 0u;
-                t.slot[j] = r;
-            }
-        if (act) {
-            got = r + 1;
-            if (r == 0) {
-                top_key = m;
-                top = key_logit(m);
-            }
-            if (p_z > 0.0f) {
-                c = c + route_exp(key_logit(m) - top);
-                if (c >= p_z) live = false;
-            }
+        for (int j = 0; j < P; ++j) {
+            const bool take = mine && !hit && t.key[j] == m;
+            hit = hit || take;
+            t.key[j] = take ? 0u : t.key[j];
+            t.slot[j] = take ? r : t.slot[j];
+        }
+        got = act ? r + 1 : got;
+        if (r == 0) {
+            top_key = m;
+            top = key_logit(m);
+        }
+        if constexpr (kTopP) {
+            const float cn = c + route_exp(key_logit(m) - top);
+            c = act ? cn : c;
+            live = live && !(act && cn >= p_z);
         }
     }
     return got;
@@ -490,7 +496,8 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
         }
         uint32_t top_key = 0u;
         const float p_z = (kOea && p < 1.0f) ? p * Z : 0.0f;
-        const int got = group_select<G>(t, real, 0, kOea ? k0 : k, top_key, p_z);
+        const int got = p_z > 0.0f ? group_select<G, true>(t, real, 0, kOea ? k0 : k, top_key, p_z)
+                                   : group_select<G, false>(t, real, 0, kOea ? k0 : k, top_key, p_z);
         got1[r] = got;
         top1[r] = top_key;
         if (i < B) {
@@ -551,7 +558,7 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
             }
             uint32_t top_key = top1[r];
             const int count = pruned ? got1[r] : keep;
-            const int got = group_select<G>(t, real, got1[r], count, top_key, 0.0f);
+            const int got = group_select<G, false>(t, real, got1[r], count, top_key, 0.0f);
             if (i < B) group_write<G>(t, i, k, got, key_logit(top_key), true, 0.0f, idx, w, idx_copy);
         }
     }
@@ -721,7 +728,7 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(const XT* _
 // of 16 lanes land in part[row][4 e + t].
 template <typename XT, int kE>
 __device__ __forceinline__ void gemv_4x4(const XT* __restrict__ x, const float* __restrict__ w_r, int H, int N,
-                                         int e0, int t0, int nt, int g, int tid, float (*part)[kGemvTok]) {
+                                         int e0, int t0, int nt, int g, int tid, float (*part)[4 * kE]) {
     constexpr int kT = 4;
     const int lane = tid & (kWave - 1);
     const int col0 = 8 * lane + 512 * (tid / kWave);
@@ -770,8 +777,12 @@ __device__ __forceinline__ void gemv_4x4(const XT* __restrict__ x, const float* 
 // count routes and dispatches the whole batch (its 16 wavefronts, one token
 // per wavefront at a time), reading the logits with device-scope loads, and
 // clears the count for the next call.  No workgroup waits for another.
-constexpr int kFusedExperts = 2;   // experts per workgroup
 constexpr int kFusedGroups = 4;    // thread groups per workgroup, 4 tokens each
+// Experts per workgroup: 2 while the grid of (N/2) x (B/16) workgroups fits
+// the chip in one round (B <= 64: 256 workgroups; one 1024-thread workgroup
+// per CU at this kernel's register use), 4 for larger batches, which would
+// otherwise take two rounds.
+constexpr int kFusedMaxB2 = 64;
 
 __device__ __forceinline__ void wait_vmem() {   // s_waitcnt vmcnt(0)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -779,7 +790,7 @@ __device__ __forceinline__ void wait_vmem() {   // s_waitcnt vmcnt(0)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename XT, bool kOea, int G>
+template <typename XT, bool kOea, int G, int kFusedExperts>
 __global__ __launch_bounds__(kGemvThreads * kFusedGroups) void router_route_kernel(
         const XT* __restrict__ x, const float* __restrict__ w_r, int B, int H, int N, float* __restrict__ logits,
         int k, int k0, float p, int renorm, int32_t* __restrict__ idx, float* __restrict__ w,
@@ -787,9 +798,10 @@ __global__ __launch_bounds__(kGemvThreads * kFusedGroups) void router_route_kern
         int32_t* __restrict__ cnt, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
         int32_t* __restrict__ active, int pruned, int max_p, const int32_t* __restrict__ n_valid,
         const int32_t* __restrict__ k0_by_batch, int32_t* __restrict__ sync) {
-    __shared__ float part[kFusedGroups][kGemvThreads / 16][kGemvTok];
+    __shared__ float part[kFusedGroups][kGemvThreads / 16][4 * kFusedExperts];
     __shared__ int last_s;
-    static_assert(kFusedGroups * 4 == kGemvTok && kFusedExperts * 4 <= kGemvTok, "gemv_4x4 layout");
+    static_assert(kFusedGroups * 4 == kGemvTok && kFusedExperts * kGemvTok <= kGemvThreads * kFusedGroups,
+                  "gemv_4x4 layout");
     const int g = threadIdx.x / kGemvThreads;
     const int tid = threadIdx.x - g * kGemvThreads;
     const int e0 = blockIdx.x * kFusedExperts;
@@ -915,16 +927,22 @@ hipError_t launch_router_route_dispatch(const void* x, int x_dtype, const float*
                                         const int32_t* k0_by_batch, float* logits, int32_t* idx, float* w,
                                         int32_t* n_base, uint32_t* mask, int32_t* cnt, int32_t* offsets,
                                         int32_t* perm, int32_t* active, int32_t* T, int32_t* sync, hipStream_t s) {
-    const dim3 grid((N + kFusedExperts - 1) / kFusedExperts, (B + kGemvTok - 1) / kGemvTok);
+    const int fe = B <= kFusedMaxB2 ? 2 : 4;
+    const dim3 grid((N + fe - 1) / fe, (B + kGemvTok - 1) / kGemvTok);
     const int threads = kGemvThreads * kFusedGroups;
     const bool oea = mode != MOE_ROUTE_TOPK;
     const int pruned = mode == MOE_ROUTE_PRUNED;
     const int mp = mode == MOE_ROUTE_OEA ? max_p : N;
-#define MOE_FUSED(XT_, G_, OEA_)                                                                                 \
-    router_route_kernel<XT_, OEA_, G_><<<grid, threads, 0, s>>>(                                                 \
+#define MOE_FUSED_E(XT_, G_, OEA_, E_)                                                                          \
+    router_route_kernel<XT_, OEA_, G_, E_><<<grid, threads, 0, s>>>(                                             \
         static_cast<const XT_*>(x), w_r, B, H, N, logits, k, OEA_ ? k0 : k, OEA_ ? p : 1.0f, OEA_ ? 1 : renorm,  \
         idx, w, OEA_ ? n_base : nullptr, OEA_ ? mask : nullptr, T, cnt, offsets, perm, active, OEA_ ? pruned : 0,  \
         OEA_ ? mp : N, n_valid, OEA_ ? k0_by_batch : nullptr, sync)
+#define MOE_FUSED(XT_, G_, OEA_)                                     \
+    do {                                                             \
+        if (fe == 2) MOE_FUSED_E(XT_, G_, OEA_, 2);                  \
+        else MOE_FUSED_E(XT_, G_, OEA_, 4);                          \
+    } while (0)
 #define MOE_FUSED_G(XT_)                                  \
     if (B <= kSmallBatch) {                               \
         if (oea) MOE_FUSED(XT_, 64, true);                \
@@ -940,6 +958,7 @@ hipError_t launch_router_route_dispatch(const void* x, int x_dtype, const float*
     }
 #undef MOE_FUSED_G
 #undef MOE_FUSED
+#undef MOE_FUSED_E
     return hipGetLastError();
 }
 
