@@ -12,5 +12,5 @@ from ._lib import (  # noqa: F401
     budget_create, budget_release, budget_try_reserve, pool_alloc, pool_create, pool_free, residency_create,
     residency_select, residency_stats, residency_step,
 )
-from .layer import ExpertTensors, MoELayer, k0_schedule  # noqa: F401
+from .layer import ExpertTensors, MoELayer, capture_layers, k0_schedule  # noqa: F401
 from .residency import Residency, ema_hot_set, pinned_hi_version  # noqa: F401

@@ -154,6 +154,31 @@ class MoELayer:
         return graph
 
 
+def capture_layers(calls, mode: str = "oea", k0: int = 3, p: float = 1.0, max_p: int | None = None,
+                   n_valid=None, k0_by_batch=None) -> torch.cuda.CUDAGraph:
+    """Capture the forward calls of several layers, in the order given, into
+    one HIP graph; `calls` is a list of (MoELayer, x) pairs.  One replay runs
+    them all (a decode step's MoE layers), so the fixed cost of launching a
+    graph is paid once per step rather than once per layer, and the host
+    spends one replay call on the whole step.  Each layer's results land in
+    its own buffers(B), as with MoELayer.capture."""
+    calls = list(calls)
+    if not calls:
+        raise ValueError("no layers to capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside capture (allocates every layer's buffers)
+        for layer, x in calls:
+            layer.forward(x, mode, k0, p, max_p=max_p, n_valid=n_valid, k0_by_batch=k0_by_batch)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for layer, x in calls:
+            layer.forward(x, mode, k0, p, max_p=max_p, n_valid=n_valid, k0_by_batch=k0_by_batch)
+    return graph
+
+
 def k0_schedule(k: int, B_max: int, steps: list[tuple[int, int]], device="cuda") -> torch.Tensor:
     """Device table for moe_route_dispatch's k0_by_batch: entry b is the k0
     for a batch of b real tokens.

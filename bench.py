@@ -231,6 +231,20 @@ def main():
         torch.cuda.synchronize()
         graph_ms = [evl[i].elapsed_time(ev1[i]) for i in range(args.steps)]
         del graphs
+        # every layer copy in one graph (a decode step's MoE layers): one replay per step
+        n_l = len(layers)
+        g_all = moe.capture_layers([(layers[c], xs[c % len(xs)]) for c in range(n_l)], mode, k0, 1.0)
+        n_rep = max(args.steps // n_l, 4)
+        for i in range(2):
+            g_all.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n_rep):
+            g_all.replay()
+        torch.cuda.synchronize()
+        step_wall = time.perf_counter() - t0
+        del g_all
+        step_bytes = sum(Ts[c % len(Ts)] * W_e + fixed_layer for c in range(n_l))
         Tsteps = [Ts[i % len(Ts)] for i in range(args.steps)]
         layer_bytes = sum(t * W_e + fixed_layer for t in Tsteps)
         ffn_bytes = sum(t * W_e + fixed_ffn for t in Tsteps)
@@ -255,6 +269,8 @@ def main():
             graph_us_p50=float(np.percentile(graph_ms, 50) * 1e3),
             graph_us_p90=float(np.percentile(graph_ms, 90) * 1e3),
             graph_gbps=layer_bytes / graph_wall / 1e9,
+            graph_step_us_per_layer=step_wall / (n_rep * n_l) * 1e6,
+            graph_step_gbps=step_bytes * n_rep / step_wall / 1e9,
         )
 
     if args.only == "mixed":   # profiler runs of the mixed-residency layer alone (Qwen3-30B shape)
@@ -779,9 +795,12 @@ def read_ceiling(gib=4, reps=10, shapes=(4, 8, 16, 32)):
 
 def small_batch_graphs(layers, N, k, H, steps=60):
     """Whole-layer latency (router GEMV + routing + dispatch + expert FFN) at
-    B = 1, 2, 4, 8, eager launches against one captured HIP graph per layer
-    copy (page OEA section 7: graph replay of small decode batches), OEA
-    k0 = 3 and vanilla top-8; medians of per-step HIP events."""
+    B = 1, 2, 4, 8 (page OEA section 7: graph replay of small decode
+    batches), OEA k0 = 3 and vanilla top-8; medians of per-step HIP events:
+    eager launches against one captured HIP graph per layer copy, and the 8
+    layer copies as one decode step, eager against one graph of all 8
+    (per layer).  host_us: the host's time per layer call, eager forward
+    against the 8-layer graph's replay, without synchronisation."""
     import numpy as np
     import torch
 
@@ -821,9 +840,44 @@ def small_batch_graphs(layers, N, k, H, steps=60):
             torch.cuda.synchronize()
             graph_us = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(steps)])) * 1e3
             del graphs
+            # the 8 copies as one decode step: eager, then one graph of all of them
+            n_l = len(layers)
+            reps = max(steps // 4, 8)
+            for i in range(reps):
+                e0[i].record(stream)
+                for c in range(n_l):
+                    layers[c].forward(xs[c], mode, k0, 1.0)
+                e1[i].record(stream)
+            torch.cuda.synchronize()
+            eager_step = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(reps)])) * 1e3
+            g_all = moe.capture_layers(list(zip(layers, xs)), mode, k0, 1.0)
+            for i in range(2):
+                g_all.replay()
+            for i in range(reps):
+                e0[i].record(stream)
+                g_all.replay()
+                e1[i].record(stream)
+            torch.cuda.synchronize()
+            graph_step = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(reps)])) * 1e3
+            t0 = time.perf_counter()
+            for i in range(reps):
+                g_all.replay()
+            host_graph = (time.perf_counter() - t0) / (reps * n_l) * 1e6
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(reps):
+                for c in range(n_l):
+                    layers[c].forward(xs[c], mode, k0, 1.0)
+            host_eager = (time.perf_counter() - t0) / (reps * n_l) * 1e6
+            torch.cuda.synchronize()
+            del g_all
             T = int(layers[0].forward(xs[0], mode, k0, 1.0).disp["T"].item())
             out.append({"B": B, "routing": f"oea_k0_{k0}" if mode == "oea" else f"top{k}", "T_first_copy": T,
-                        "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2)})
+                        "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2),
+                        "step_of_%d_layers" % n_l: {"eager_us_per_layer": round(eager_step / n_l, 2),
+                                                    "graph_us_per_layer": round(graph_step / n_l, 2),
+                                                    "host_us_per_layer_eager": round(host_eager, 1),
+                                                    "host_us_per_layer_graph": round(host_graph, 1)}})
     return out
 
 

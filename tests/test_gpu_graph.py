@@ -80,3 +80,26 @@ def test_graph_follows_the_batch_size_k0_table():
         torch.cuda.synchronize()
         assert int(alone.disp["T"].item()) == T_graph, rep
         assert _same_rows(alone.y, y_graph[:n_real], n_real * k), rep
+
+
+def test_one_graph_for_several_layers():
+    # a decode step's layers in one graph: every replay, with eager work and
+    # synchronisation between replays, reproduces each layer's eager result
+    N, k, H, I, B = 32, 8, 512, 256, 4
+    seeds = (31, 32, 33)
+    layers = [build_layer(N, k, H, I, s, fmt="bf16")[0] for s in seeds]
+    refs = [build_layer(N, k, H, I, s, fmt="bf16")[0] for s in seeds]
+    xs = [_x(40 + j, B, H).clone() for j in range(len(layers))]
+    graph = moe.capture_layers(list(zip(layers, xs)), "oea", 3, 1.0)
+    for rep in range(3):
+        for j, x in enumerate(xs):
+            x.copy_(_x(100 * rep + j, B, H))
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, (lay, ref) in enumerate(zip(layers, refs)):
+            y_graph = lay.buffers(B).y.clone()
+            T_graph = int(lay.buffers(B).disp["T"].item())
+            eager = ref.forward(xs[j], "oea", 3, 1.0)
+            torch.cuda.synchronize()
+            assert torch.equal(y_graph, eager.y), (rep, j)
+            assert T_graph == int(eager.disp["T"].item()), (rep, j)
