@@ -103,6 +103,8 @@ _SIGNATURES = [
     ("moe_residency_get_stats", [_P, ctypes.POINTER(ResidencyStats)], _I),
     ("moe_residency_destroy", [_P], _I),
     ("moe_stream_read", [_P, _S, _I, _P, _P], _I),
+    ("moe_expert_ffn_phase_events", [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _S, _P, _P],
+     _I),
     ("moe_status_str", [_I], ctypes.c_char_p),
     ("moe_last_error", [], ctypes.c_char_p),
 ]
@@ -352,6 +354,26 @@ def stream_read(buf, out, waves_per_cu: int = 8, stream=None):
     _check("moe_stream_read", lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(waves_per_cu),
                                                     _ptr(out), _stream(stream)))
     return out
+
+
+def expert_ffn_phase_events(table, N: int, H: int, I: int, x, idx, w, disp, y, ws, events, stream=None):
+    """moe_expert_ffn_phase_events: the expert FFN call with four torch.cuda
+    Events (timing enabled) recorded before phase A, after phase A, after
+    phase B and after the combine, on the stream the kernels run on."""
+    if len(events) != 4:
+        raise ValueError("four events")
+    st = stream if stream is not None else torch.cuda.current_stream()
+    handles = (ctypes.c_void_p * 4)()
+    for i, ev in enumerate(events):
+        if ev.cuda_event == 0:   # torch creates the HIP event on its first record
+            ev.record(st)
+        handles[i] = ev.cuda_event
+    B, k = idx.shape
+    _check("moe_expert_ffn_phase_events", lib().moe_expert_ffn_phase_events(
+        _ptr(table), N, H, I, _ptr(x), _x_dtype(x), _ptr(idx), _ptr(w), _ptr(disp["offsets"]),
+        _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]), B, k, _ptr(y), _ptr(ws),
+        ws.numel() * ws.element_size(), ctypes.cast(handles, ctypes.c_void_p), _stream(stream)))
+    return y
 
 
 def status_str(status: int) -> str:

@@ -271,6 +271,22 @@ MOE_API int moe_hotness_ema(float* S, const int32_t* cnt, int N, float alpha, vo
     return hip_status(moe::launch_hotness_ema(S, cnt, N, alpha, as_stream(stream)), "moe_hotness_ema");
 }
 
+MOE_API int moe_expert_ffn_phase_events(const moe_expert_handle* table, int N, int H, int I, const void* x,
+                                        int x_dtype, const int32_t* idx, const float* w, const int32_t* offsets,
+                                        const int32_t* perm, const int32_t* active, const int32_t* T, int B, int k,
+                                        float* y, void* ws, size_t ws_bytes, void* const* events, void* stream) {
+    if (!events) return fail(MOE_EINVAL, "null events array");
+    int st = check_ffn(table, N, H, I, x, x_dtype, idx, w, offsets, perm, active, T, B, k, y);
+    if (st) return st;
+    if (!ws) return fail(MOE_EINVAL, "null workspace");
+    if (ws_bytes < moe::ffn_workspace_bytes(B, k, H, I)) return fail(MOE_EINVAL, "workspace too small");
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+    hipEvent_t ev[4];
+    for (int i = 0; i < 4; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
+    const moe::FfnArgs a = ffn_args(table, N, H, I, x, x_dtype, idx, w, offsets, perm, active, T, B, k, y);
+    return hip_status(moe::launch_expert_ffn(a, ws, as_stream(stream), ev), "moe_expert_ffn_phase_events");
+}
+
 MOE_API int moe_stream_read(const void* buf, size_t bytes, int waves_per_cu, uint32_t* out, void* stream) {
     if (!buf || !out) return fail(MOE_EINVAL, "null pointer");
     if (bytes < 16 || bytes % 16) return fail(MOE_EINVAL, "bytes must be a positive multiple of 16");

@@ -1078,36 +1078,36 @@ size_t ffn_workspace_bytes(int B, int k, int H, int I) {
     return align256(pairs * I * sizeof(float)) + align256(pairs * H * sizeof(float));
 }
 
-hipError_t launch_expert_ffn(const FfnArgs& in, void* ws, hipStream_t s) {
+hipError_t launch_expert_ffn(const FfnArgs& in, void* ws, hipStream_t s, hipEvent_t const* ev) {
+    auto mark = [&](int i) { return ev != nullptr && ev[i] != nullptr ? hipEventRecord(ev[i], s) : hipSuccess; };
     FfnArgs a = in;
     const size_t pairs = static_cast<size_t>(a.B) * a.k;
     char* p = static_cast<char*>(ws);
     a.hbuf = reinterpret_cast<float*>(p);
     a.dbuf = reinterpret_cast<float*>(p + align256(pairs * a.I * sizeof(float)));
+    hipError_t e = mark(0);
+    if (e != hipSuccess) return e;
     if (pairs <= static_cast<size_t>(kSmallPairs)) {
         // one workgroup per (slot, item) for every slot that T can reach
         const int slots = std::min(static_cast<int>(pairs), a.N);
         ffn_small_kernel<0><<<slots * ((a.I / 16 + small_rb<0>() - 1) / small_rb<0>()), kSmallThreads, 0, s>>>(a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
         ffn_small_kernel<1><<<slots * ((a.H / 16 + small_rb<1>() - 1) / small_rb<1>()), kSmallThreads, 0, s>>>(a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
     } else {
         const int cus = device_cus();
         // grids are whole multiples of kXcds workgroups (the virtual numbering needs it)
         const int g0 = (waves_per_simd<0>() * cus) / kXcds * kXcds;
         const int g1 = (waves_per_simd<1>() * cus) / kXcds * kXcds;
         ffn_kernel<0><<<g0 > 0 ? g0 : kXcds, kThreads, 0, s>>>(a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
         ffn_kernel<1><<<g1 > 0 ? g1 : kXcds, kThreads, 0, s>>>(a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
     }
     dim3 cg((a.H / 4 + kWave - 1) / kWave, a.B);
     combine_kernel<<<cg, kWave, 0, s>>>(a);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return mark(3);
 }
 
 }  // namespace moe

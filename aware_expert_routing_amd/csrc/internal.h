@@ -91,7 +91,9 @@ struct FfnArgs {
 
 size_t ffn_workspace_bytes(int B, int k, int H, int I);
 bool ffn_cost_fits(int B, int k, int N, int H, int I);   // the device partition's 32-bit cost sums
-hipError_t launch_expert_ffn(const FfnArgs& a, void* ws, hipStream_t s);
+// ev: null, or four events recorded on s before phase A, after phase A, after
+// phase B and after the combine (null entries are skipped).
+hipError_t launch_expert_ffn(const FfnArgs& a, void* ws, hipStream_t s, hipEvent_t const* ev = nullptr);
 hipError_t ffn_noalloc_workspace(void** out);   // this device's static workspace
 hipError_t launch_stream_read(const void* buf, size_t bytes, int waves_per_cu, uint32_t* out, int cus,
                               hipStream_t s);

@@ -84,9 +84,10 @@ def sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per expert-FFN call from the committed counter summary, or
-    None when it is missing or was taken on different kernel sources."""
+def measured_traffic(prefix=""):
+    """HBM bytes per expert-FFN call (prefix "") or per phase-A launch (prefix
+    "phase_a_") from the committed counter summary, or None when it is missing
+    or was taken on different kernel sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -97,7 +98,7 @@ def measured_traffic():
     if kv.get("sources_sha256") != sources_sha256():
         return None
     try:
-        return int(float(kv["fetch_bytes_per_call"]) + float(kv["write_bytes_per_call"]))
+        return int(float(kv[prefix + "fetch_bytes_per_call"]) + float(kv[prefix + "write_bytes_per_call"]))
     except (KeyError, ValueError):
         return None
 
@@ -210,6 +211,19 @@ def main():
         torch.cuda.synchronize()
         ffn_ms = [ev0[i].elapsed_time(ev1[i]) for i in range(args.steps)]
         layer_ms = [evl[i].elapsed_time(ev1[i]) for i in range(args.steps)]
+        # the same steps with the FFN call's three launches timed apart (events
+        # recorded by the library between them, on the stream they run on)
+        evp = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            lay = layers[i % len(layers)]
+            x = xs[i % len(xs)]
+            buf = lay.buffers(B)
+            moe.router_route_dispatch(x, lay.w_r, k, mode, k0, 1.0, True, buf.route, buf.disp, buf.logits,
+                                      buf.extra["sync"])
+            moe.expert_ffn_phase_events(lay.table, N, H, I, x, buf.route["idx"], buf.route["w"], buf.disp, buf.y,
+                                        buf.ws, evp[i])
+        torch.cuda.synchronize()
+        phase_ms = [[evp[i][j].elapsed_time(evp[i][j + 1]) for i in range(args.steps)] for j in range(3)]
         # the same steps replayed from HIP graphs (one per layer copy and batch)
         graphs = {}
         for i in range(args.steps):
@@ -271,6 +285,9 @@ def main():
             graph_gbps=layer_bytes / graph_wall / 1e9,
             graph_step_us_per_layer=step_wall / (n_rep * n_l) * 1e6,
             graph_step_gbps=step_bytes * n_rep / step_wall / 1e9,
+            phase_us=[float(np.mean(m) * 1e3) for m in phase_ms],
+            phase_us_p50=[float(np.median(m) * 1e3) for m in phase_ms],
+            phase_a_bytes_per_launch=float(np.mean([t * 2 * H * I * 2 for t in Tsteps])) + B * H * 2,
         )
 
     if args.only == "mixed":   # profiler runs of the mixed-residency layer alone (Qwen3-30B shape)
@@ -356,6 +373,20 @@ def main():
             "frac_of_read_ceiling": None if ceiling is None else round(head["ffn_gbps"] / ceiling["gbps"], 4),
             "ffn_us_p10_p50_p90": [round(head["ffn_us_p10"], 2), round(head["ffn_us_p50"], 2),
                                    round(head["ffn_us_p90"], 2)],
+        },
+        "roofline_dominant_kernel": {
+            "bound": "hbm",
+            "kernel": "ffn_kernel<0> (phase A: gate/up + SwiGLU; the heaviest of the expert FFN's three launches)",
+            "achieved": round(head["phase_a_bytes_per_launch"] / head["phase_us"][0] / 1e3, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(head["phase_a_bytes_per_launch"] / head["phase_us"][0] / 1e3 / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic("phase_a_") if (args.config == "qwen30b" and B == 16 and args.k0 == 3)
+                       else None,
+            "bytes_per_launch": round(head["phase_a_bytes_per_launch"]),
+            "us_mean": round(head["phase_us"][0], 2),
+            "us_p50": round(head["phase_us_p50"][0], 2),
+            "phase_us_mean_a_b_combine": [round(v, 2) for v in head["phase_us"]],
         },
         "layer_us_p10_p50_p90": [round(head["layer_us_p10"], 2), round(head["layer_us_p50"], 2),
                                  round(head["layer_us_p90"], 2)],

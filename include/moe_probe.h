@@ -1,6 +1,7 @@
 /*
- * moe_probe.h -- measurement reference kernel of libmoe (not part of the MoE
- * layer's path).  Conventions as in moe.h: device pointers, the call only
+ * moe_probe.h -- measurement entry points of libmoe (not part of the MoE
+ * layer's path): a read-stream reference kernel and a phase-timed copy of the
+ * expert FFN call.  Conventions as in moe.h: device pointers, the call only
  * enqueues on `stream`, never allocates or synchronises, and validates its
  * arguments on the host first.
  */
@@ -9,6 +10,8 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+#include "moe.h"
 
 #ifdef __cplusplus
 extern "C" {
@@ -29,6 +32,22 @@ extern "C" {
  * Errors: MOE_EINVAL for null or misaligned pointers or a bad size or shape.
  */
 int moe_stream_read(const void *buf, size_t bytes, int waves_per_cu, uint32_t *out, void *stream);
+
+/*
+ * The expert FFN with its three launches timed apart: moe_expert_ffn (same
+ * arguments, validation, kernels and results) with four caller-created HIP
+ * events (hipEvent_t, passed as void*) recorded on `stream` before phase A
+ * (gate/up + SwiGLU), after phase A, after phase B (down projection and
+ * routing weight) and after the combine.  Elapsed times between them are the
+ * phases' durations on the stream the kernels run on; the heaviest phase is
+ * the one priced against the HBM roofline [OEA section 4, Eq. 2: each active
+ * expert costs one weight fetch].  A null entry of `events` is skipped.
+ * Errors: as moe_expert_ffn; MOE_EINVAL for a null `events` array.
+ */
+int moe_expert_ffn_phase_events(const moe_expert_handle *table, int N, int H, int I, const void *x, int x_dtype,
+                                const int32_t *idx, const float *w, const int32_t *offsets, const int32_t *perm,
+                                const int32_t *active, const int32_t *T, int B, int k, float *y, void *ws,
+                                size_t ws_bytes, void *const *events, void *stream);
 
 #ifdef __cplusplus
 }

@@ -341,3 +341,17 @@ def test_binding_refuses_short_or_mistyped_device_tables():
             moe.router_route_dispatch(x, w_r, 4, "oea", 2, **kw)
     with pytest.raises(ValueError):
         moe.router_route_dispatch(x, w_r, 4, "oea", 2, sync=torch.zeros(1, dtype=torch.int64))
+
+
+def test_expert_ffn_phase_events_validates_like_the_ffn_call():
+    # the phase-timed copy runs the same validation before anything is recorded or launched
+    lib = moe.lib()
+    need = moe.ffn_workspace_bytes(16, 8, 2048, 768)
+    evs = (ctypes.c_void_p * 4)()
+    ev_ptr = ctypes.cast(evs, ctypes.c_void_p)
+    args = lambda H, I, ws, events: (FAKE, 128, H, I, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 8, FAKE,
+                                     FAKE, ws, events, None)
+    assert lib.moe_expert_ffn_phase_events(*args(2048, 768, need, None)) == -1        # no events array
+    assert lib.moe_expert_ffn_phase_events(*args(2046, 768, need, ev_ptr)) == -1      # H % 32
+    assert lib.moe_expert_ffn_phase_events(*args(2048, 768, need - 1, ev_ptr)) == -1  # workspace
+    assert lib.moe_expert_ffn_phase_events(*args(32768, 768, 1 << 40, ev_ptr)) == -2  # beyond limits

@@ -203,6 +203,26 @@ def test_ffn_repeat_runs_are_bit_identical():
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("B", [1, 16])
+def test_phase_timed_call_matches_the_ffn_call(B):
+    # moe_expert_ffn_phase_events runs the same kernels: y bit for bit, and
+    # the four events it records are in stream order with non-negative gaps
+    # (B = 1 takes the column-split kernels, B = 16 the per-wave ones)
+    N, k, H, I = 32, 8, 512, 256
+    layer, _ = build_layer(N, k, H, I, 8, fmt="bf16", with_router=False)
+    _, xd = _x(8, B, H, "bf16")
+    logits = torch.from_numpy(synth.logits(8, B, N, 2.0)).to(DEV)
+    buf = layer.forward(xd, "oea", 3, logits=logits)
+    y_ref = buf.y.clone()
+    y = torch.full_like(y_ref, float("nan"))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    moe.expert_ffn_phase_events(layer.table, N, H, I, xd, buf.route["idx"], buf.route["w"], buf.disp, y, buf.ws, ev)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    gaps = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+    assert all(g >= 0.0 for g in gaps), gaps
+
+
 # ---------------------------------------------------------------------------
 # Full-size layers, whole path from x (router GEMV on the GPU), in the launch
 # configuration the benchmark times.
