@@ -836,6 +836,158 @@ __global__ __launch_bounds__(kGemvThreads * kFusedGroups) void router_route_kern
     if (threadIdx.x == 0) __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// Batches of more than 16 tokens with vanilla top-k or simplified OEA (no
+// rank limit, not pruned), routed by token groups: workgroup g routes tokens
+// 16 g .. 16 g + 15, one token per wavefront as for small batches, so a large
+// batch's selections run on B/16 CUs side by side instead of on one.
+//   Vanilla top-k: route_group_kernel<false> writes idx and w; the dispatch
+//   (dispatch_kernel) follows.
+//   OEA: route_group_kernel<true> runs Phase 1 and leaves each token's
+//   baseline in its idx row (slots 0 .. n_i - 1, then -1); in the next
+//   launch every workgroup rebuilds S_base from those rows (integer OR in
+//   LDS) and runs Phase 2 for its tokens, and the workgroup that completes
+//   the count dispatches the batch.  A row that another workgroup has
+//   already extended in Phase 2 only adds members of S_base, so the union is
+//   the same whichever it reads.
+// Every selection depends only on the token's own logits and on S_base, so
+// idx, n_base, the mask and T equal the one-workgroup path's bit for bit.
+// ---------------------------------------------------------------------------
+constexpr int kGroupTok = 16;
+
+// Token i's logits (two experts per lane) and fresh selection state.
+template <bool kCoherent>
+__device__ __forceinline__ void group_token_load(const float* __restrict__ logits, int i, int N, bool real,
+                                                 Tok<2>& t) {
+    const int e_first = 2 * (threadIdx.x & (kWave - 1));
+    float L[2];
+    if ((N & 1) == 0) {
+        if (real && e_first < N) load_logit2<kCoherent>(logits + static_cast<size_t>(i) * N + e_first, L[0], L[1]);
+        else L[0] = L[1] = kNegInf;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            L[j] = (real && e_first + j < N) ? load_logit<kCoherent>(logits + static_cast<size_t>(i) * N + e_first + j)
+                                             : kNegInf;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        t.l[j] = L[j];
+        t.key[j] = (real && e_first + j < N) ? order_key(L[j]) : 0u;
+        t.slot[j] = -1;
+    }
+}
+
+// Launch: ceil(B / 16) workgroups of 1024 threads.  kOea: Phase 1 and the
+// baseline rows (and n_base); else vanilla top-k written in full.  Workgroup
+// 0 also clears *T_out, the next launch's completion count.
+template <bool kOea>
+__global__ __launch_bounds__(1024) void route_group_kernel(const float* __restrict__ logits, int B, int N, int k,
+                                                           int k0, float p, int renorm, int32_t* __restrict__ idx,
+                                                           float* __restrict__ w, int32_t* __restrict__ n_base,
+                                                           int32_t* __restrict__ T_out,
+                                                           const int32_t* __restrict__ n_valid,
+                                                           const int32_t* __restrict__ k0_by_batch) {
+    const int B_real = n_valid != nullptr ? min(max(*n_valid, 0), B) : B;
+    if (kOea && k0_by_batch != nullptr) k0 = min(max(k0_by_batch[B_real], 1), k);
+    if (kOea && blockIdx.x == 0 && threadIdx.x == 0) *T_out = 0;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int i = kGroupTok * blockIdx.x + threadIdx.x / kWave;
+    if (i >= B) return;   // whole wavefronts; the kernel has no barrier
+    const bool real = i < B_real;
+    Tok<2> t;
+    group_token_load<false>(logits, i, N, real, t);
+    const bool need_z = kOea ? (p < 1.0f) : (renorm == 0);
+    float Z = 0.0f;
+    if (need_z) {   // normaliser over all experts, relative to the top logit
+        const float m = key_logit(Grp<64>::max_u32(lane_max<2>(t.key)));
+        float sj[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sj[j] = t.key[j] != 0u ? route_exp(t.l[j] - m) : 0.0f;
+        Z = Grp<64>::tree_sum(lane_tree_sum<2>(sj));
+    }
+    uint32_t top_key = 0u;
+    const float p_z = (kOea && p < 1.0f) ? p * Z : 0.0f;
+    const int got = p_z > 0.0f ? group_select<64, true>(t, real, 0, kOea ? k0 : k, top_key, p_z)
+                               : group_select<64, false>(t, real, 0, kOea ? k0 : k, top_key, p_z);
+    if (!kOea) {
+        group_write<64>(t, i, k, got, key_logit(top_key), renorm != 0, Z, idx, w, nullptr);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (t.slot[j] >= 0) idx[i * k + t.slot[j]] = 2 * lane + j;
+        if (lane >= got && lane < k) idx[i * k + lane] = -1;
+        if (lane == 0 && n_base != nullptr) n_base[i] = got;
+    }
+}
+
+// OEA Phase 2 of token group blockIdx.x and, in the workgroup that completes
+// the count in *T_out, the dispatch of the whole batch (which then writes T
+// there).  Launch: ceil(B / 16) workgroups of 1024 threads.
+__global__ __launch_bounds__(1024) void route_group_p2_kernel(const float* __restrict__ logits, int B, int N, int k,
+                                                              int32_t* __restrict__ idx, float* __restrict__ w,
+                                                              uint32_t* __restrict__ mask_out,
+                                                              const int32_t* __restrict__ n_valid,
+                                                              int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ perm, int32_t* __restrict__ active,
+                                                              int32_t* __restrict__ T_out) {
+    __shared__ uint32_t sbase[kMaxExperts / 32];
+    __shared__ int last_s;
+    __shared__ int32_t idx_l[kMaxBatch * kMaxTopK];
+    const int B_real = n_valid != nullptr ? min(max(*n_valid, 0), B) : B;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    if (tid < kMaxExperts / 32) sbase[tid] = 0u;
+    __syncthreads();
+    for (int q = tid; q < B * k; q += blockDim.x) {   // the union of every token's baseline
+        const int e = idx[q];
+        if (e >= 0 && e < N) atomicOr(&sbase[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+    int T = 0;
+#pragma unroll
+    for (int wd = 0; wd < kMaxExperts / 32; ++wd) T += __popc(sbase[wd]);
+    const int keep = T < k ? T : k;
+    const int i = kGroupTok * blockIdx.x + tid / kWave;
+    if (i < B) {   // whole wavefronts
+        const bool real = i < B_real;
+        Tok<2> t;
+        group_token_load<false>(logits, i, N, real, t);
+        // the rank-0 key (the token's largest) and the baseline slots from Phase 1
+        uint32_t top_key = Grp<64>::max_u32(lane_max<2>(t.key));
+        const int e_first = 2 * lane;
+        const int32_t my = lane < k ? idx[i * k + lane] : -1;
+        const int got1 = real ? __popcll(__ballot(lane < k && my >= 0)) : 0;   // baselines fill slots 0 .. n_i - 1
+        for (int r = 0; r < got1; ++r) {
+            const int e = __shfl(my, r, kWave);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (e == e_first + j) {
+                    t.slot[j] = r;
+                    t.key[j] = 0u;
+                }
+        }
+        const uint32_t sw = sbase[e_first >> 5] >> (e_first & 31);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (!(t.key[j] != 0u && ((sw >> j) & 1u))) t.key[j] = 0u;
+        const int got = group_select<64, false>(t, real, got1, keep, top_key, 0.0f);
+        group_write<64>(t, i, k, got, key_logit(top_key), true, 0.0f, idx, w, nullptr);
+    }
+    // Hand-off: this workgroup's idx and w stores complete before the count
+    // (an agent-scope release and, in the completing workgroup, acquire).
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0)
+        last_s = __hip_atomic_fetch_add(T_out, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                 static_cast<int>(gridDim.x) - 1;
+    __syncthreads();
+    if (!last_s) return;
+    if (mask_out != nullptr && tid < (N + 31) / 32) mask_out[tid] = sbase[tid];
+    for (int q = tid; q < B * k; q += blockDim.x) idx_l[q] = idx[q];
+    __syncthreads();
+    dispatch_block(idx_l, B, N, k, cnt, offsets, perm, active, T_out);
+}
+
 __global__ void hotness_kernel(float* S, const int32_t* cnt, int N, float alpha) {
     int e = blockIdx.x * blockDim.x + threadIdx.x;
     if (e < N) S[e] = alpha * S[e] + (1.0f - alpha) * static_cast<float>(cnt[e]);
@@ -900,11 +1052,49 @@ hipError_t launch_route(const float* logits, int B, int N, int k, int k0, float 
     return hipGetLastError();
 }
 
+namespace {
+
+// Batches above kGroupMinBatch with vanilla top-k or simplified OEA take the
+// token-group kernels (logits already in memory).  Below it one workgroup
+// selects faster than a second launch costs: measured at N = 128, k = 8 the
+// split is 1-2 us slower at 32 tokens, even at 64 and 7-10 us faster at 128.
+constexpr int kGroupMinBatch = 48;
+bool route_by_groups(int B, int N, int mode, int max_p) {
+    return B > kGroupMinBatch && (mode == MOE_ROUTE_TOPK || (mode == MOE_ROUTE_OEA && max_p >= N));
+}
+
+hipError_t launch_route_groups(const float* logits, int B, int N, int k, int mode, int k0, float p, int renorm,
+                               const int32_t* n_valid, const int32_t* k0_by_batch, int32_t* idx, float* w,
+                               int32_t* n_base, uint32_t* mask, int32_t* cnt, int32_t* offsets, int32_t* perm,
+                               int32_t* active, int32_t* T, hipStream_t s) {
+    const int groups = (B + kGroupTok - 1) / kGroupTok;
+    if (mode == MOE_ROUTE_TOPK) {
+        route_group_kernel<false><<<groups, kGroupTok * kWave, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w,
+                                                                        nullptr, nullptr, n_valid, nullptr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        dispatch_kernel<<<1, 512, 0, s>>>(idx, B, N, k, cnt, offsets, perm, active, T);
+        return hipGetLastError();
+    }
+    route_group_kernel<true><<<groups, kGroupTok * kWave, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, T,
+                                                                   n_valid, k0_by_batch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    route_group_p2_kernel<<<groups, kGroupTok * kWave, 0, s>>>(logits, B, N, k, idx, w, mask, n_valid, cnt, offsets,
+                                                               perm, active, T);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int mode, int k0, float p, int max_p,
                                  int renorm, const int32_t* n_valid, const int32_t* k0_by_batch, int32_t* idx,
                                  float* w, int32_t* n_base,
                                  uint32_t* mask, int32_t* cnt, int32_t* offsets, int32_t* perm, int32_t* active,
                                  int32_t* T, hipStream_t s) {
+    if (route_by_groups(B, N, mode, max_p))
+        return launch_route_groups(logits, B, N, k, mode, k0, p, renorm, n_valid, k0_by_batch, idx, w, n_base, mask,
+                                   cnt, offsets, perm, active, T, s);
     const bool oea = mode != MOE_ROUTE_TOPK;
 #define MOE_ROUTE(G_, OEA_)                                                                                      \
     route_kernel<OEA_, true, G_><<<1, route_threads(B), 0, s>>>(                                                 \
@@ -927,6 +1117,13 @@ hipError_t launch_router_route_dispatch(const void* x, int x_dtype, const float*
                                         const int32_t* k0_by_batch, float* logits, int32_t* idx, float* w,
                                         int32_t* n_base, uint32_t* mask, int32_t* cnt, int32_t* offsets,
                                         int32_t* perm, int32_t* active, int32_t* T, int32_t* sync, hipStream_t s) {
+    if (route_by_groups(B, N, mode, mode == MOE_ROUTE_OEA ? max_p : N)) {
+        // large batches: the logits in their own launch, then the token-group kernels
+        hipError_t e = launch_router_logits(x, x_dtype, w_r, B, H, N, logits, s);
+        if (e != hipSuccess) return e;
+        return launch_route_groups(logits, B, N, k, mode, k0, p, renorm, n_valid, k0_by_batch, idx, w, n_base, mask,
+                                   cnt, offsets, perm, active, T, s);
+    }
     const int fe = B <= kFusedMaxB2 ? 2 : 4;
     const dim3 grid((N + fe - 1) / fe, (B + kGemvTok - 1) / kGemvTok);
     const int threads = kGemvThreads * kFusedGroups;

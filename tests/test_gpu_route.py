@@ -151,6 +151,13 @@ def test_fused_route_dispatch_parity(B, N, k, mode, k0, p, kind, scale, zipf):
     (16, 128, 8, "topk", 0, 1.0, None, 7, 1.0, 1.1),
     (128, 128, 8, "pruned", 3, 0.8, None, 100, 4.0, 1.1),
     (8, 16, 4, "oea", 2, 1.0, 3, 0, 1.0, 0.0),            # every token padding
+    # batches above 48 tokens route by token groups (one workgroup per 16
+    # tokens, OEA Phase 2 in a second launch): padding, ragged last groups
+    (72, 128, 8, "oea", 3, 1.0, None, 40, 1.0, 1.1),
+    (100, 128, 8, "topk", 0, 1.0, None, 77, 2.0, 1.1),
+    (49, 128, 8, "oea", 3, 0.8, None, None, 4.0, 0.0),
+    (81, 64, 8, "oea", 2, 1.0, None, 16, 1.0, 1.1),       # whole padding groups
+    (128, 128, 8, "oea", 3, 1.0, None, None, 1.0, 1.1),
 ])
 def test_route_variants_parity(B, N, k, mode, k0, p, max_p, nv, scale, zipf):
     # page OEA section 5 (maxP, k_max, pruned) and section 7 (padding tokens)
@@ -287,11 +294,16 @@ def test_handle_publish_writes_the_record():
     (7, 23, 520, 4, "oea", 2, 0.9, 5, "f32"),
     (19, 33, 1024, 8, "topk", 0, 1.0, None, "bf16"),       # two token groups, the second ragged
     (40, 33, 1024, 8, "oea", 3, 1.0, 37, "bf16"),
+    # above 48 tokens vanilla top-k and simplified OEA route by token groups
+    # after the router launch
+    (97, 128, 2048, 8, "oea", 3, 0.9, 90, "bf16"),
+    (65, 33, 1024, 8, "topk", 0, 1.0, None, "bf16"),
 ])
 def test_fused_router_route_dispatch(B, N, H, k, mode, k0, p, nv, dtype):
-    # one launch: router GEMV slices, then the last workgroup routes and
-    # dispatches; same logits as moe_router_logits bit for bit, routing as the
-    # oracle's on those logits; the sync word is left at zero for the next call
+    # up to 48 tokens (and for pruned or max-rank OEA at any size) one launch:
+    # router GEMV slices, then the last workgroup routes and dispatches; same
+    # logits as moe_router_logits bit for bit, routing as the oracle's on
+    # those logits; the sync word is left at zero for the next call
     x = synth.activations(40 + B, B, H)
     wr = torch.from_numpy(synth.router_weight(40, N, H)).to(DEV)
     xd = bf16_dev(synth.to_bf16_bits(x)) if dtype == "bf16" else torch.from_numpy(x).to(DEV)
