@@ -208,6 +208,37 @@ __device__ __forceinline__ int group_select(Tok<Grp<G>::kPer>& t, bool active, i
                                             float p_z) {
     constexpr int P = Grp<G>::kPer;
     const int l = threadIdx.x & (G - 1);
+    if constexpr (G == 64) {
+        // One token per wavefront: every condition is uniform, so the loop
+        // runs on scalar registers and only the owner lane's update is a
+        // per-lane select.
+        if (!__builtin_amdgcn_readfirstlane(static_cast<int>(active))) return r0;
+        int got = r0;
+        float c = 0.0f, top = 0.0f;
+        const int end = min(count, kMaxTopK);
+        for (int r = r0; r < end; ++r) {
+            const uint32_t lmax = max(t.key[0], t.key[1]);
+            const uint32_t m = Grp<64>::max_u32(lmax);
+            if (m == 0u) break;
+            const int owner = __ffsll(static_cast<unsigned long long>(__ballot(lmax == m))) - 1;
+            const bool mine = l == owner;
+            const bool first = t.key[0] == m;
+            t.key[0] = (mine && first) ? 0u : t.key[0];
+            t.slot[0] = (mine && first) ? r : t.slot[0];
+            t.key[1] = (mine && !first) ? 0u : t.key[1];
+            t.slot[1] = (mine && !first) ? r : t.slot[1];
+            got = r + 1;
+            if (r == 0) {
+                top_key = m;
+                top = key_logit(m);
+            }
+            if constexpr (kTopP) {
+                c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c + route_exp(key_logit(m) - top))));
+                if (c >= p_z) break;
+            }
+        }
+        return got;
+    }
     int got = r0;
     bool live = active;
     float c = 0.0f, top = 0.0f;
@@ -315,29 +346,44 @@ __device__ __forceinline__ void group_kth(const uint32_t (&key_in)[Grp<G>::kPer]
 // expert's bucket is the number of lower-numbered tokens routed to the same
 // expert, read off a per-expert token bitmask, so the result needs no
 // ordering of atomics.  `idx` may live in LDS or in global memory.
+// The dispatch's LDS: per-expert counts and token bitmasks, then offsets.
+struct DispLds {
+    int cnt[kMaxExperts];
+    int off[kMaxExperts + 1];
+    unsigned long long tokmask[kMaxExperts][kMaxBatch / 64];
+};
+__device__ __forceinline__ void disp_clear(DispLds& d) {
+    for (int e = threadIdx.x; e < kMaxExperts; e += blockDim.x) {
+        d.cnt[e] = 0;
+        d.tokmask[e][0] = 0ull;
+        d.tokmask[e][1] = 0ull;
+    }
+}
+// Count the routed pair (token t, expert e) (e valid).
+__device__ __forceinline__ void disp_add(DispLds& d, int t, int e) {
+    atomicAdd(&d.cnt[e], 1);
+    atomicOr(&d.tokmask[e][t >> 6], 1ull << (t & 63));
+}
+
+// kCounted: the caller cleared d and counted every pair with disp_add (and
+// synchronised the workgroup after); otherwise this function does both.
+template <bool kCounted = false>
 __device__ __forceinline__ void dispatch_block(const int32_t* idx, int B, int N, int k, int32_t* cnt,
                                                int32_t* offsets, int32_t* perm, int32_t* active,
-                                               int32_t* T_out) {
-    __shared__ int cnt_s[kMaxExperts];
-    __shared__ int off_s[kMaxExperts + 1];
-    __shared__ unsigned long long tokmask[kMaxExperts][kMaxBatch / 64];
+                                               int32_t* T_out, DispLds& d) {
+    int* const cnt_s = d.cnt;
+    int* const off_s = d.off;
     const int tid = threadIdx.x;
     const int pairs = B * k;
-    for (int e = tid; e < kMaxExperts; e += blockDim.x) {
-        cnt_s[e] = 0;
-        tokmask[e][0] = 0ull;
-        tokmask[e][1] = 0ull;
-    }
-    __syncthreads();
-    for (int q = tid; q < pairs; q += blockDim.x) {
-        const int e = idx[q];
-        if (e >= 0 && e < N) {
-            const int t = q / k;
-            atomicAdd(&cnt_s[e], 1);
-            atomicOr(&tokmask[e][t >> 6], 1ull << (t & 63));
+    if constexpr (!kCounted) {
+        disp_clear(d);
+        __syncthreads();
+        for (int q = tid; q < pairs; q += blockDim.x) {
+            const int e = idx[q];
+            if (e >= 0 && e < N) disp_add(d, q / k, e);
         }
+        __syncthreads();
     }
-    __syncthreads();
     if (tid < kWave) {
         const int lane = tid;
         const int c0 = 2 * lane < N ? cnt_s[2 * lane] : 0;
@@ -376,7 +422,7 @@ __device__ __forceinline__ void dispatch_block(const int32_t* idx, int B, int N,
         const int e = idx[q];
         if (e >= 0 && e < N) {
             const int t = q / k;
-            const unsigned long long lo = tokmask[e][0], hi = tokmask[e][1];
+            const unsigned long long lo = d.tokmask[e][0], hi = d.tokmask[e][1];
             const int below = t < 64 ? __popcll(lo & ((1ull << t) - 1ull))
                                      : __popcll(lo) + __popcll(hi & ((1ull << (t - 64)) - 1ull));
             perm[off_s[e] + below] = q;
@@ -422,9 +468,8 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     constexpr int P = Gr::kPer;
     constexpr int R = Gr::kRounds;
     __shared__ uint32_t sbase[kMaxExperts / 32];
-    __shared__ int sbase_count;
-    __shared__ int n_l[kMaxBatch];
     __shared__ int32_t idx_l[kDispatch ? kMaxBatch * kMaxTopK : 1];
+    __shared__ DispLds disp_l;   // with dispatch: pairs are counted as they are written
     // tokens at or past n_valid are padding: no experts, nothing added to S_base
     const int B_real = n_valid != nullptr ? min(max(*n_valid, 0), B) : B;
     // batch-size-dependent k0, looked up on the device from the real batch size
@@ -435,6 +480,7 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     const int nwaves = blockDim.x / kWave;
     const int e_first = P * l;
     if (threadIdx.x < kMaxExperts / 32) sbase[threadIdx.x] = 0u;
+    if constexpr (kDispatch) disp_clear(disp_l);
 
     float L[R][P];
     if ((N & 1) == 0) {   // every lane's experts come in 8-byte aligned pairs (e_first and i N are even)
@@ -503,11 +549,12 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
         if (i < B) {
             if (!kOea) {
                 group_write<G>(t, i, k, got, key_logit(top_key), renorm != 0, Z, idx, w, idx_copy);
+                if constexpr (kDispatch)
+#pragma unroll
+                    for (int j = 0; j < P; ++j)
+                        if (t.slot[j] >= 0) disp_add(disp_l, i, e_first + j);
             } else {
-                if (l == 0) {
-                    n_l[i] = got;
-                    if (n_base != nullptr) n_base[i] = got;
-                }
+                if (l == 0 && n_base != nullptr) n_base[i] = got;
 #pragma unroll
                 for (int j = 0; j < P; ++j)
                     if (t.slot[j] >= 0) atomicOr(&sbase[(e_first + j) >> 5], 1u << ((e_first + j) & 31));
@@ -516,15 +563,11 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     }
     if constexpr (kOea) {
         __syncthreads();
-        if (threadIdx.x == 0) {
-            int c = 0;
-            for (int wd = 0; wd < kMaxExperts / 32; ++wd) c += __popc(sbase[wd]);
-            sbase_count = c;
-            if (T_out != nullptr && !kDispatch) *T_out = c;   // with dispatch, T comes from there
-        }
+        int T = 0;   // |S_base|, counted by every thread
+#pragma unroll
+        for (int wd = 0; wd < kMaxExperts / 32; ++wd) T += __popc(sbase[wd]);
+        if (threadIdx.x == 0 && T_out != nullptr && !kDispatch) *T_out = T;   // with dispatch, T comes from there
         if (mask_out != nullptr && threadIdx.x < (N + 31) / 32) mask_out[threadIdx.x] = sbase[threadIdx.x];
-        __syncthreads();
-        const int T = sbase_count;
         const int keep = T < k ? T : k;
 
         // Phase 2: token i keeps the first min(k, T) members of S_base in its
@@ -559,12 +602,18 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
             uint32_t top_key = top1[r];
             const int count = pruned ? got1[r] : keep;
             const int got = group_select<G, false>(t, real, got1[r], count, top_key, 0.0f);
-            if (i < B) group_write<G>(t, i, k, got, key_logit(top_key), true, 0.0f, idx, w, idx_copy);
+            if (i < B) {
+                group_write<G>(t, i, k, got, key_logit(top_key), true, 0.0f, idx, w, idx_copy);
+                if constexpr (kDispatch)
+#pragma unroll
+                    for (int j = 0; j < P; ++j)
+                        if (t.slot[j] >= 0) disp_add(disp_l, i, e_first + j);
+            }
         }
     }
     if constexpr (kDispatch) {
         __syncthreads();
-        dispatch_block(idx_l, B, N, k, cnt, offsets, perm, active, T_out);
+        dispatch_block<true>(idx_l, B, N, k, cnt, offsets, perm, active, T_out, disp_l);
     }
 }
 
@@ -592,7 +641,8 @@ __global__ __launch_bounds__(512) void dispatch_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ perm, int32_t* __restrict__ active,
                                                        int32_t* __restrict__ T_out) {
-    dispatch_block(idx, B, N, k, cnt, offsets, perm, active, T_out);
+    __shared__ DispLds d;
+    dispatch_block(idx, B, N, k, cnt, offsets, perm, active, T_out, d);
 }
 
 // Router logits: one workgroup per (expert, group of 16 tokens); its 4 waves split the hidden
@@ -934,9 +984,11 @@ __global__ __launch_bounds__(1024) void route_group_p2_kernel(const float* __res
     __shared__ uint32_t sbase[kMaxExperts / 32];
     __shared__ int last_s;
     __shared__ int32_t idx_l[kMaxBatch * kMaxTopK];
+    __shared__ DispLds disp_l;
     const int B_real = n_valid != nullptr ? min(max(*n_valid, 0), B) : B;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     if (tid < kMaxExperts / 32) sbase[tid] = 0u;
+    disp_clear(disp_l);
     __syncthreads();
     for (int q = tid; q < B * k; q += blockDim.x) {   // the union of every token's baseline
         const int e = idx[q];
@@ -983,9 +1035,13 @@ __global__ __launch_bounds__(1024) void route_group_p2_kernel(const float* __res
     __syncthreads();
     if (!last_s) return;
     if (mask_out != nullptr && tid < (N + 31) / 32) mask_out[tid] = sbase[tid];
-    for (int q = tid; q < B * k; q += blockDim.x) idx_l[q] = idx[q];
+    for (int q = tid; q < B * k; q += blockDim.x) {   // copy and count the routed pairs
+        const int e = idx[q];
+        idx_l[q] = e;
+        if (e >= 0 && e < N) disp_add(disp_l, q / k, e);
+    }
     __syncthreads();
-    dispatch_block(idx_l, B, N, k, cnt, offsets, perm, active, T_out);
+    dispatch_block<true>(idx_l, B, N, k, cnt, offsets, perm, active, T_out, disp_l);
 }
 
 __global__ void hotness_kernel(float* S, const int32_t* cnt, int N, float alpha) {
