@@ -470,6 +470,29 @@ def _time_steps(step, n, warm=3):
     return (time.perf_counter() - t0) / n * 1e6
 
 
+def _graph_us(call, reps=16, replays=20):
+    """GPU time of one call: `reps` calls captured in one HIP graph, replayed
+    `replays` times (the graph's own launch cost is spread over the reps)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / (reps * replays) * 1e6
+
+
 def batch_sweep(layers, w_r, N, k, H, I, batches=5, steps=30):
     """Routing + dispatch + expert FFN latency and T over B = 1..128 for
     vanilla top-8, simplified OEA (k0 = 3, 5) and full OEA (k0 in {3, 5},
@@ -492,8 +515,7 @@ def batch_sweep(layers, w_r, N, k, H, I, batches=5, steps=30):
         xs = [torch.from_numpy(synth.to_bf16_bits(synth.activations(100 + b, B, H)).view(np.int16)).to(dev)
               .view(torch.bfloat16) for b in range(batches)]
         base = [moe.router_logits(x, w_r) for x in xs]
-        router_us[B] = round(_time_steps(lambda i: moe.router_logits(xs[i % batches], w_r,
-                                                                         layers[0].buffers(B).logits), steps), 2)
+        router_us[B] = round(_graph_us(lambda: moe.router_logits(xs[0], w_r, layers[0].buffers(B).logits)), 2)
         for zipf in (1.1, 0.0):
             beta = torch.from_numpy(synth.zipf_bias(N, zipf)).to(dev)
             logits = [l + beta[None, :] for l in base]
@@ -522,7 +544,8 @@ def batch_sweep(layers, w_r, N, k, H, I, batches=5, steps=30):
         c2, r2 = _fit([q["T"] for q in sel], [q["us"] for q in sel], [q["sum_cnt"] for q in sel])
         fits[fam] = {"us = b*T + c": {"b": c1[0], "c": c1[1], "r2": r1},
                      "us = b*T + a*sum_cnt + c": {"b": c2[0], "a": c2[1], "c": c2[2], "r2": r2}}
-    return {"what": "route+dispatch+expert FFN per step, logits given (router GEMV timed apart)",
+    return {"what": "route+dispatch+expert FFN per step, logits given (router GEMV timed apart, GPU time from a "
+                    "graph of 16 calls)",
             "router_us": router_us, "fits": fits, "points": points}
 
 
