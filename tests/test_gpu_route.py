@@ -216,7 +216,10 @@ def test_dispatch_with_empty_slots_and_rows():
 
 
 @pytest.mark.parametrize("B,H,N,dtype", [(4, 256, 16, "f32"), (16, 2048, 128, "bf16"), (128, 2048, 128, "bf16"),
-                                          (33, 4096, 128, "bf16"), (5, 520, 24, "f32")])
+                                          (33, 4096, 128, "bf16"), (5, 520, 24, "f32"),
+                                          # above 16 tokens, two experts per workgroup: odd N (the last
+                                          # workgroup's second expert is past N), ragged token groups
+                                          (100, 1024, 33, "f32"), (17, 520, 23, "bf16")])
 def test_router_logits_within_fp32_bound(B, H, N, dtype):
     x = synth.activations(5, B, H)
     wr = synth.router_weight(5, N, H)
@@ -298,6 +301,7 @@ def test_handle_publish_writes_the_record():
     # after the router launch
     (97, 128, 2048, 8, "oea", 3, 0.9, 90, "bf16"),
     (65, 33, 1024, 8, "topk", 0, 1.0, None, "bf16"),
+    (70, 40, 520, 8, "oea", 3, 0.9, 66, "f32"),            # fp32 activations, padding
 ])
 def test_fused_router_route_dispatch(B, N, H, k, mode, k0, p, nv, dtype):
     # up to 48 tokens (and for pruned or max-rank OEA at any size) one launch:
