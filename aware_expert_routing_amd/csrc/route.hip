@@ -917,8 +917,8 @@ __global__ __launch_bounds__(kGemvThreads * kFusedGroups) void router_logits_wid
 }
 
 // ---------------------------------------------------------------------------
-// Batches of more than 16 tokens with vanilla top-k or simplified OEA (no
-// rank limit, not pruned), routed by token groups: workgroup g routes tokens
+// Batches of more than kGroupMinBatch (48) tokens with vanilla top-k or
+// simplified OEA (no rank limit, not pruned), routed by token groups: workgroup g routes tokens
 // 16 g .. 16 g + 15, one token per wavefront as for small batches, so a large
 // batch's selections run on B/16 CUs side by side instead of on one.
 //   Vanilla top-k: route_group_kernel<false> writes idx and w; the dispatch
