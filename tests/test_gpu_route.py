@@ -179,15 +179,16 @@ def test_route_variants_parity(B, N, k, mode, k0, p, max_p, nv, scale, zipf):
         assert int(disp["T"].item()) == dref["T"]
 
 
-@pytest.mark.parametrize("mode", ["oea", "pruned"])
-def test_batch_size_dependent_k0_table(mode):
+@pytest.mark.parametrize("mode,B", [("oea", 32), ("pruned", 32), ("oea", 96)])
+def test_batch_size_dependent_k0_table(mode, B):
     # page OEA section 7 notes: k0 chosen from the real batch size (k at B = 1,
-    # larger at small B); the table is read on the device from n_valid
-    B, N, k = 32, 128, 8
+    # larger at small B); the table is read on the device from n_valid.  At
+    # 96 tokens simplified OEA routes by token groups, each group reading it.
+    N, k = 128, 8
     table = moe.k0_schedule(k, B, [(2, 6), (8, 4), (24, 2)], device=DEV)
     tab = table.cpu().numpy()
     assert tab[1] == k and tab[2] == 6 and tab[7] == 6 and tab[8] == 4 and tab[24] == 2 and tab[32] == 2
-    for seed, nv in enumerate([1, 2, 5, 8, 17, 24, 32, None]):
+    for seed, nv in enumerate([1, 2, 5, 8, 17, 24, 32, None] + ([49, 80] if B > 32 else [])):
         l = _logits("normal", seed, B, N, 1.0, 1.1)
         n_valid = None if nv is None else torch.tensor([nv], dtype=torch.int32, device=DEV)
         route, disp = moe.route_dispatch(torch.from_numpy(l).to(DEV), k, mode, 1, 1.0, True, n_valid=n_valid,
