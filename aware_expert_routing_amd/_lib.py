@@ -226,7 +226,7 @@ def dispatch(idx, N: int, out=None, stream=None):
 def route_dispatch(logits, k: int, mode: str, k0: int = 0, p: float = 1.0, renorm: bool = True,
                    route=None, disp=None, stream=None, max_p: int | None = None, n_valid=None,
                    k0_by_batch=None):
-    """Routing ("topk", "oea" or "pruned") and dispatch in one launch.
+    """Routing ("topk", "oea" or "pruned") and dispatch (one launch up to 48 tokens).
 
     max_p: OEA Phase 2 rank limit (default N); n_valid: optional device int32
     tensor [1] with the number of real tokens; k0_by_batch: optional device
@@ -256,7 +256,7 @@ def route_dispatch(logits, k: int, mode: str, k0: int = 0, p: float = 1.0, renor
 def router_route_dispatch(x, w_r, k: int, mode: str, k0: int = 0, p: float = 1.0, renorm: bool = True,
                           route=None, disp=None, logits=None, sync=None, stream=None, max_p: int | None = None,
                           n_valid=None, k0_by_batch=None):
-    """Router logits, routing and dispatch in one launch.  sync: device int32
+    """Router logits, routing and dispatch (one launch up to 48 tokens).  sync: device int32
     [1] that starts at zero (allocated here if None).  Returns (logits, route,
     disp)."""
     B, H = x.shape

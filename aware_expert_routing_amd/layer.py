@@ -103,7 +103,7 @@ class MoELayer:
     def route(self, logits: torch.Tensor, mode: str, k0: int = 0, p: float = 1.0,
               buf: Buffers | None = None, stream=None, max_p: int | None = None, n_valid=None,
               k0_by_batch=None) -> Buffers:
-        """Routing ("topk", "oea" or "pruned") and dispatch in one launch; n_valid
+        """Routing ("topk", "oea" or "pruned") and dispatch (one launch up to 48 tokens); n_valid
         (device int32 [1]) marks trailing tokens as padding; k0_by_batch (device
         int32 [B+1], see k0_schedule) picks k0 from the real batch size."""
         B = logits.shape[0]
@@ -122,7 +122,8 @@ class MoELayer:
                 logits: torch.Tensor | None = None, stream=None, max_p: int | None = None,
                 n_valid=None, k0_by_batch=None) -> Buffers:
         """Whole layer.  If `logits` is given the router GEMV is skipped;
-        otherwise router, routing and dispatch run as one launch."""
+        otherwise router, routing and dispatch run together (one launch up to 48
+        tokens)."""
         B = x.shape[0]
         buf = self.buffers(B)
         if logits is None:

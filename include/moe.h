@@ -146,9 +146,14 @@ int moe_dispatch(const int32_t *idx, int B, int N, int k, int32_t *cnt, int32_t 
                  int32_t *perm, int32_t *active, int32_t *T, void *stream);
 
 /*
- * Routing and dispatch in one launch, with the general OEA knobs [OEA
- * sections 2 Q1/Q2, 3, 4 (Eq. 2), 5 (maxP, k_max, pruned vs OEA) and 7
- * (padding tokens must not inflate T)].
+ * Routing and dispatch, with the general OEA knobs [OEA sections 2 Q1/Q2, 3,
+ * 4 (Eq. 2), 5 (maxP, k_max, pruned vs OEA) and 7 (padding tokens must not
+ * inflate T)].  One launch, in which one workgroup routes and dispatches the
+ * batch, for batches of up to 48 tokens and for pruned and max_p < N modes;
+ * above 48 tokens vanilla top-k and simplified OEA route 16 tokens per
+ * workgroup and take two launches (top-k: routing, then dispatch; OEA: Phase
+ * 1, then Phase 2 with the dispatch in the workgroup that finishes last).
+ * The results are the same either way.
  *   mode MOE_ROUTE_TOPK   : vanilla top-k (renorm as in moe_route_topk)
  *   mode MOE_ROUTE_OEA    : OEA; Phase 2 may take only experts the token
  *                           ranks within its top max_p (k0 <= max_p <= N;
@@ -171,8 +176,8 @@ int moe_dispatch(const int32_t *idx, int B, int N, int k, int32_t *cnt, int32_t 
  *             real batch size of each replay.
  *   Outputs as moe_route_oea (n_base, sbase_mask may be NULL; ignored for
  *   top-k) followed by moe_dispatch on idx; T = number of active experts
- *   (for OEA and pruned also |S_base|).  The routed pairs stay on chip
- *   between routing and dispatch.
+ *   (for OEA and pruned also |S_base|).  In the one-launch form the routed
+ *   pairs stay on chip between routing and dispatch.
  */
 enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_OEA = 1, MOE_ROUTE_PRUNED = 2 };
 int moe_route_dispatch(const float *logits, int B, int N, int k, int mode, int k0, float p, int max_p,
@@ -182,16 +187,20 @@ int moe_route_dispatch(const float *logits, int B, int N, int k, int mode, int k
                        int32_t *T, void *stream);
 
 /*
- * Router logits, routing and dispatch in one launch [OEA section 2 Q1: the
- * router scores every expert for every token; then as moe_route_dispatch].
+ * Router logits, routing and dispatch [OEA section 2 Q1: the router scores
+ * every expert for every token; then as moe_route_dispatch].
  *   x, x_dtype, w_r, H : as moe_router_logits; logits [B, N] fp32 receives
  *                        the router output (the routing decisions use it)
  *   the remaining arguments are those of moe_route_dispatch, plus
  *   sync : device int32 [1], zero before the first call; every call leaves
  *          it at zero.  Calls sharing a sync word must be ordered (e.g. on
  *          one stream).
- * The launch's workgroups each compute a slice of the logits; the one that
- * finishes last routes and dispatches the batch, so no workgroup waits.
+ * Where moe_route_dispatch takes one launch, this is one launch too: its
+ * workgroups each compute a slice of the logits, and the one that finishes
+ * last routes and dispatches the batch, so no workgroup waits.  Otherwise
+ * (above 48 tokens, vanilla top-k or simplified OEA) the logits are computed
+ * as by moe_router_logits and the token-group routing follows; sync is then
+ * not touched.  The logits have the same bits on every path.
  * Requires H a positive multiple of 8, plus the conditions of
  * moe_route_dispatch.
  */
