@@ -853,8 +853,10 @@ def small_batch_graphs(layers, N, k, H, steps=60):
     batches), OEA k0 = 3 and vanilla top-8; medians of per-step HIP events:
     eager launches against one captured HIP graph per layer copy, and the 8
     layer copies as one decode step, eager against one graph of all 8
-    (per layer).  host_us: the host's time per layer call, eager forward
-    against the 8-layer graph's replay, without synchronisation."""
+    (per layer), the graph also from cold caches (a 1 GB buffer written and
+    read before each step, outside its events).  host_us: the host's time per
+    layer call, eager forward against the 8-layer graph's replay, without
+    synchronisation."""
     import numpy as np
     import torch
 
@@ -863,6 +865,9 @@ def small_batch_graphs(layers, N, k, H, steps=60):
 
     dev = layers[0].device
     stream = torch.cuda.current_stream()
+    # written and read before each cold step (outside its events): 1 GB, more
+    # than the L2s and the 256 MB MALL hold, so no weights survive in a cache
+    flush = torch.zeros(1 << 28, device=dev, dtype=torch.float32)
     out = []
     for B in (1, 2, 4, 8):
         xs = [torch.from_numpy(synth.to_bf16_bits(synth.activations(600 + c, B, H)).view(np.int16)).to(dev)
@@ -913,6 +918,15 @@ def small_batch_graphs(layers, N, k, H, steps=60):
                 e1[i].record(stream)
             torch.cuda.synchronize()
             graph_step = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(reps)])) * 1e3
+            # the same replays from cold caches (the step's expert weights at
+            # B = 1, OEA k0 = 3 -- 8 x 3 experts, 226 MB -- would fit the MALL)
+            for i in range(reps):
+                flush.add_(1.0)
+                e0[i].record(stream)
+                g_all.replay()
+                e1[i].record(stream)
+            torch.cuda.synchronize()
+            graph_step_cold = float(np.median([e0[i].elapsed_time(e1[i]) for i in range(reps)])) * 1e3
             t0 = time.perf_counter()
             for i in range(reps):
                 g_all.replay()
@@ -930,6 +944,7 @@ def small_batch_graphs(layers, N, k, H, steps=60):
                         "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2),
                         "step_of_%d_layers" % n_l: {"eager_us_per_layer": round(eager_step / n_l, 2),
                                                     "graph_us_per_layer": round(graph_step / n_l, 2),
+                                                    "graph_us_per_layer_cold": round(graph_step_cold / n_l, 2),
                                                     "host_us_per_layer_eager": round(host_eager, 1),
                                                     "host_us_per_layer_graph": round(host_graph, 1)}})
     return out
