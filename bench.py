@@ -170,11 +170,24 @@ def main():
     fixed_ffn = B * H * 2 + B * H * 4
 
     def run_mode(mode, k0):
-        # T per batch (identical for every layer copy: same weights)
-        Ts = []
+        # T per batch (identical for every layer copy: same weights), and the
+        # routing's own counters: routed pairs, the cnt histogram over active
+        # experts (bins 1, 2, 3-4, 5-8, 9-16, 17-32, 33-128 tokens), and the
+        # tokens' baseline counts n_i (OEA)
+        Ts, sum_cnt, hist, n_base = [], [], np.zeros(7, np.int64), []
+        edges = np.array([1, 2, 3, 5, 9, 17, 33, 129])
         for b in range(args.batches):
             buf = layers[0].forward(xs[b], mode, k0, 1.0)
             Ts.append(int(buf.disp["T"].item()))
+            cnt = buf.disp["cnt"].cpu().numpy()
+            sum_cnt.append(int(cnt.sum()))
+            hist += np.histogram(cnt[cnt > 0], bins=edges)[0]
+            if mode == "oea":
+                n_base.append(float(buf.route["n_base"].float().mean().item()))
+        routing_counters = {"sum_cnt_mean": float(np.mean(sum_cnt)),
+                            "cnt_hist_bins": ["1", "2", "3-4", "5-8", "9-16", "17-32", "33-128"],
+                            "cnt_hist_per_batch": [round(float(h) / args.batches, 2) for h in hist],
+                            "n_i_mean": round(float(np.mean(n_base)), 3) if n_base else None}
         stream = torch.cuda.current_stream()
         n_ev = args.steps
         evl = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
@@ -269,6 +282,7 @@ def main():
             gbps=layer_bytes / wall / 1e9,
             T_mean=float(np.mean(Tsteps)),
             T_per_batch=Ts,
+            routing_counters=routing_counters,
             ffn_us=ffn_s / args.steps * 1e6,
             ffn_us_p10=float(np.percentile(ffn_ms, 10) * 1e3),
             ffn_us_p50=float(np.percentile(ffn_ms, 50) * 1e3),
