@@ -93,17 +93,3 @@ def routing_order_is_robust(logits32: np.ndarray, ref_idx: np.ndarray, eps: floa
             return False
     return True
 
-
-def sample_tokens(cnt_idx: np.ndarray, N: int, n: int = 8, hot_take: int = 4) -> list[int]:
-    """Up to hot_take tokens of the most-routed expert, then evenly spaced
-    tokens, n in all (fewer if the batch is smaller)."""
-    B = cnt_idx.shape[0]
-    cnt = np.bincount(cnt_idx[cnt_idx >= 0].ravel(), minlength=N)
-    hot = int(np.argmax(cnt))
-    toks = [int(i) for i in np.nonzero((cnt_idx == hot).any(1))[0][:hot_take]]
-    for i in np.linspace(0, B - 1, n).round().astype(int):
-        if len(toks) >= n:
-            break
-        if int(i) not in toks:
-            toks.append(int(i))
-    return sorted(toks)
