@@ -922,7 +922,8 @@ __global__ __launch_bounds__(kGemvThreads * kFusedGroups) void router_logits_wid
 // 16 g .. 16 g + 15, one token per wavefront as for small batches, so a large
 // batch's selections run on B/16 CUs side by side instead of on one.
 //   Vanilla top-k: route_group_kernel<false> writes idx and w; the dispatch
-//   (dispatch_kernel) follows.
+//   (dispatch_kernel) follows, or, when the caller has a completion count
+//   (the router's sync word), runs in the routing launch's last workgroup.
 //   OEA: route_group_kernel<true> runs Phase 1 and leaves each token's
 //   baseline in its idx row (slots 0 .. n_i - 1, then -1); in the next
 //   launch every workgroup rebuilds S_base from those rows (integer OR in
@@ -958,23 +959,47 @@ __device__ __forceinline__ void group_token_load(const float* __restrict__ logit
     }
 }
 
-// Launch: ceil(B / 16) workgroups of 1024 threads.  kOea: Phase 1 and the
-// baseline rows (and n_base); else vanilla top-k written in full.  Workgroup
-// 0 also clears *T_out, the next launch's completion count.
+// The hand-off after a token-group kernel's writes: every wavefront waits
+// for its stores, the barrier orders them before thread 0's count (an
+// agent-scope release and, in the workgroup that completes the count,
+// acquire), and that workgroup writes S_base (when given) and dispatches the
+// batch from idx.  The dispatch writes T to T_out, which may be the count
+// itself; with reset the count is stored back to zero afterwards.
+__device__ __forceinline__ void group_dispatch_last(int32_t* __restrict__ idx, int B, int N, int k,
+                                                    int32_t* __restrict__ count, bool reset,
+                                                    int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ perm, int32_t* __restrict__ active,
+                                                    int32_t* __restrict__ T_out, uint32_t* __restrict__ mask_out,
+                                                    const uint32_t* sbase) {
+    __shared__ int last_s;
+    __shared__ int32_t idx_l[kMaxBatch * kMaxTopK];
+    __shared__ DispLds disp_l;
+    const int tid = threadIdx.x;
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0)
+        last_s = __hip_atomic_fetch_add(count, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                 static_cast<int>(gridDim.x) - 1;
+    __syncthreads();
+    if (!last_s) return;
+    if (mask_out != nullptr && tid < (N + 31) / 32) mask_out[tid] = sbase[tid];
+    disp_clear(disp_l);
+    __syncthreads();
+    for (int q = tid; q < B * k; q += blockDim.x) {   // copy and count the routed pairs
+        const int e = idx[q];
+        idx_l[q] = e;
+        if (e >= 0 && e < N) disp_add(disp_l, q / k, e);
+    }
+    __syncthreads();
+    dispatch_block<true>(idx_l, B, N, k, cnt, offsets, perm, active, T_out, disp_l);
+    if (reset && tid == 0) *count = 0;   // the next call's launches come after this one
+}
+
+// One token of route_group_kernel: its selection and its writes.
 template <bool kOea>
-__global__ __launch_bounds__(1024) void route_group_kernel(const float* __restrict__ logits, int B, int N, int k,
-                                                           int k0, float p, int renorm, int32_t* __restrict__ idx,
-                                                           float* __restrict__ w, int32_t* __restrict__ n_base,
-                                                           int32_t* __restrict__ T_out,
-                                                           const int32_t* __restrict__ n_valid,
-                                                           const int32_t* __restrict__ k0_by_batch) {
-    const int B_real = n_valid != nullptr ? min(max(*n_valid, 0), B) : B;
-    if (kOea && k0_by_batch != nullptr) k0 = min(max(k0_by_batch[B_real], 1), k);
-    if (kOea && blockIdx.x == 0 && threadIdx.x == 0) *T_out = 0;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int i = kGroupTok * blockIdx.x + threadIdx.x / kWave;
-    if (i >= B) return;   // whole wavefronts; the kernel has no barrier
-    const bool real = i < B_real;
+__device__ __forceinline__ void group_route_token(const float* __restrict__ logits, int N, int k, int k0, float p,
+                                                  int renorm, int32_t* __restrict__ idx, float* __restrict__ w,
+                                                  int32_t* __restrict__ n_base, int i, bool real, int lane) {
     Tok<2> t;
     group_token_load<false>(logits, i, N, real, t);
     const bool need_z = kOea ? (p < 1.0f) : (renorm == 0);
@@ -1001,6 +1026,35 @@ __global__ __launch_bounds__(1024) void route_group_kernel(const float* __restri
     }
 }
 
+// Launch: ceil(B / 16) workgroups of 1024 threads.  kOea: Phase 1 and the
+// baseline rows (and n_base); else vanilla top-k written in full.  Workgroup
+// 0 also clears *T_out, the next launch's completion count (OEA).  Top-k
+// with a completion count `count` (zero on entry, left at zero): the
+// workgroup that completes it dispatches the batch, as Phase 2 does for OEA.
+template <bool kOea>
+__global__ __launch_bounds__(1024) void route_group_kernel(const float* __restrict__ logits, int B, int N, int k,
+                                                           int k0, float p, int renorm, int32_t* __restrict__ idx,
+                                                           float* __restrict__ w, int32_t* __restrict__ n_base,
+                                                           int32_t* __restrict__ T_out,
+                                                           const int32_t* __restrict__ n_valid,
+                                                           const int32_t* __restrict__ k0_by_batch,
+                                                           int32_t* __restrict__ count, int32_t* __restrict__ cnt,
+                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ active) {
+    const int B_real = n_valid != nullptr ? min(max(*n_valid, 0), B) : B;
+    if (kOea && k0_by_batch != nullptr) k0 = min(max(k0_by_batch[B_real], 1), k);
+    if (kOea && blockIdx.x == 0 && threadIdx.x == 0) *T_out = 0;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int i = kGroupTok * blockIdx.x + threadIdx.x / kWave;
+    if (!kOea && count != nullptr) {   // every wavefront reaches the hand-off's barriers
+        if (i < B) group_route_token<kOea>(logits, N, k, k0, p, renorm, idx, w, n_base, i, i < B_real, lane);
+        group_dispatch_last(idx, B, N, k, count, true, cnt, offsets, perm, active, T_out, nullptr, nullptr);
+        return;
+    }
+    if (i >= B) return;   // whole wavefronts; no barrier follows
+    group_route_token<kOea>(logits, N, k, k0, p, renorm, idx, w, n_base, i, i < B_real, lane);
+}
+
 // OEA Phase 2 of token group blockIdx.x and, in the workgroup that completes
 // the count in *T_out, the dispatch of the whole batch (which then writes T
 // there).  Launch: ceil(B / 16) workgroups of 1024 threads.
@@ -1012,13 +1066,9 @@ __global__ __launch_bounds__(1024) void route_group_p2_kernel(const float* __res
                                                               int32_t* __restrict__ perm, int32_t* __restrict__ active,
                                                               int32_t* __restrict__ T_out) {
     __shared__ uint32_t sbase[kMaxExperts / 32];
-    __shared__ int last_s;
-    __shared__ int32_t idx_l[kMaxBatch * kMaxTopK];
-    __shared__ DispLds disp_l;
     const int B_real = n_valid != nullptr ? min(max(*n_valid, 0), B) : B;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     if (tid < kMaxExperts / 32) sbase[tid] = 0u;
-    disp_clear(disp_l);
     __syncthreads();
     for (int q = tid; q < B * k; q += blockDim.x) {   // the union of every token's baseline
         const int e = idx[q];
@@ -1055,23 +1105,8 @@ __global__ __launch_bounds__(1024) void route_group_p2_kernel(const float* __res
         const int got = group_select<64, false>(t, real, got1, keep, top_key, 0.0f);
         group_write<64>(t, i, k, got, key_logit(top_key), true, 0.0f, idx, w, nullptr);
     }
-    // Hand-off: this workgroup's idx and w stores complete before the count
-    // (an agent-scope release and, in the completing workgroup, acquire).
-    wait_vmem();
-    __syncthreads();
-    if (tid == 0)
-        last_s = __hip_atomic_fetch_add(T_out, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-                 static_cast<int>(gridDim.x) - 1;
-    __syncthreads();
-    if (!last_s) return;
-    if (mask_out != nullptr && tid < (N + 31) / 32) mask_out[tid] = sbase[tid];
-    for (int q = tid; q < B * k; q += blockDim.x) {   // copy and count the routed pairs
-        const int e = idx[q];
-        idx_l[q] = e;
-        if (e >= 0 && e < N) disp_add(disp_l, q / k, e);
-    }
-    __syncthreads();
-    dispatch_block<true>(idx_l, B, N, k, cnt, offsets, perm, active, T_out, disp_l);
+    // the count is T_out (cleared by the Phase-1 launch); the dispatch then writes T there
+    group_dispatch_last(idx, B, N, k, T_out, false, cnt, offsets, perm, active, T_out, mask_out, sbase);
 }
 
 __global__ void hotness_kernel(float* S, const int32_t* cnt, int N, float alpha) {
@@ -1161,21 +1196,26 @@ bool route_by_groups(int B, int N, int mode, int max_p) {
     return B > kGroupMinBatch && (mode == MOE_ROUTE_TOPK || (mode == MOE_ROUTE_OEA && max_p >= N));
 }
 
+// count: null, or a caller's word that is zero on entry (and left at zero):
+// vanilla top-k then dispatches in the routing launch's last workgroup
+// instead of a launch of its own.
 hipError_t launch_route_groups(const float* logits, int B, int N, int k, int mode, int k0, float p, int renorm,
                                const int32_t* n_valid, const int32_t* k0_by_batch, int32_t* idx, float* w,
                                int32_t* n_base, uint32_t* mask, int32_t* cnt, int32_t* offsets, int32_t* perm,
-                               int32_t* active, int32_t* T, hipStream_t s) {
+                               int32_t* active, int32_t* T, int32_t* count, hipStream_t s) {
     const int groups = (B + kGroupTok - 1) / kGroupTok;
     if (mode == MOE_ROUTE_TOPK) {
         route_group_kernel<false><<<groups, kGroupTok * kWave, 0, s>>>(logits, B, N, k, k, 1.0f, renorm, idx, w,
-                                                                        nullptr, nullptr, n_valid, nullptr);
+                                                                        nullptr, T, n_valid, nullptr, count, cnt,
+                                                                        offsets, perm, active);
         hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (e != hipSuccess || count != nullptr) return e;
         dispatch_kernel<<<1, 512, 0, s>>>(idx, B, N, k, cnt, offsets, perm, active, T);
         return hipGetLastError();
     }
     route_group_kernel<true><<<groups, kGroupTok * kWave, 0, s>>>(logits, B, N, k, k0, p, 1, idx, w, n_base, T,
-                                                                   n_valid, k0_by_batch);
+                                                                   n_valid, k0_by_batch, nullptr, nullptr, nullptr,
+                                                                   nullptr, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     route_group_p2_kernel<<<groups, kGroupTok * kWave, 0, s>>>(logits, B, N, k, idx, w, mask, n_valid, cnt, offsets,
@@ -1192,7 +1232,7 @@ hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int m
                                  int32_t* T, hipStream_t s) {
     if (route_by_groups(B, N, mode, max_p))
         return launch_route_groups(logits, B, N, k, mode, k0, p, renorm, n_valid, k0_by_batch, idx, w, n_base, mask,
-                                   cnt, offsets, perm, active, T, s);
+                                   cnt, offsets, perm, active, T, nullptr, s);
     const bool oea = mode != MOE_ROUTE_TOPK;
 #define MOE_ROUTE(G_, OEA_)                                                                                      \
     route_kernel<OEA_, true, G_><<<1, route_threads(B), 0, s>>>(                                                 \
@@ -1216,11 +1256,12 @@ hipError_t launch_router_route_dispatch(const void* x, int x_dtype, const float*
                                         int32_t* n_base, uint32_t* mask, int32_t* cnt, int32_t* offsets,
                                         int32_t* perm, int32_t* active, int32_t* T, int32_t* sync, hipStream_t s) {
     if (route_by_groups(B, N, mode, mode == MOE_ROUTE_OEA ? max_p : N)) {
-        // large batches: the logits in their own launch, then the token-group kernels
+        // large batches: the logits in their own launch, then the token-group
+        // kernels (top-k dispatches in its routing launch, counting in sync)
         hipError_t e = launch_router_logits(x, x_dtype, w_r, B, H, N, logits, s);
         if (e != hipSuccess) return e;
         return launch_route_groups(logits, B, N, k, mode, k0, p, renorm, n_valid, k0_by_batch, idx, w, n_base, mask,
-                                   cnt, offsets, perm, active, T, s);
+                                   cnt, offsets, perm, active, T, sync, s);
     }
     const int fe = B <= kFusedMaxB2 ? 2 : 4;
     const dim3 grid((N + fe - 1) / fe, (B + kGemvTok - 1) / kGemvTok);

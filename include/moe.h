@@ -199,8 +199,9 @@ int moe_route_dispatch(const float *logits, int B, int N, int k, int mode, int k
  * workgroups each compute a slice of the logits, and the one that finishes
  * last routes and dispatches the batch, so no workgroup waits.  Otherwise
  * (above 48 tokens, vanilla top-k or simplified OEA) the logits are computed
- * as by moe_router_logits and the token-group routing follows; sync is then
- * not touched.  The logits have the same bits on every path.
+ * as by moe_router_logits and the token-group routing follows (vanilla top-k
+ * counts its workgroups in sync and dispatches in the last one; sync is again
+ * left at zero).  The logits have the same bits on every path.
  * Requires H a positive multiple of 8, plus the conditions of
  * moe_route_dispatch.
  */

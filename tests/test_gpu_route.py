@@ -306,7 +306,8 @@ def test_handle_publish_writes_the_record():
 ])
 def test_fused_router_route_dispatch(B, N, H, k, mode, k0, p, nv, dtype):
     # up to 48 tokens (and for pruned or max-rank OEA at any size) one launch:
-    # router GEMV slices, then the last workgroup routes and dispatches; same
+    # router GEMV slices, then the last workgroup routes and dispatches; above
+    # that the token-group kernels, whose last workgroup dispatches; same
     # logits as moe_router_logits bit for bit, routing as the oracle's on
     # those logits; the sync word is left at zero for the next call
     x = synth.activations(40 + B, B, H)
