@@ -303,6 +303,10 @@ def test_handle_publish_writes_the_record():
     (97, 128, 2048, 8, "oea", 3, 0.9, 90, "bf16"),
     (65, 33, 1024, 8, "topk", 0, 1.0, None, "bf16"),
     (70, 40, 520, 8, "oea", 3, 0.9, 66, "f32"),            # fp32 activations, padding
+    # vanilla top-k above 48 tokens: the last routing workgroup dispatches
+    (128, 128, 2048, 8, "topk", 0, 1.0, None, "bf16"),     # the benchmarked B = 128 layer
+    (100, 128, 2048, 16, "topk", 0, 1.0, 61, "bf16"),      # k = 16, padding, ragged last group
+    (49, 128, 1024, 1, "topk", 0, 1.0, None, "f32"),       # k = 1, one token past one launch
 ])
 def test_fused_router_route_dispatch(B, N, H, k, mode, k0, p, nv, dtype):
     # up to 48 tokens (and for pruned or max-rank OEA at any size) one launch:
