@@ -554,18 +554,29 @@ __device__ __forceinline__ void run_items(const char* x_in, const int32_t* perm_
                 for (int t = 0; t < NT; ++t) acc[m][r][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     };
     zero();
-    // The weight stages go out first; the token lookups (perm, then the
-    // activation rows) follow, so their round trips overlap the weights'.
+    // The perm entries go out first, then the weight stages: loads return in
+    // order, so the wait for the perm entries does not cover the weights, and
+    // the activation rows they address are requested while the weights are
+    // still in flight.
+    if constexpr (PRE == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int tok = 16 * t + n;
+            pair[t] = ((const __attribute__((address_space(1))) int32_t*)perm)[first + (tok < cnt ? tok : 0)];
+        }
+        // keep the weight loads below (the perm loads stay first)
+        __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         if (d < PRE) ring[d] = pre[d];
         else issue(ring[d], 0, d);
     }
+    // and the address arithmetic on the perm entries (which waits for them) below them
+    if constexpr (PRE == 0) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int tok = 16 * t + n;
         if constexpr (PRE > 0) pair[t] = pre_pair;
-        else pair[t] = ((const __attribute__((address_space(1))) int32_t*)perm)[first + (tok < cnt ? tok : 0)];
         if constexpr (PHASE == 0)
             arow[t] = xg + static_cast<size_t>(pair[t] / k) * H * (XF32 ? 4 : 2);
         else
