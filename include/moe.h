@@ -35,7 +35,7 @@ extern "C" {
 enum {
     MOE_OK = 0,
     MOE_EINVAL = -1,         /* argument out of range or null pointer           */
-    MOE_EUNSUPPORTED = -2,   /* valid but beyond this build's limits (B > 128)  */
+    MOE_EUNSUPPORTED = -2,   /* valid but beyond the library's limits (B > 128) */
     MOE_EHIP = -3,           /* a HIP runtime call or kernel launch failed      */
     MOE_EFULL = -4           /* a pool has no free block (backpressure; retry   */
                              /* later), see moe_residency.h                     */
