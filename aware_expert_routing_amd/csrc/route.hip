@@ -5,7 +5,7 @@
 //   section 2 Q2   OEA Phase 1 (top-n_i baseline, n_i = min(k0, t_i), t_i an
 //                  adaptive top-p count), the union S_base, Phase 2 piggyback
 //                  of experts already in S_base, renormalised scores;
-//   section 3      Algorithm 1 flow: the "if e_ij in S_base" gate;
+//   section 3      Algorithm 1 flow: a candidate is kept only if it is a member of S_base;
 //   section 4      Eq. 2: cnt_i per expert and T = #{i : cnt_i > 0}.
 // Page "DynaExq" section 2.5: hotness score S <- alpha S + (1 - alpha) c.
 //

@@ -12,7 +12,7 @@
  *     keeps each token's top-n_i with n_i = min(k0, t_i), t_i an adaptive top-p
  *     count; S_base is the union; Phase 2 adds lower-ranked experts only if they
  *     are already in S_base; kept scores are renormalised.
- *   - section 3 (Algorithm 1 flow, the "if e_ij in S_base" gate), section 5
+ *   - section 3 (Algorithm 1 flow: a candidate is kept only if it is a member of S_base), section 5
  *     (Figure 3: simplified OEA drops p and maxP and sets k_max = k).
  *   - section 4, Eq. 2: cnt_i is the number of tokens routed to expert i,
  *     T the number of experts with cnt_i > 0.
