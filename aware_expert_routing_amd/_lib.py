@@ -154,8 +154,13 @@ def _check_i32_table(t, need: int, name: str, device) -> None:
 
 
 def _stream(stream=None) -> int:
+    """The raw HIP stream handle to launch on: `stream`'s (a torch stream or
+    an int handle), else the current stream of the current device (read
+    without building a torch Stream object, which costs microseconds per call)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
+    if isinstance(stream, int):
+        return stream
     return stream.cuda_stream
 
 
@@ -292,9 +297,8 @@ def expert_ffn(table, N: int, H: int, I: int, x, idx, w, disp, y=None, ws=None, 
     dev = x.device
     if y is None:
         y = torch.empty(B, H, device=dev, dtype=torch.float32)
-    nbytes = ffn_workspace_bytes(B, k, H, I)
-    if ws is None:
-        ws = torch.zeros(nbytes, device=dev, dtype=torch.uint8)
+    if ws is None:   # (a caller's workspace is checked for size by the library)
+        ws = torch.zeros(ffn_workspace_bytes(B, k, H, I), device=dev, dtype=torch.uint8)
     _check("moe_expert_ffn", lib().moe_expert_ffn(
         _ptr(table), N, H, I, _ptr(x), _x_dtype(x), _ptr(idx), _ptr(w), _ptr(disp["offsets"]),
         _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]), B, k, _ptr(y), _ptr(ws),

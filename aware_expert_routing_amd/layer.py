@@ -126,6 +126,7 @@ class MoELayer:
         tokens)."""
         B = x.shape[0]
         buf = self.buffers(B)
+        stream = L._stream(stream)   # looked up once for both calls
         if logits is None:
             if mode not in ("topk", "oea", "pruned"):
                 raise ValueError(mode)
