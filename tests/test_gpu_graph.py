@@ -103,3 +103,33 @@ def test_one_graph_for_several_layers():
             torch.cuda.synchronize()
             assert torch.equal(y_graph, eager.y), (rep, j)
             assert T_graph == int(eager.disp["T"].item()), (rep, j)
+
+
+@pytest.mark.parametrize("B", [16, 1])
+def test_forward_on_a_side_stream(B):
+    # the layer launches on the caller's stream: the current stream when none
+    # is given (inside `with torch.cuda.stream(s)`), a torch stream, or its raw
+    # handle; each gives the default stream's result bit for bit
+    N, k, H, I = 32, 8, 512, 256
+    layer, _ = build_layer(N, k, H, I, 12, fmt="bf16")
+    ref_layer, _ = build_layer(N, k, H, I, 12, fmt="bf16")
+    x = _x(7, B, H)
+    ref = ref_layer.forward(x, "oea", 3, 1.0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()   # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    for how in ("context", "stream", "handle"):
+        layer.buffers(B).y.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            xs = x.clone()   # produced on the side stream, consumed there without a sync
+            if how == "context":
+                out = layer.forward(xs, "oea", 3, 1.0)
+            elif how == "stream":
+                out = layer.forward(xs, "oea", 3, 1.0, stream=side)
+            else:
+                out = layer.forward(xs, "oea", 3, 1.0, stream=side.cuda_stream)
+        side.synchronize()
+        assert torch.equal(out.y, ref.y), how
+        for key in ("cnt", "offsets", "perm", "active", "T"):
+            assert torch.equal(out.disp[key], ref.disp[key]), (how, key)
