@@ -181,6 +181,32 @@ def test_route_dispatch_rejects_bad_arguments():
     assert lib.moe_route_dispatch(*args(N=0)) == -1
 
 
+def test_router_route_dispatch_rejects_bad_arguments():
+    # the layer's routing call checks everything before it launches: a
+    # missing completion word, the activation type, H, the mode and its knobs,
+    # and sizes past the supported batch
+    lib = moe.lib()
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("x", FAKE), ("x_dtype", moe.MOE_DT_BF16), ("w_r", FAKE), ("B", 64), ("H", 2048), ("N", 128), ("k", 8),
+        ("mode", 0), ("k0", 0), ("p", 1.0), ("max_p", 128), ("renorm", 1), ("n_valid", None), ("k0_by_batch", None),
+        ("logits", FAKE), ("idx", FAKE), ("w", FAKE), ("n_base", None), ("mask", None), ("cnt", FAKE),
+        ("offsets", FAKE), ("perm", FAKE), ("active", FAKE), ("T", FAKE), ("sync", FAKE), ("stream", None))]
+    f = lib.moe_router_route_dispatch
+    assert f(*args(sync=None)) == -1 and "null" in lib.moe_last_error().decode()
+    assert f(*args(logits=None)) == -1
+    assert f(*args(x_dtype=7)) == -1
+    assert f(*args(H=2044)) == -1 and "multiple of 8" in lib.moe_last_error().decode()
+    assert f(*args(H=0)) == -1
+    assert f(*args(mode=5)) == -1
+    assert f(*args(mode=1, k0=0)) == -1
+    assert f(*args(mode=1, k0=9)) == -1
+    assert f(*args(mode=1, k0=3, p=0.0)) == -1
+    assert f(*args(mode=1, k0=3, max_p=2)) == -1
+    assert f(*args(mode=1, k0=3, max_p=129)) == -1
+    assert f(*args(B=129)) == -2
+    assert f(*args(k=0)) == -1
+
+
 # ---------------------------------------------------------------------------
 # residency host objects (include/moe_residency.h): pure host bookkeeping
 # ---------------------------------------------------------------------------
