@@ -133,3 +133,32 @@ def test_forward_on_a_side_stream(B):
         assert torch.equal(out.y, ref.y), how
         for key in ("cnt", "offsets", "perm", "active", "T"):
             assert torch.equal(out.disp[key], ref.disp[key]), (how, key)
+
+
+@pytest.mark.parametrize("mode,k0,B,n_reals", [("topk", 0, 64, (64, 50, 64)), ("oea", 3, 64, (64, 33, 64)),
+                                               ("topk", 0, 100, (100, 61, 17))])
+def test_graph_replays_above_48_tokens(mode, k0, B, n_reals):
+    # above 48 tokens the layer routes by token groups after the router launch
+    # and the last routing workgroup dispatches, counting workgroups in a word
+    # it leaves at zero: every replay must still match the eager result
+    N, k, H, I = 64, 8, 512, 256
+    layer, _ = build_layer(N, k, H, I, 13, fmt="bf16")
+    eager_layer, _ = build_layer(N, k, H, I, 13, fmt="bf16")
+    x_static = _x(20, B, H).clone()
+    nv = torch.tensor([B], dtype=torch.int32, device=DEV)
+    graph = layer.capture(x_static, mode, k0, 1.0, n_valid=nv)
+    for rep, n_real in enumerate(n_reals):
+        x_static.copy_(_x(21 + rep, B, H))
+        nv.fill_(n_real)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(layer.buffers(B).extra["sync"].item()) == 0, rep
+        y_graph = layer.buffers(B).y.clone()
+        got = {key: t.clone() for key, t in layer.buffers(B).disp.items()}
+        ref = eager_layer.forward(x_static, mode, k0, 1.0, n_valid=nv)
+        torch.cuda.synchronize()
+        assert torch.equal(y_graph, ref.y), rep
+        for key in got:
+            assert torch.equal(got[key], ref.disp[key]), (rep, key)
+        if n_real < B:
+            assert torch.count_nonzero(y_graph[n_real:]).item() == 0
