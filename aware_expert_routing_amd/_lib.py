@@ -72,7 +72,7 @@ _SIGNATURES = [
     ("moe_route_topk", [_P, _I, _I, _I, _I, _P, _P, _P], _I),
     ("moe_route_oea", [_P, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P], _I),
     ("moe_dispatch", [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
-    ("moe_route_dispatch", [_P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    ("moe_route_dispatch", [_P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
      _I),
     ("moe_router_route_dispatch", [_P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I] + [_P] * 14, _I),
     ("moe_ffn_workspace_bytes", [_I, _I, _I, _I], _S),
@@ -230,13 +230,15 @@ def dispatch(idx, N: int, out=None, stream=None):
 
 def route_dispatch(logits, k: int, mode: str, k0: int = 0, p: float = 1.0, renorm: bool = True,
                    route=None, disp=None, stream=None, max_p: int | None = None, n_valid=None,
-                   k0_by_batch=None):
+                   k0_by_batch=None, sync=None):
     """Routing ("topk", "oea" or "pruned") and dispatch (one launch up to 48 tokens).
 
     max_p: OEA Phase 2 rank limit (default N); n_valid: optional device int32
     tensor [1] with the number of real tokens; k0_by_batch: optional device
-    int32 tensor [B+1], the k0 to use for each real batch size.  Returns
-    (route, disp) dicts.
+    int32 tensor [B+1], the k0 to use for each real batch size; sync: optional
+    device int32 [1], zero on entry and left at zero (vanilla top-k above 48
+    tokens then dispatches in its routing launch).  Returns (route, disp)
+    dicts.
     """
     B, N = logits.shape
     dev = logits.device
@@ -250,11 +252,12 @@ def route_dispatch(logits, k: int, mode: str, k0: int = 0, p: float = 1.0, renor
     m = {"topk": MOE_ROUTE_TOPK, "oea": MOE_ROUTE_OEA, "pruned": MOE_ROUTE_PRUNED}[mode]
     _check_i32_table(n_valid, 1, "n_valid", dev)
     _check_i32_table(k0_by_batch, B + 1, "k0_by_batch", dev)
+    _check_i32_table(sync, 1, "sync", dev)
     _check("moe_route_dispatch", lib().moe_route_dispatch(
         _ptr(logits), B, N, k, m, int(k0), float(p), N if max_p is None else int(max_p), int(bool(renorm)),
         _ptr(n_valid), _ptr(k0_by_batch), _ptr(route["idx"]), _ptr(route["w"]), _ptr(route.get("n_base")), _ptr(route.get("mask")),
         _ptr(disp["cnt"]), _ptr(disp["offsets"]), _ptr(disp["perm"]), _ptr(disp["active"]), _ptr(disp["T"]),
-        _stream(stream)))
+        _ptr(sync), _stream(stream)))
     return route, disp
 
 

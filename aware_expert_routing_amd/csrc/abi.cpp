@@ -108,7 +108,7 @@ MOE_API int moe_route_dispatch(const float* logits, int B, int N, int k, int mod
                                int renorm, const int32_t* n_valid, const int32_t* k0_by_batch, int32_t* idx,
                                float* w, int32_t* n_base,
                                uint32_t* sbase_mask, int32_t* cnt, int32_t* offsets, int32_t* perm,
-                               int32_t* active, int32_t* T, void* stream) {
+                               int32_t* active, int32_t* T, int32_t* sync, void* stream) {
     if (!logits || !idx || !w || !cnt || !offsets || !perm || !active || !T) return fail(MOE_EINVAL, "null pointer");
     int st = check_sizes(B, N, k);
     if (st) return st;
@@ -124,7 +124,7 @@ MOE_API int moe_route_dispatch(const float* logits, int B, int N, int k, int mod
                                                  renorm, n_valid, oea_like ? k0_by_batch : nullptr, idx, w,
                                                  oea_like ? n_base : nullptr,
                                                  oea_like ? sbase_mask : nullptr, cnt, offsets, perm, active, T,
-                                                 as_stream(stream)),
+                                                 sync, as_stream(stream)),
                       "moe_route_dispatch");
 }
 

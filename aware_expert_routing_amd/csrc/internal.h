@@ -39,7 +39,7 @@ hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int m
                                  int renorm, const int32_t* n_valid, const int32_t* k0_by_batch, int32_t* idx,
                                  float* w, int32_t* n_base,
                                  uint32_t* mask, int32_t* cnt, int32_t* offsets, int32_t* perm, int32_t* active,
-                                 int32_t* T, hipStream_t s);
+                                 int32_t* T, int32_t* sync, hipStream_t s);
 hipError_t launch_router_route_dispatch(const void* x, int x_dtype, const float* w_r, int B, int H, int N, int k,
                                         int mode, int k0, float p, int max_p, int renorm, const int32_t* n_valid,
                                         const int32_t* k0_by_batch, float* logits, int32_t* idx, float* w,

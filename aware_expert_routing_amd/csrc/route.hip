@@ -922,8 +922,9 @@ __global__ __launch_bounds__(kGemvThreads * kFusedGroups) void router_logits_wid
 // 16 g .. 16 g + 15, one token per wavefront as for small batches, so a large
 // batch's selections run on B/16 CUs side by side instead of on one.
 //   Vanilla top-k: route_group_kernel<false> writes idx and w; the dispatch
-//   (dispatch_kernel) follows, or, when the caller has a completion count
-//   (the router's sync word), runs in the routing launch's last workgroup.
+//   (dispatch_kernel) follows, or, when the caller passes a completion count
+//   (a sync word that is zero on entry), runs in the routing launch's last
+//   workgroup.
 //   OEA: route_group_kernel<true> runs Phase 1 and leaves each token's
 //   baseline in its idx row (slots 0 .. n_i - 1, then -1); in the next
 //   launch every workgroup rebuilds S_base from those rows (integer OR in
@@ -1229,10 +1230,10 @@ hipError_t launch_route_dispatch(const float* logits, int B, int N, int k, int m
                                  int renorm, const int32_t* n_valid, const int32_t* k0_by_batch, int32_t* idx,
                                  float* w, int32_t* n_base,
                                  uint32_t* mask, int32_t* cnt, int32_t* offsets, int32_t* perm, int32_t* active,
-                                 int32_t* T, hipStream_t s) {
+                                 int32_t* T, int32_t* sync, hipStream_t s) {
     if (route_by_groups(B, N, mode, max_p))
         return launch_route_groups(logits, B, N, k, mode, k0, p, renorm, n_valid, k0_by_batch, idx, w, n_base, mask,
-                                   cnt, offsets, perm, active, T, nullptr, s);
+                                   cnt, offsets, perm, active, T, sync, s);
     const bool oea = mode != MOE_ROUTE_TOPK;
 #define MOE_ROUTE(G_, OEA_)                                                                                      \
     route_kernel<OEA_, true, G_><<<1, route_threads(B), 0, s>>>(                                                 \

@@ -111,7 +111,7 @@ class MoELayer:
         if mode not in ("topk", "oea", "pruned"):
             raise ValueError(mode)
         L.route_dispatch(logits, self.k, mode, k0, p, True, buf.route, buf.disp, stream, max_p, n_valid,
-                         k0_by_batch)
+                         k0_by_batch, buf.extra["sync"])
         return buf
 
     def ffn(self, x: torch.Tensor, buf: Buffers, stream=None) -> torch.Tensor:

@@ -174,6 +174,10 @@ int moe_dispatch(const int32_t *idx, int B, int N, int k, int32_t *cnt, int32_t 
  *             [1, k]; the k0 argument then only bounds max_p's check.  The
  *             table is read on the device, so a captured graph follows the
  *             real batch size of each replay.
+ *   sync : NULL, or a device int32 [1], zero before the first call and left
+ *          at zero by every call (calls sharing it must be ordered, e.g. on
+ *          one stream): with it, vanilla top-k above 48 tokens dispatches in
+ *          its routing launch's last workgroup instead of a launch of its own
  *   Outputs as moe_route_oea (n_base, sbase_mask may be NULL; ignored for
  *   top-k) followed by moe_dispatch on idx; T = number of active experts
  *   (for OEA and pruned also |S_base|).  In the one-launch form the routed
@@ -184,17 +188,15 @@ int moe_route_dispatch(const float *logits, int B, int N, int k, int mode, int k
                        int renorm, const int32_t *n_valid, const int32_t *k0_by_batch, int32_t *idx,
                        float *w, int32_t *n_base,
                        uint32_t *sbase_mask, int32_t *cnt, int32_t *offsets, int32_t *perm, int32_t *active,
-                       int32_t *T, void *stream);
+                       int32_t *T, int32_t *sync, void *stream);
 
 /*
  * Router logits, routing and dispatch [OEA section 2 Q1: the router scores
  * every expert for every token; then as moe_route_dispatch].
  *   x, x_dtype, w_r, H : as moe_router_logits; logits [B, N] fp32 receives
  *                        the router output (the routing decisions use it)
- *   the remaining arguments are those of moe_route_dispatch, plus
- *   sync : device int32 [1], zero before the first call; every call leaves
- *          it at zero.  Calls sharing a sync word must be ordered (e.g. on
- *          one stream).
+ *   the remaining arguments are those of moe_route_dispatch, but sync is
+ *          required here (the router's workgroups count themselves in it).
  * Where moe_route_dispatch takes one launch, this is one launch too: its
  * workgroups each compute a slice of the logits, and the one that finishes
  * last routes and dispatches the batch, so no workgroup waits.  Otherwise

@@ -170,7 +170,8 @@ def test_route_dispatch_rejects_bad_arguments():
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("logits", FAKE), ("B", 16), ("N", 128), ("k", 8), ("mode", 1), ("k0", 3), ("p", 1.0), ("max_p", 128),
         ("renorm", 1), ("n_valid", None), ("k0_by_batch", None), ("idx", FAKE), ("w", FAKE), ("n_base", None), ("mask", None),
-        ("cnt", FAKE), ("offsets", FAKE), ("perm", FAKE), ("active", FAKE), ("T", FAKE), ("stream", None))]
+        ("cnt", FAKE), ("offsets", FAKE), ("perm", FAKE), ("active", FAKE), ("T", FAKE), ("sync", None),
+        ("stream", None))]
     assert lib.moe_route_dispatch(*args(mode=3)) == -1
     assert lib.moe_route_dispatch(*args(max_p=2)) == -1          # max_p < k0
     assert lib.moe_route_dispatch(*args(max_p=129)) == -1        # max_p > N

@@ -142,6 +142,29 @@ def test_fused_route_dispatch_parity(B, N, k, mode, k0, p, kind, scale, zipf):
             assert dref["T"] == ref["T"]
 
 
+@pytest.mark.parametrize("B,N,k,nv,scale,zipf", [(64, 128, 8, None, 1.0, 0.0), (128, 128, 8, None, 2.0, 1.1),
+                                                  (100, 64, 16, 71, 4.0, 1.1), (49, 33, 1, None, 1.0, 0.0)])
+def test_route_dispatch_with_a_sync_word(B, N, k, nv, scale, zipf):
+    # above 48 tokens vanilla top-k given a zero-on-entry sync word dispatches
+    # in its routing launch's last workgroup: the same outputs as the oracle,
+    # and the word is left at zero for the next call
+    sync = torch.zeros(1, dtype=torch.int32, device=DEV)
+    n_valid = None if nv is None else torch.tensor([nv], dtype=torch.int32, device=DEV)
+    for seed in range(3):
+        l = _logits("normal", 60 + seed, B, N, scale, zipf)
+        route, disp = moe.route_dispatch(torch.from_numpy(l).to(DEV), k, "topk", 0, 1.0, True, n_valid=n_valid,
+                                         sync=sync)
+        torch.cuda.synchronize()
+        assert int(sync.item()) == 0
+        ref = oracle.route(l, k, oea=False, n_valid=nv)
+        assert np.array_equal(route["idx"].cpu().numpy(), ref["idx"]), seed
+        assert np.abs(route["w"].cpu().numpy().astype(np.float64) - ref["w"]).max() <= 1e-6
+        dref = oracle.dispatch(ref["idx"], N)
+        for key in ("cnt", "offsets", "perm", "active"):
+            assert np.array_equal(disp[key].cpu().numpy(), dref[key]), key
+        assert int(disp["T"].item()) == dref["T"]
+
+
 @pytest.mark.parametrize("B,N,k,mode,k0,p,max_p,nv,scale,zipf", [
     (16, 128, 8, "pruned", 3, 1.0, None, None, 0.9, 0.0), (64, 128, 8, "pruned", 5, 0.5, None, None, 4.0, 1.1),
     (16, 128, 8, "oea", 3, 1.0, 8, None, 0.9, 0.0),        # piggyback only within the token's top-8
